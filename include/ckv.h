@@ -1,0 +1,183 @@
+/*
+ * ckv.h -- C ABI of libckv.so: ClusterKV's clustering, recall and sparse
+ * attention on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   "ClusterKV article": the intelliparadigm.com article
+ *     "大模型KV Cache压缩技术：ClusterKV的语义空间优化", a write-up of the DAC'25
+ *     paper "ClusterKV: Manipulating LLM KV Cache in Semantic Space for
+ *     Recallable Compression".
+ *   "ClusterKV abstract": the arxivdaily.com listing of arXiv 2412.03213
+ *     (recall at semantic-cluster granularity; clustering, selection,
+ *     indexing and caching).
+ *
+ * Vocabulary.  A *unit* is one KV head of one sequence of one layer:
+ * unit u = b * n_kv_heads + h.  Query head g of KV head h is query head
+ * h * group + g (grouped-query attention).  head_dim must be 128.  Tokens
+ * [0, n_sink) are sinks and never clustered; tokens [n_sink, n_clustered)
+ * are clustered; tokens [n_clustered, n_total) are recent and not yet
+ * clustered.  m = n_clustered - n_sink.
+ *
+ * Data types.  bf16 buffers are uint16_t bit patterns.  All pointers in
+ * ckv_layer and all array arguments are DEVICE pointers (hipMalloc'd memory
+ * of the current device), 16-byte aligned, owned by the caller.  The library
+ * allocates and frees nothing, keeps no global state beyond a thread-local
+ * error string, and never synchronises: every call enqueues work on the given
+ * HIP stream (NULL = the legacy default stream) and returns; results are
+ * valid once that stream has reached them.
+ *
+ * Errors.  Every entry point returns CKV_OK (0) or a negative code.  Argument
+ * errors are detected on the host before anything is enqueued, so a failed
+ * call writes nothing.  ckv_last_error() returns a thread-local text for the
+ * last failing call on this thread.
+ *
+ * Calls that use the workspace take a caller-owned device buffer of at least
+ * ckv_workspace_bytes() bytes.  The workspace must be zero-filled once before
+ * its first use (ckv_workspace_init does that on the stream).  Calls sharing
+ * one workspace must be ordered (same stream, or synchronised); calls on
+ * different workspaces and different layers are independent.
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKV_OK 0
+#define CKV_EINVAL (-1)       /* null/misaligned pointer, size out of range   */
+#define CKV_ENOSPACE (-2)     /* workspace too small, cache capacity exceeded */
+#define CKV_EHIP (-3)         /* HIP launch or runtime error                  */
+#define CKV_EUNSUPPORTED (-4) /* head_dim != 128, group > 16, K > 1024        */
+
+#define CKV_HEAD_DIM 128
+#define CKV_MAX_GROUP 16
+#define CKV_MAX_CLUSTERS 1024
+
+/* One layer's cache and cluster state (a plain struct the caller fills). */
+typedef struct ckv_layer {
+  int32_t batch;        /* sequences                                         */
+  int32_t n_kv_heads;   /* KV heads per layer; units = batch * n_kv_heads    */
+  int32_t group;        /* query heads per KV head, 1..16                    */
+  int32_t head_dim;     /* must be 128                                       */
+  int32_t n_sink;       /* unclustered leading tokens (16 in the method)     */
+  int32_t n_clusters;   /* K, 1..1024                                        */
+  int32_t capacity;     /* token rows per unit in k_tok / v_tok              */
+  int32_t n_total;      /* tokens in the cache; the library advances it     */
+  int32_t n_clustered;  /* sinks + clustered tokens; the library advances it */
+  int32_t reserved;     /* set to 0                                          */
+  /* token-order cache, bf16 [units, capacity, 128] */
+  uint16_t* k_tok;
+  uint16_t* v_tok;
+  /* cluster-ordered copy of the clustered rows, bf16 [units, capacity - n_sink, 128];
+     row p holds token perm[p] */
+  uint16_t* k_clu;
+  uint16_t* v_clu;
+  /* second copy of the same shape, written by ckv_cluster_incremental and
+     then swapped with k_clu / v_clu (may be NULL if incremental is never used) */
+  uint16_t* k_clu_alt;
+  uint16_t* v_clu_alt;
+  uint16_t* cdir;       /* bf16 [units, K, 128]: unit-direction centroids used for assignment */
+  double* csum;         /* f64 [units, K, 128]: sum of members' unit keys                     */
+  double* msum;         /* f64 [units, K, 128]: sum of members' keys                          */
+  float* cmean;         /* f32 [units, K, 128]: mean key (scoring centroid); 0 if empty       */
+  int32_t* csize;       /* [units, K]: members per cluster                                    */
+  int32_t* offsets;     /* [units, K + 1]: cluster j = positions offsets[j] .. offsets[j+1]-1 */
+  int32_t* assign;      /* [units, capacity - n_sink]: cluster of token n_sink + i            */
+  int32_t* perm;        /* [units, capacity - n_sink]: token id at cluster-order position p   */
+} ckv_layer;
+
+/* Text of the last error on this thread ("" if none).  Never NULL. */
+const char* ckv_last_error(void);
+
+/* sizeof(ckv_layer), so that language bindings can check their mirror of it. */
+size_t ckv_abi_layer_bytes(void);
+
+/* Bytes of workspace every call on layer L needs for budgets up to max_budget.
+ * Returns 0 if L is invalid (see ckv_last_error). */
+size_t ckv_workspace_bytes(const ckv_layer* L, int32_t max_budget);
+
+/* Zero-fill a workspace on stream s (with a kernel, so it may be captured in a
+ * HIP graph).  ws: device pointer, 16-byte aligned; ws_bytes > 0. */
+int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prefill clustering (ClusterKV article §3.2 prefill; §3.1 centroid; §4.1 layout).
+ * Clusters tokens [n_sink, n) of every unit into K clusters by cosine K-means:
+ *   init     c_j = bf16(x_I(j) / |x_I(j)|) with I = init_idx[u, :] -- K distinct
+ *            indices in [0, m) into the clustered tokens, drawn by the caller
+ *            (device int32 [units, K]); an index outside [0, m) gives a zero
+ *            direction;
+ *   iters rounds of: a_i = argmax_j x_i . c_j (ties -> smallest j);
+ *            S_j = sum of unit keys of members; c_j = bf16_rne(S_j / |S_j|)
+ *            (empty or zero-sum clusters keep c_j);
+ * then writes, from the final labels: assign, csize, offsets, perm (stable:
+ * ascending token id inside a cluster), csum, msum, cmean = msum / csize,
+ * and the cluster-ordered rows k_clu / v_clu.
+ * Reads k_tok / v_tok rows [0, n).  Requires n_sink >= 0, 1 <= K <= m,
+ * n <= capacity, iters >= 1.  Sets n_total = n_clustered = n on success.
+ */
+int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Append one decoded token per unit: k_new, v_new are bf16 [units, 128]
+ * (device).  Writes row n_total of k_tok / v_tok and advances n_total.
+ * CKV_ENOSPACE if n_total == capacity.
+ */
+int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void* stream);
+
+/*
+ * Incremental clustering (ClusterKV article §3.2 decoding-stage update): the
+ * recent tokens [n_clustered, n_total) are assigned to the current directions
+ * (ties -> smallest j), added to csum / msum / csize, and the touched
+ * clusters get c_j = bf16_rne(csum_j / |csum_j|) (if nonzero) and
+ * cmean_j = msum_j / csize_j.  Old tokens keep their cluster; K is unchanged.
+ * The index (offsets, perm) is rebuilt over all clustered tokens and the
+ * cluster-ordered copy is rewritten into k_clu_alt / v_clu_alt, which are then
+ * swapped with k_clu / v_clu in *L.  The caller decides when to call it (the
+ * method does so every 320 decoded tokens).  Requires the state written by a
+ * previous prefill or incremental call (assign / csize / csum / msum of the
+ * already clustered tokens) and non-NULL k_clu_alt / v_clu_alt.  A call with
+ * no recent tokens does nothing.  Sets n_clustered = n_total.
+ */
+int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Cluster-granularity recall (ClusterKV article §3.3; GQA reading: one recall
+ * per KV head with the group's summed query q_bar = sum_g q_g).
+ *   q:        bf16 [batch, n_kv_heads * group, 128] (device)
+ *   sel_pos:  int32 [units, budget] (device, written): ascending cluster-order
+ *             positions of the recalled tokens in the first sel_count[u] slots
+ *   sel_count int32 [units] (device, written): exactly min(budget, m)
+ * Clusters are visited by descending q_bar . cmean_j (ties -> smaller j; empty
+ * clusters never), taken whole while they fit in the remaining budget; the
+ * first cluster that does not fit contributes its highest-q_bar.k tokens
+ * (ties -> smaller position) to fill the budget exactly.  Requires
+ * n_clustered - n_sink >= K, budget >= 0.
+ */
+int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+               int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse decode (ClusterKV article §3.1 attention; §4.1 cluster-contiguous
+ * rows): for every query head g of unit u,
+ *   out[b, h * group + g, :] = softmax(q_g . K_S^T / sqrt(128)) V_S
+ * over S = sinks [0, n_sink) of k_tok/v_tok, the sel_count[u] rows of
+ * k_clu/v_clu listed in sel_pos[u, :] (row stride `budget`), and the recent
+ * rows [n_clustered, n_total) of k_tok/v_tok.  out is f32
+ * [batch, n_kv_heads * group, 128] (device, written); an empty S gives 0.
+ * sel_count[u] must be <= min(budget, m) and every listed position < m.
+ */
+int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos,
+                      const int32_t* sel_count, int32_t budget, float* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKV_H */

@@ -1,0 +1,25 @@
+"""ClusterKV hot path on AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libckv.so`` (hand-written HIP, built in-tree by
+``semantic_cluster_sparse_amd.build``).  ``ckv`` is a ctypes binding with the
+same names as the C ABI in ``include/ckv.h``; ``layer.Layer`` allocates one
+layer's device buffers with PyTorch and forwards to those calls.  There is no
+CPU or PyTorch fallback: importing the binding fails loudly when the library
+is missing.
+"""
+
+from .ckv import (  # noqa: F401
+    CkvError,
+    CkvLayerStruct,
+    ckv_abi_layer_bytes,
+    ckv_append,
+    ckv_cluster_incremental,
+    ckv_cluster_prefill,
+    ckv_last_error,
+    ckv_select,
+    ckv_sparse_decode,
+    ckv_workspace_bytes,
+    ckv_workspace_init,
+    load_library,
+    library_path,
+)

@@ -1,0 +1,296 @@
+// C ABI of libckv.so: host-side validation, workspace layout and launch
+// orchestration.  Declarations and the full contract live in include/ckv.h.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ckv.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CKV_OK;
+  return fail(CKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t counters;  // reserved, kept zero
+  size_t hist;      // prefill / incremental: [units, tiles, K] int32
+  size_t scores;    // select: [units, K] f32
+  size_t cut;       // select: [units, clu_cap] u32 keys of the cut cluster
+  size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
+  size_t total;
+  size_t off_hist, off_scores, off_cut, off_partials;
+};
+
+int group_tier(int g) {
+  int t = 1;
+  while (t < g) t <<= 1;
+  return t;
+}
+
+Layout layout_of(const ckv_layer* L) {
+  const size_t units = (size_t)L->batch * L->n_kv_heads;
+  const size_t clu_cap = (size_t)(L->capacity - L->n_sink);
+  const size_t tiles = (clu_cap + ckv::kSortTile - 1) / ckv::kSortTile;
+  Layout w;
+  w.counters = align256(units * 2 * sizeof(uint32_t));
+  w.hist = align256(units * tiles * L->n_clusters * sizeof(int32_t));
+  w.scores = align256(units * L->n_clusters * sizeof(float));
+  w.cut = align256(units * clu_cap * sizeof(uint32_t));
+  w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
+  w.off_hist = w.counters;
+  w.off_scores = w.counters;
+  w.off_cut = w.counters + w.scores;
+  w.off_partials = w.counters;
+  size_t body = w.hist;
+  if (w.scores + w.cut > body) body = w.scores + w.cut;
+  if (w.partials > body) body = w.partials;
+  w.total = w.counters + body;
+  return w;
+}
+
+// Checks shared by every call that takes a layer.
+int check_layer(const ckv_layer* L) {
+  if (!L) return fail(CKV_EINVAL, "layer is NULL");
+  if (L->head_dim != CKV_HEAD_DIM) return fail(CKV_EUNSUPPORTED, "head_dim %d != 128", L->head_dim);
+  if (L->group < 1) return fail(CKV_EINVAL, "group %d < 1", L->group);
+  if (L->group > CKV_MAX_GROUP) return fail(CKV_EUNSUPPORTED, "group %d > %d", L->group, CKV_MAX_GROUP);
+  if (L->batch < 1 || L->n_kv_heads < 1) return fail(CKV_EINVAL, "batch and n_kv_heads must be >= 1");
+  if ((long long)L->batch * L->n_kv_heads > (1 << 24)) return fail(CKV_EINVAL, "too many units");
+  if (L->n_clusters < 1) return fail(CKV_EINVAL, "n_clusters %d < 1", L->n_clusters);
+  if (L->n_clusters > CKV_MAX_CLUSTERS)
+    return fail(CKV_EUNSUPPORTED, "n_clusters %d > %d", L->n_clusters, CKV_MAX_CLUSTERS);
+  if (L->n_sink < 0) return fail(CKV_EINVAL, "n_sink %d < 0", L->n_sink);
+  if (L->capacity <= L->n_sink) return fail(CKV_EINVAL, "capacity %d <= n_sink %d", L->capacity, L->n_sink);
+  if (L->capacity > (1 << 30)) return fail(CKV_EINVAL, "capacity too large");
+  if (L->n_total < 0 || L->n_total > L->capacity)
+    return fail(CKV_EINVAL, "n_total %d outside [0, capacity]", L->n_total);
+  if (L->n_clustered < 0 || L->n_clustered > L->n_total)
+    return fail(CKV_EINVAL, "n_clustered %d outside [0, n_total]", L->n_clustered);
+  return CKV_OK;
+}
+
+int check_ptrs(const char* names, int n, ...) {
+  va_list ap;
+  va_start(ap, n);
+  for (int i = 0; i < n; ++i) {
+    const void* p = va_arg(ap, const void*);
+    if (!aligned16(p)) {
+      va_end(ap);
+      return fail(CKV_EINVAL, "pointer %d of (%s) is NULL or not 16-byte aligned", i, names);
+    }
+  }
+  va_end(ap);
+  return CKV_OK;
+}
+
+int check_ws(const ckv_layer* L, const void* ws, size_t ws_bytes) {
+  if (!aligned16(ws)) return fail(CKV_EINVAL, "workspace is NULL or not 16-byte aligned");
+  const Layout w = layout_of(L);
+  if (ws_bytes < w.total)
+    return fail(CKV_ENOSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+  return CKV_OK;
+}
+
+int clustered_tokens(const ckv_layer* L) { return L->n_clustered - L->n_sink; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ckv_last_error(void) { return g_err; }
+
+size_t ckv_abi_layer_bytes(void) { return sizeof(ckv_layer); }
+
+size_t ckv_workspace_bytes(const ckv_layer* L, int32_t max_budget) {
+  if (check_layer(L) != CKV_OK) return 0;
+  if (max_budget < 0) {
+    fail(CKV_EINVAL, "max_budget %d < 0", max_budget);
+    return 0;
+  }
+  return layout_of(L).total;
+}
+
+int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16(ws)) return fail(CKV_EINVAL, "workspace is NULL or not 16-byte aligned");
+  if (ws_bytes == 0) return fail(CKV_EINVAL, "ws_bytes is 0");
+  return hip_status(ckv::launch_zero(ws, ws_bytes, (hipStream_t)stream), "workspace init");
+}
+
+int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (iters < 1) return fail(CKV_EINVAL, "iters %d < 1", iters);
+  if (n > L->capacity) return fail(CKV_EINVAL, "n %d > capacity %d", n, L->capacity);
+  const int m = n - L->n_sink;
+  if (m < L->n_clusters) return fail(CKV_EINVAL, "need n_clusters %d <= m = n - n_sink = %d", L->n_clusters, m);
+  rc = check_ptrs("k_tok,v_tok,k_clu,v_clu,cdir,csum,msum,cmean,csize,offsets,assign,perm,init_idx", 13,
+                  L->k_tok, L->v_tok, L->k_clu, L->v_clu, L->cdir, L->csum, L->msum, L->cmean, L->csize,
+                  L->offsets, L->assign, L->perm, init_idx);
+  if (rc) return rc;
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+
+  const hipStream_t s = (hipStream_t)stream;
+  const int units = L->batch * L->n_kv_heads;
+  const int K = L->n_clusters;
+  const int clu_stride = L->capacity - L->n_sink;
+  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
+  const Layout w = layout_of(L);
+  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
+
+  hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
+  if (e != hipSuccess) return hip_status(e, "init");
+  for (int it = 0; it < iters; ++it) {
+    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s);
+    if (e != hipSuccess) return hip_status(e, "assign");
+    e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
+    if (e != hipSuccess) return hip_status(e, "hist");
+    e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
+    if (e != hipSuccess) return hip_status(e, "scatter");
+    const int mode = (it == iters - 1) ? ckv::kUpdFinal : ckv::kUpdIter;
+    e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->perm, clu_stride, L->offsets, K, L->csum,
+                           L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s);
+    if (e != hipSuccess) return hip_status(e, "update");
+  }
+  L->n_total = n;
+  L->n_clustered = n;
+  return CKV_OK;
+}
+
+int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  rc = check_ptrs("k_tok,v_tok,k_new,v_new", 4, L->k_tok, L->v_tok, k_new, v_new);
+  if (rc) return rc;
+  if (L->n_total >= L->capacity) return fail(CKV_ENOSPACE, "cache full (capacity %d)", L->capacity);
+  const int units = L->batch * L->n_kv_heads;
+  hipError_t e = ckv::launch_append(k_new, v_new, L->k_tok, L->v_tok, L->capacity, L->n_total, units,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "append");
+  L->n_total += 1;
+  return CKV_OK;
+}
+
+int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->n_clustered < L->n_sink) return fail(CKV_EINVAL, "no cluster state (n_clustered < n_sink)");
+  if (L->n_total == L->n_clustered) return CKV_OK;
+  rc = check_ptrs("k_tok,v_tok,k_clu_alt,v_clu_alt,cdir,csum,msum,cmean,csize,offsets,assign,perm", 12,
+                  L->k_tok, L->v_tok, L->k_clu_alt, L->v_clu_alt, L->cdir, L->csum, L->msum, L->cmean,
+                  L->csize, L->offsets, L->assign, L->perm);
+  if (rc) return rc;
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+
+  const hipStream_t s = (hipStream_t)stream;
+  const int units = L->batch * L->n_kv_heads;
+  const int K = L->n_clusters;
+  const int clu_stride = L->capacity - L->n_sink;
+  const int m_old = L->n_clustered - L->n_sink;
+  const int m_new = L->n_total - L->n_clustered;
+  const int m = m_old + m_new;
+  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
+  const Layout w = layout_of(L);
+  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
+
+  hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
+                                    clu_stride, m_old, units, s);
+  if (e != hipSuccess) return hip_status(e, "assign");
+  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
+  if (e != hipSuccess) return hip_status(e, "hist");
+  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
+  if (e != hipSuccess) return hip_status(e, "scatter");
+  e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->perm, clu_stride, L->offsets, K,
+                         L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu_alt, L->v_clu_alt, units, s);
+  if (e != hipSuccess) return hip_status(e, "update");
+  uint16_t* tk = L->k_clu;
+  uint16_t* tv = L->v_clu;
+  L->k_clu = L->k_clu_alt;
+  L->v_clu = L->v_clu_alt;
+  L->k_clu_alt = tk;
+  L->v_clu_alt = tv;
+  L->n_clustered = L->n_total;
+  return CKV_OK;
+}
+
+int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
+               void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
+  if (clustered_tokens(L) < L->n_clusters)
+    return fail(CKV_EINVAL, "no cluster state: clustered tokens %d < n_clusters %d", clustered_tokens(L),
+                L->n_clusters);
+  rc = check_ptrs("q,cmean,offsets,k_clu,sel_count", 5, q, L->cmean, L->offsets, L->k_clu, sel_count);
+  if (rc) return rc;
+  if (budget > 0 && !aligned16(sel_pos)) return fail(CKV_EINVAL, "sel_pos is NULL or not 16-byte aligned");
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+  const Layout w = layout_of(L);
+  const int units = L->batch * L->n_kv_heads;
+  hipError_t e = ckv::launch_select(q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_clu,
+                                    L->capacity - L->n_sink, budget, sel_pos, sel_count,
+                                    (float*)((char*)ws + w.off_scores), (uint32_t*)((char*)ws + w.off_cut),
+                                    units, (hipStream_t)stream);
+  return hip_status(e, "select");
+}
+
+int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, const int32_t* sel_count,
+                      int32_t budget, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
+  if (L->n_clustered < L->n_sink)
+    return fail(CKV_EINVAL, "n_clustered %d < n_sink %d: cluster the prefix first", L->n_clustered, L->n_sink);
+  rc = check_ptrs("q,k_tok,v_tok,sel_count,out", 5, q, L->k_tok, L->v_tok, sel_count, out);
+  if (rc) return rc;
+  const int m = clustered_tokens(L) > 0 ? clustered_tokens(L) : 0;
+  const int cmax = budget < m ? budget : m;
+  if (cmax > 0) {
+    rc = check_ptrs("sel_pos,k_clu,v_clu", 3, sel_pos, L->k_clu, L->v_clu);
+    if (rc) return rc;
+  }
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+  const int units = L->batch * L->n_kv_heads;
+  const long long rmax = (long long)L->n_sink + cmax + (L->n_total - L->n_clustered);
+  // Split-K heuristic: about 4 workgroups per CU over the whole launch, at least
+  // 64 rows per chunk, at most kMaxChunks chunks per unit.
+  long long chunk = (rmax * units + 1023) / 1024;
+  if (chunk < 64) chunk = 64;
+  const long long min_chunk = (rmax + ckv::kMaxChunks - 1) / ckv::kMaxChunks;
+  if (chunk < min_chunk) chunk = min_chunk;
+  chunk = (chunk + 15) / 16 * 16;
+  long long n_chunks = (rmax + chunk - 1) / chunk;
+  if (n_chunks < 1) n_chunks = 1;
+  const Layout w = layout_of(L);
+  hipError_t e = ckv::launch_sparse_decode(
+      q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
+      sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
+      (float*)((char*)ws + w.off_partials), out, units, (hipStream_t)stream);
+  return hip_status(e, "sparse_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,439 @@
+// Cosine K-means kernels: initial directions, MFMA assignment with a fused
+// row argmax, per-tile histograms, stable counting-sort scatter, and the
+// per-cluster segmented reduction that updates the centroid state and writes
+// the cluster-contiguous copy of the K/V rows.
+//
+// Method: ClusterKV article ("大模型KV Cache压缩技术：ClusterKV的语义空间优化"),
+// §3.2 (cosine K-means over the non-sink keys at prefill; online incremental
+// clustering during decoding), §3.1 (the centroid as the members' mean),
+// §4.1 (half-precision matrix multiply for the distances; cluster-contiguous
+// KV storage).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ckv {
+
+// ---------------------------------------------------------------------------
+// Initial directions: one wave per (unit, cluster); lane l holds dims 2l, 2l+1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void init_dirs_kernel(const uint16_t* __restrict__ k_tok,
+                                                        int capacity, int n_sink, int m,
+                                                        const int32_t* __restrict__ init_idx,
+                                                        int K, uint16_t* __restrict__ cdir,
+                                                        int units) {
+  const int lane = lane_id();
+  const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= (long)units * K) return;
+  const int u = (int)(gw / K);
+  const int j = (int)(gw % K);
+  const int idx = init_idx[(long)u * K + j];
+  const bool valid = idx >= 0 && idx < m;
+  const int row = valid ? n_sink + idx : 0;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(k_tok + ((size_t)u * capacity + row) * kHeadDim + 2 * lane);
+  const double x0 = (double)bf16_lo(w), x1 = (double)bf16_hi(w);
+  double n2 = x0 * x0 + x1 * x1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) n2 += __shfl_xor(n2, o);
+  uint32_t out = 0;
+  if (valid && n2 > 0.0) {
+    const double nrm = sqrt(n2);
+    out = (uint32_t)f64_to_bf16_rne(x0 / nrm) | ((uint32_t)f64_to_bf16_rne(x1 / nrm) << 16);
+  }
+  *reinterpret_cast<uint32_t*>(cdir + ((size_t)u * K + j) * kHeadDim + 2 * lane) = out;
+}
+
+// ---------------------------------------------------------------------------
+// Assignment: scores = X C^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16), fp32
+// accumulate, argmax fused in registers.  A workgroup owns 256 keys (4 waves x
+// 4 tiles of 16 rows) held as MFMA A-operands in registers and walks the
+// unit's directions in LDS chunks of 128.  Lane l of a 16x16 output tile holds
+// column (direction) l%16 of rows 4*(l/16)..+3; the running best per row is
+// kept per lane in increasing direction order (so ties keep the smaller
+// index) and merged across the 16 lanes at the end.
+// ---------------------------------------------------------------------------
+constexpr int kAsMt = 4;                    // 16-row tiles per wave
+constexpr int kAsRows = 4 * 16 * kAsMt;     // rows per workgroup
+constexpr int kAsChunk = 128;               // directions per LDS chunk
+constexpr int kAsLds = kHeadDim + 8;        // padded LDS row (272 B): conflict-free b128 reads
+
+__global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict__ k_tok,
+                                                     int capacity, int row0, int count,
+                                                     const uint16_t* __restrict__ cdir, int K,
+                                                     int32_t* __restrict__ assign, int clu_stride,
+                                                     int first, int tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t cs[kAsChunk * kAsLds];
+  const int u = blockIdx.x / tiles;
+  const int tile = blockIdx.x % tiles;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+  const int wrow0 = tile * kAsRows + wave * (16 * kAsMt);
+
+  const uint16_t* kbase = k_tok + ((size_t)u * capacity + row0) * kHeadDim;
+  bf16x8 a[kAsMt][4];
+#pragma unroll
+  for (int mt = 0; mt < kAsMt; ++mt) {
+    int r = wrow0 + mt * 16 + r16;
+    r = r < count ? r : count - 1;
+    const uint16_t* src = kbase + (size_t)r * kHeadDim + kg * 8;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[mt][s] = *reinterpret_cast<const bf16x8*>(src + s * 32);
+  }
+
+  float best[kAsMt][4];
+  int bidx[kAsMt][4];
+#pragma unroll
+  for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      best[mt][i] = -INFINITY;
+      bidx[mt][i] = 0;
+    }
+
+  const uint16_t* cbase = cdir + (size_t)u * K * kHeadDim;
+  for (int c0 = 0; c0 < K; c0 += kAsChunk) {
+    const int nc = min(kAsChunk, K - c0);
+    const int ntile = (nc + 15) >> 4;
+    __syncthreads();
+    for (int e = threadIdx.x; e < ntile * 16 * 16; e += blockDim.x) {
+      const int row = e >> 4, ch = e & 15;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < nc) v = *reinterpret_cast<const uint4*>(cbase + (size_t)(c0 + row) * kHeadDim + ch * 8);
+      *reinterpret_cast<uint4*>(cs + row * kAsLds + ch * 8) = v;
+    }
+    __syncthreads();
+    for (int t = 0; t < ntile; ++t) {
+      bf16x8 b[4];
+      const uint16_t* bp = cs + (t * 16 + r16) * kAsLds + kg * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(bp + s * 32);
+      const int j = c0 + t * 16 + r16;
+      const bool jv = (t * 16 + r16) < nc;
+#pragma unroll
+      for (int mt = 0; mt < kAsMt; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = jv ? acc[i] : -INFINITY;
+          if (v > best[mt][i]) {
+            best[mt][i] = v;
+            bidx[mt][i] = j;
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float bv = best[mt][i];
+      int bi = bidx[mt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      bidx[mt][i] = bi;
+    }
+
+  int32_t* out = assign + (size_t)u * clu_stride + first;
+#pragma unroll
+  for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wrow0 + mt * 16 + kg * 4 + i;
+      if (r16 == i && r < count) out[r] = bidx[mt][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Counting sort by cluster label, stable in token order.
+// hist: per (unit, tile of kSortTile tokens) label counts.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ assign,
+                                                   int clu_stride, int count, int K,
+                                                   int32_t* __restrict__ hist, int tiles) {
+  __shared__ int h[kMaxClusters];
+  const int u = blockIdx.x / tiles;
+  const int t = blockIdx.x % tiles;
+  for (int c = threadIdx.x; c < K; c += blockDim.x) h[c] = 0;
+  __syncthreads();
+  const int lo = t * kSortTile, hi = min(count, lo + kSortTile);
+  const int32_t* a = assign + (size_t)u * clu_stride;
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    int c = a[i];
+    c = c < 0 ? 0 : (c >= K ? K - 1 : c);
+    atomicAdd(&h[c], 1);
+  }
+  __syncthreads();
+  int32_t* out = hist + ((size_t)u * tiles + t) * K;
+  for (int c = threadIdx.x; c < K; c += blockDim.x) out[c] = h[c];
+}
+
+// Lanes of the wave holding the same label as this lane (among `valid` lanes).
+__device__ __forceinline__ unsigned long long match_label(int c, bool valid, int nbits) {
+  unsigned long long peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (c >> b) & 1;
+    const unsigned long long m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// scatter: each workgroup places the tokens of one tile.  Start of cluster c
+// for this tile = offsets[c] + (tokens of c in earlier tiles); inside the tile
+// each wave owns 512 consecutive tokens, and inside a wave batches of 64 are
+// placed in lane order via the peers mask.  Writes offsets from tile 0.
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ assign,
+                                                      int clu_stride, int count, int K,
+                                                      const int32_t* __restrict__ hist, int tiles,
+                                                      int n_sink, int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ offsets) {
+  __shared__ int base[kMaxClusters];
+  __shared__ int hw[4][kMaxClusters];
+  __shared__ int scan_scratch[8];
+  const int u = blockIdx.x / tiles;
+  const int t = blockIdx.x % tiles;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int32_t* hu = hist + (size_t)u * tiles * K;
+
+  int running = 0;
+  for (int c0 = 0; c0 < K; c0 += blockDim.x) {
+    const int c = c0 + threadIdx.x;
+    int total = 0, before = 0;
+    if (c < K) {
+      for (int tt = 0; tt < tiles; ++tt) {
+        const int v = hu[(size_t)tt * K + c];
+        total += v;
+        if (tt < t) before += v;
+      }
+    }
+    int chunk_total;
+    const int excl = block_exclusive_scan(total, scan_scratch, &chunk_total);
+    if (c < K) {
+      base[c] = running + excl + before;
+      if (t == 0) offsets[(size_t)u * (K + 1) + c] = running + excl;
+    }
+    running += chunk_total;
+  }
+  if (t == 0 && threadIdx.x == 0) offsets[(size_t)u * (K + 1) + K] = running;
+
+  for (int e = threadIdx.x; e < 4 * kMaxClusters; e += blockDim.x) (&hw[0][0])[e] = 0;
+  __syncthreads();
+  const int32_t* a = assign + (size_t)u * clu_stride;
+  const int wlo = t * kSortTile + wave * (kSortTile / 4);
+  for (int b = 0; b < kSortTile / 4; b += kWave) {
+    const int i = wlo + b + lane;
+    if (i < count) {
+      int c = a[i];
+      c = c < 0 ? 0 : (c >= K ? K - 1 : c);
+      atomicAdd(&hw[wave][c], 1);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < K; c += blockDim.x) {
+    int run = base[c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int v = hw[w][c];
+      hw[w][c] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+
+  int nbits = 0;
+  while ((1 << nbits) < K) ++nbits;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* pu = perm + (size_t)u * clu_stride;
+  for (int b = 0; b < kSortTile / 4; b += kWave) {
+    const int i = wlo + b + lane;
+    const bool valid = i < count;
+    int c = valid ? a[i] : 0;
+    c = c < 0 ? 0 : (c >= K ? K - 1 : c);
+    const unsigned long long peers = match_label(c, valid, nbits);
+    int bs = 0;
+    if (valid) bs = hw[wave][c];
+    if (valid) {
+      const int rank = __popcll(peers & lt);
+      pu[bs + rank] = n_sink + i;
+      if ((peers >> lane) == 1ull) hw[wave][c] = bs + __popcll(peers);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Update: one wave per (unit, cluster).  Four rows per step (16 lanes x 8 dims
+// each).  Sums in f64: S_j = sum x/|x|, M_j = sum x.  Iteration mode rebuilds
+// S from scratch and refreshes the direction; final mode also writes M, the
+// mean and the cluster-ordered K/V rows; incremental mode adds only the
+// members past the old size (new tokens sort last in their cluster), keeps
+// the old sums, refreshes touched clusters and rewrites every row.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void update_kernel(
+    const uint16_t* __restrict__ k_tok, const uint16_t* __restrict__ v_tok, int capacity,
+    const int32_t* __restrict__ perm, int clu_stride, const int32_t* __restrict__ offsets, int K,
+    double* __restrict__ csum, double* __restrict__ msum, float* __restrict__ cmean,
+    int32_t* __restrict__ csize, uint16_t* __restrict__ cdir, uint16_t* __restrict__ k_dst,
+    uint16_t* __restrict__ v_dst, int units) {
+  const int lane = lane_id();
+  const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= (long)units * K) return;
+  const int u = (int)(gw / K);
+  const int j = (int)(gw % K);
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int lo = offsets[(size_t)u * (K + 1) + j];
+  const int hi = offsets[(size_t)u * (K + 1) + j + 1];
+  const int n = hi - lo;
+  const size_t sidx = ((size_t)u * K + j) * kHeadDim + li * 8;
+  const int n_old = (MODE == kUpdIncr) ? csize[(size_t)u * K + j] : 0;
+  const int acc_from = lo + n_old;
+
+  double s[8], mm[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) s[t] = mm[t] = 0.0;
+
+  const int32_t* pu = perm + (size_t)u * clu_stride;
+  for (int p = lo + g; p < hi; p += 4) {
+    int tok = pu[p];
+    tok = tok < 0 ? 0 : (tok >= capacity ? capacity - 1 : tok);
+    const uint4 kx = *reinterpret_cast<const uint4*>(k_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
+    if (MODE != kUpdIter) {
+      const uint4 vx = *reinterpret_cast<const uint4*>(v_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
+      *reinterpret_cast<uint4*>(k_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = kx;
+      *reinterpret_cast<uint4*>(v_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = vx;
+    }
+    double x[8];
+    x[0] = bf16_lo(kx.x); x[1] = bf16_hi(kx.x);
+    x[2] = bf16_lo(kx.y); x[3] = bf16_hi(kx.y);
+    x[4] = bf16_lo(kx.z); x[5] = bf16_hi(kx.z);
+    x[6] = bf16_lo(kx.w); x[7] = bf16_hi(kx.w);
+    double n2 = 0.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
+    n2 = xor_sum16(n2);
+    if (p >= acc_from) {
+      const double inv = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        s[t] += x[t] * inv;
+        if (MODE != kUpdIter) mm[t] += x[t];
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    s[t] += __shfl_xor(s[t], 16);
+    s[t] += __shfl_xor(s[t], 32);
+    if (MODE != kUpdIter) {
+      mm[t] += __shfl_xor(mm[t], 16);
+      mm[t] += __shfl_xor(mm[t], 32);
+    }
+  }
+  if (MODE == kUpdIncr) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      s[t] += csum[sidx + t];
+      mm[t] += msum[sidx + t];
+    }
+  }
+  double ns2 = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ns2 += s[t] * s[t];
+  ns2 = xor_sum16(ns2);
+  if (g != 0) return;
+
+#pragma unroll
+  for (int t = 0; t < 8; ++t) csum[sidx + t] = s[t];
+  const bool touched = (MODE == kUpdIncr) ? (n > n_old) : (n > 0);
+  if (touched && ns2 > 0.0) {
+    const double nrm = sqrt(ns2);
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      w[t] = (uint32_t)f64_to_bf16_rne(s[2 * t] / nrm) | ((uint32_t)f64_to_bf16_rne(s[2 * t + 1] / nrm) << 16);
+    *reinterpret_cast<uint4*>(cdir + sidx) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (MODE != kUpdIter) {
+    float mu[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      msum[sidx + t] = mm[t];
+      mu[t] = n > 0 ? (float)(mm[t] / (double)n) : 0.0f;
+    }
+    *reinterpret_cast<float4*>(cmean + sidx) = make_float4(mu[0], mu[1], mu[2], mu[3]);
+    *reinterpret_cast<float4*>(cmean + sidx + 4) = make_float4(mu[4], mu[5], mu[6], mu[7]);
+  }
+  if (li == 0) csize[(size_t)u * K + j] = n;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int m,
+                            const int32_t* init_idx, int K, uint16_t* cdir, int units,
+                            hipStream_t s) {
+  const long waves = (long)units * K;
+  hipLaunchKernelGGL(init_dirs_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, k_tok,
+                     capacity, n_sink, m, init_idx, K, cdir, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
+                         const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
+                         int first, int units, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int tiles = (count + kAsRows - 1) / kAsRows;
+  hipLaunchKernelGGL(assign_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, k_tok,
+                     capacity, row0, count, cdir, K, assign, clu_stride, first, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist(const int32_t* assign, int clu_stride, int count, int K,
+                       int32_t* hist, int tiles, int units, hipStream_t s) {
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, assign,
+                     clu_stride, count, K, hist, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int K,
+                          const int32_t* hist, int tiles, int n_sink, int32_t* perm,
+                          int32_t* offsets, int units, hipStream_t s) {
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, assign,
+                     clu_stride, count, K, hist, tiles, n_sink, perm, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity,
+                         const int32_t* perm, int clu_stride, const int32_t* offsets, int K,
+                         double* csum, double* msum, float* cmean, int32_t* csize,
+                         uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units,
+                         hipStream_t s) {
+  const long waves = (long)units * K;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (mode == kUpdIter)
+    hipLaunchKernelGGL(update_kernel<kUpdIter>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
+                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+  else if (mode == kUpdFinal)
+    hipLaunchKernelGGL(update_kernel<kUpdFinal>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
+                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+  else
+    hipLaunchKernelGGL(update_kernel<kUpdIncr>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
+                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+  return hipGetLastError();
+}
+
+}  // namespace ckv

@@ -1,0 +1,64 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernel
+// translation units.  Every launcher only enqueues on `s` and returns the
+// launch status; argument validation happens in api.hip before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckv {
+
+constexpr int kSortTile = 2048;     // clustered tokens per histogram / scatter tile
+constexpr int kMaxClusters = 1024;  // K limit of the LDS-resident per-cluster arrays
+constexpr int kMaxGroup = 16;
+constexpr int kMaxChunks = 64;      // split-K chunks per unit in sparse decode
+constexpr int kPartialStride = 130; // floats per (chunk, head) partial: o[128], m, l
+
+enum UpdateMode { kUpdIter = 0, kUpdFinal = 1, kUpdIncr = 2 };
+
+// c_j = bf16(x_idx / |x_idx|) for idx = init_idx[u, j] (zero if idx outside [0, m)).
+hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int m,
+                            const int32_t* init_idx, int K, uint16_t* cdir, int units,
+                            hipStream_t s);
+
+// assign[u, first + i] = argmax_j k_tok[u, row0 + i] . cdir[u, j] for i < count.
+hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
+                         const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
+                         int first, int units, hipStream_t s);
+
+// Per-tile histograms of assign[u, 0:count): hist[u, tile, K].
+hipError_t launch_hist(const int32_t* assign, int clu_stride, int count, int K,
+                       int32_t* hist, int tiles, int units, hipStream_t s);
+
+// Stable counting sort by label: perm[u, pos] = n_sink + i, offsets[u, 0..K].
+hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int K,
+                          const int32_t* hist, int tiles, int n_sink, int32_t* perm,
+                          int32_t* offsets, int units, hipStream_t s);
+
+// Per-cluster segmented reduction over the members listed by perm/offsets.
+hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
+                         int capacity, const int32_t* perm, int clu_stride,
+                         const int32_t* offsets, int K, double* csum, double* msum,
+                         float* cmean, int32_t* csize, uint16_t* cdir, uint16_t* k_dst,
+                         uint16_t* v_dst, int units, hipStream_t s);
+
+// Recall: cluster scores, then rank / prefix / cut / partial top-k per unit.
+hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
+                         const int32_t* offsets, int K, const uint16_t* k_clu, int clu_stride,
+                         int budget, int32_t* sel_pos, int32_t* sel_count, float* scores_ws,
+                         uint32_t* cut_ws, int units, hipStream_t s);
+
+// Split-K sparse decode plus the log-sum-exp merge of the chunk partials.
+hipError_t launch_sparse_decode(const uint16_t* q, int group, const uint16_t* k_tok,
+                                const uint16_t* v_tok, int capacity, const uint16_t* k_clu,
+                                const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
+                                const int32_t* sel_count, int budget, int m, int n_sink,
+                                int n_clustered, int n_total, int chunk_rows, int n_chunks,
+                                float* partials, float* out, int units, hipStream_t s);
+
+hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok,
+                         uint16_t* v_tok, int capacity, int row, int units, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace ckv

@@ -1,0 +1,108 @@
+"""One layer's device buffers, allocated with PyTorch, and the calls on them.
+
+``Layer`` owns the tensors a ``ckv_layer`` points at (token-order K/V, the
+cluster-ordered copies, the centroid state and the index) plus a workspace,
+and forwards to the C ABI through ``ckv``.  PyTorch only allocates memory and
+supplies the current HIP stream; every step of the method runs in libckv.so.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import ckv
+
+HEAD_DIM = 128
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Layer:
+    def __init__(self, batch: int, n_kv_heads: int, group: int, n_clusters: int, capacity: int,
+                 n_sink: int = 16, max_budget: int = 2048, incremental: bool = True,
+                 device: str | torch.device = "cuda"):
+        self.device = torch.device(device)
+        self.units = batch * n_kv_heads
+        self.group = group
+        self.n_sink = n_sink
+        self.n_clusters = n_clusters
+        self.capacity = capacity
+        u, K, d = self.units, n_clusters, HEAD_DIM
+        clu = capacity - n_sink
+        bf = dict(dtype=torch.bfloat16, device=self.device)
+        self.k_tok = torch.zeros((u, capacity, d), **bf)
+        self.v_tok = torch.zeros((u, capacity, d), **bf)
+        self.k_clu = torch.zeros((u, clu, d), **bf)
+        self.v_clu = torch.zeros((u, clu, d), **bf)
+        self.k_clu_alt = torch.zeros((u, clu, d), **bf) if incremental else None
+        self.v_clu_alt = torch.zeros((u, clu, d), **bf) if incremental else None
+        self.cdir = torch.zeros((u, K, d), **bf)
+        self.csum = torch.zeros((u, K, d), dtype=torch.float64, device=self.device)
+        self.msum = torch.zeros((u, K, d), dtype=torch.float64, device=self.device)
+        self.cmean = torch.zeros((u, K, d), dtype=torch.float32, device=self.device)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.csize = torch.zeros((u, K), **i32)
+        self.offsets = torch.zeros((u, K + 1), **i32)
+        self.assign = torch.zeros((u, clu), **i32)
+        self.perm = torch.zeros((u, clu), **i32)
+        self.struct = ckv.CkvLayerStruct(
+            batch=batch, n_kv_heads=n_kv_heads, group=group, head_dim=HEAD_DIM, n_sink=n_sink,
+            n_clusters=n_clusters, capacity=capacity, n_total=0, n_clustered=0, reserved=0)
+        self._bind()
+        self.ws_bytes = ckv.ckv_workspace_bytes(self.struct, max_budget)
+        self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=self.device)
+        ckv.ckv_workspace_init(self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def _bind(self) -> None:
+        s = self.struct
+        for name in ("k_tok", "v_tok", "k_clu", "v_clu", "k_clu_alt", "v_clu_alt", "cdir", "csum",
+                     "msum", "cmean", "csize", "offsets", "assign", "perm"):
+            t = getattr(self, name)
+            setattr(s, name, t.data_ptr() if t is not None else None)
+
+    @property
+    def n_total(self) -> int:
+        return self.struct.n_total
+
+    @property
+    def n_clustered(self) -> int:
+        return self.struct.n_clustered
+
+    def set_counters(self, n_total: int, n_clustered: int) -> None:
+        self.struct.n_total = n_total
+        self.struct.n_clustered = n_clustered
+
+    # ----------------------------------------------------------------- calls
+    def prefill(self, n: int, iters: int, init_idx: torch.Tensor) -> None:
+        assert init_idx.dtype == torch.int32 and init_idx.is_contiguous()
+        assert tuple(init_idx.shape) == (self.units, self.n_clusters)
+        ckv.ckv_cluster_prefill(self.struct, n, iters, init_idx.data_ptr(), self.ws.data_ptr(),
+                                self.ws_bytes, _stream())
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        assert k_new.shape == (self.units, HEAD_DIM) and v_new.shape == (self.units, HEAD_DIM)
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        ckv.ckv_append(self.struct, k_new.data_ptr(), v_new.data_ptr(), _stream())
+
+    def incremental(self) -> None:
+        ckv.ckv_cluster_incremental(self.struct, self.ws.data_ptr(), self.ws_bytes, _stream())
+        # the library swapped the cluster-ordered buffers inside the struct
+        if self.struct.k_clu != self.k_clu.data_ptr():
+            self.k_clu, self.k_clu_alt = self.k_clu_alt, self.k_clu
+            self.v_clu, self.v_clu_alt = self.v_clu_alt, self.v_clu
+
+    def select(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor,
+               sel_count: torch.Tensor) -> None:
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * budget and sel_count.numel() >= self.units
+        ckv.ckv_select(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
+                       self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def sparse_decode(self, q: torch.Tensor, sel_pos: torch.Tensor, sel_count: torch.Tensor,
+                      budget: int, out: torch.Tensor) -> None:
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        assert out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_sparse_decode(self.struct, q.data_ptr(), sel_pos.data_ptr(), sel_count.data_ptr(),
+                              budget, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())

@@ -1,0 +1,144 @@
+"""C-ABI boundary checks that need no GPU.
+
+* libckv.so loads and exports every function include/ckv.h declares;
+* the binding's mirror of ckv_layer has the library's size;
+* argument errors come back as the documented codes before anything is
+  enqueued (these calls never reach a HIP launch);
+* workspace sizing is monotone in the sizes that drive it.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from semantic_cluster_sparse_amd import ckv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ckv.load_library()
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_layer_struct_size_matches():
+    assert ckv.ckv_abi_layer_bytes() == ctypes.sizeof(ckv.CkvLayerStruct)
+
+
+def _layer(**kw):
+    base = dict(batch=1, n_kv_heads=8, group=4, head_dim=128, n_sink=16, n_clusters=400,
+                capacity=32768 + 64, n_total=0, n_clustered=0, reserved=0)
+    base.update(kw)
+    return ckv.CkvLayerStruct(**base)
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; never dereferenced by these calls
+
+
+def _fill_ptrs(L):
+    for name, _ in ckv.CkvLayerStruct._fields_[10:]:
+        setattr(L, name, FAKE)
+    return L
+
+
+def test_workspace_bytes_and_errors():
+    L = _layer()
+    n1 = ckv.ckv_workspace_bytes(L, 2048)
+    assert n1 > 0 and n1 % 256 == 0
+    assert ckv.ckv_workspace_bytes(_layer(batch=2), 2048) > n1
+    assert ckv.ckv_workspace_bytes(_layer(capacity=65536), 2048) > n1
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_workspace_bytes(_layer(head_dim=64), 2048)
+    assert "head_dim" in e.value.message
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_workspace_bytes(_layer(n_clusters=0), 2048)
+    assert e.value.code == ckv.CKV_EINVAL
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, ckv.CKV_EUNSUPPORTED),
+    ("group", 17, ckv.CKV_EUNSUPPORTED),
+    ("group", 0, ckv.CKV_EINVAL),
+    ("n_clusters", 2048, ckv.CKV_EUNSUPPORTED),
+    ("n_sink", -1, ckv.CKV_EINVAL),
+    ("capacity", 16, ckv.CKV_EINVAL),
+])
+def test_layer_validation(field, value, code):
+    L = _fill_ptrs(_layer(**{field: value}))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1 << 40)
+    assert e.value.code == code
+    assert ckv.ckv_last_error()
+
+
+def test_prefill_argument_errors():
+    L = _fill_ptrs(_layer())
+    cases = [
+        (dict(n=32768, iters=0), ckv.CKV_EINVAL),               # no Lloyd round
+        (dict(n=100, iters=10), ckv.CKV_EINVAL),                # K > m
+        (dict(n=32768 + 65, iters=10), ckv.CKV_EINVAL),         # n > capacity
+    ]
+    for kw, code in cases:
+        with pytest.raises(ckv.CkvError) as e:
+            ckv.ckv_cluster_prefill(L, kw["n"], kw["iters"], FAKE, FAKE, 1 << 40)
+        assert e.value.code == code, kw
+    with pytest.raises(ckv.CkvError) as e:                      # misaligned init_idx
+        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE + 4, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    with pytest.raises(ckv.CkvError) as e:                      # workspace too small
+        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1024)
+    assert e.value.code == ckv.CKV_ENOSPACE
+    L.k_tok = None
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    assert L.n_total == 0 and L.n_clustered == 0               # nothing advanced
+
+
+def test_append_select_decode_errors():
+    L = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=100, n_clustered=100))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_append(L, FAKE, FAKE)
+    assert e.value.code == ckv.CKV_ENOSPACE and L.n_total == 100
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_select(L, FAKE, -1, FAKE, FAKE, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    L2 = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=20, n_clustered=20))
+    with pytest.raises(ckv.CkvError) as e:                      # 4 clustered tokens < K
+        ckv.ckv_select(L2, FAKE, 8, FAKE, FAKE, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    L3 = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=10, n_clustered=10))
+    with pytest.raises(ckv.CkvError) as e:                      # n_clustered < n_sink
+        ckv.ckv_sparse_decode(L3, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_sparse_decode(L, FAKE, FAKE, FAKE, 8, FAKE + 8, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_workspace_init(None, 16)
+    assert e.value.code == ckv.CKV_EINVAL
+    L4 = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=100, n_clustered=50))
+    L4.k_clu_alt = None
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_incremental(L4, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and L4.n_clustered == 50
+
+
+def test_state_inconsistency_is_rejected():
+    L = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=50, n_clustered=60))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_sparse_decode(L, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL

@@ -1,0 +1,449 @@
+"""GPU parity: libckv.so against the float64 oracle on identical bf16 inputs.
+
+Bars (from the method's precision contract):
+* assignments: bit-exact wherever the oracle's top-2 margin exceeds 1e-4 of
+  |x| (teacher-forced: zero unexcused mismatches; end-to-end: at most 0.1%
+  differing labels);
+* centroid directions: bitwise equal to the oracle's bf16 values whenever
+  the labels that produced them are equal;
+* recall: the same token set wherever the oracle's boundary scores are more
+  than 1e-4 (relative) apart; at most 0.1% of recalled tokens differ;
+* decode: max |GPU - oracle| <= 2e-3 per output element.
+Teacher-forced cases load the oracle's state into the GPU buffers; GPU
+results are never fed back to the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import (DECODE_ATOL, MISMATCH_FRACTION, SELECT_GAP, compare_assign, dev_bf16,
+                      host_bits, say, selection_boundary_gap, to_dev)
+from oracle import bf16, pipeline
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from semantic_cluster_sparse_amd.layer import Layer  # noqa: E402
+
+D = 128
+
+
+def gpu_layer(k_bits, v_bits, group, K, n_sink=16, max_budget=4096):
+    U, cap, _ = k_bits.shape
+    L = Layer(batch=U, n_kv_heads=1, group=group, n_clusters=K, capacity=cap, n_sink=n_sink,
+              max_budget=max_budget)
+    L.k_tok.copy_(dev_bf16(k_bits))
+    L.v_tok.copy_(dev_bf16(v_bits))
+    return L
+
+
+def load_state(L, states, n_sink=16):
+    """Teacher forcing: copy oracle states (one per unit) into the GPU buffers."""
+    for u, st in enumerate(states):
+        m = st["n_clustered"] - n_sink
+        L.cdir[u].copy_(dev_bf16(st["cdir_bits"]))
+        L.csum[u].copy_(torch.from_numpy(st["csum"]))
+        L.msum[u].copy_(torch.from_numpy(st["msum"]))
+        L.cmean[u].copy_(torch.from_numpy(st["cmean"].astype(np.float32)))
+        L.csize[u].copy_(torch.from_numpy(st["csize"].astype(np.int32)))
+        L.offsets[u].copy_(torch.from_numpy(st["offsets"].astype(np.int32)))
+        L.assign[u, :m].copy_(torch.from_numpy(st["assign"].astype(np.int32)))
+        L.perm[u, :m].copy_(torch.from_numpy(st["perm"].astype(np.int32)))
+        L.k_clu[u, :m].copy_(dev_bf16(st["k_clu_bits"]))
+        L.v_clu[u, :m].copy_(dev_bf16(st["v_clu_bits"]))
+
+
+def check_state(L, u, ora, x, cdir_used, n_sink=16, full=True, tag=""):
+    """Compare one unit's GPU cluster state with the oracle's. Returns #label mismatches."""
+    m = len(ora["assign"])
+    a_g = L.assign[u, :m].cpu().numpy()
+    mism, unexc = compare_assign(a_g, ora["assign"], x, cdir_used)
+    say(f"  {tag} unit {u}: label mismatches {mism} (unexcused {unexc}) of {m}")
+    assert unexc == 0
+    if mism:
+        return mism
+    assert np.array_equal(host_bits(L.cdir[u]), ora["cdir_bits"]), "directions differ"
+    assert np.array_equal(L.csize[u].cpu().numpy(), ora["csize"])
+    assert np.array_equal(L.offsets[u].cpu().numpy(), ora["offsets"])
+    assert np.array_equal(L.perm[u, :m].cpu().numpy(), ora["perm"])
+    assert np.allclose(L.csum[u].cpu().numpy(), ora["csum"], rtol=0, atol=1e-9)
+    if full:
+        assert np.allclose(L.msum[u].cpu().numpy(), ora["msum"], rtol=0, atol=1e-7)
+        mu = L.cmean[u].cpu().numpy().astype(np.float64)
+        assert np.allclose(mu, ora["cmean"], rtol=1e-6, atol=1e-6)
+        assert np.array_equal(host_bits(L.k_clu[u, :m]), ora["k_clu_bits"])
+        assert np.array_equal(host_bits(L.v_clu[u, :m]), ora["v_clu_bits"])
+    return 0
+
+
+def compare_selection(L, u, sel_pos, cnt, ora_state, sel, budget):
+    """Token sets of GPU and oracle recall; returns the differing token count."""
+    m = len(ora_state["assign"])
+    c = int(cnt[u])
+    assert c == min(budget, m)
+    pos_g = sel_pos[u, :c]
+    assert np.all(np.diff(pos_g) > 0), "positions must ascend"
+    tok_g = set(L.perm[u, :m].cpu().numpy()[pos_g].tolist())
+    tok_o = set(ora_state["perm"][sel["positions"]].tolist())
+    diff = len(tok_g ^ tok_o)
+    if diff:
+        gap = selection_boundary_gap(sel, bf16.widen(ora_state["k_clu_bits"]), ora_state["offsets"])
+        say(f"  unit {u}: recall differs by {diff} tokens; boundary gap {gap:.3g}")
+        assert gap <= SELECT_GAP
+    return diff
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def test_prefill_single_head_rounds():
+    cfg = synth.CONFIGS["single-head-2k"]
+    say(f"case: prefill {cfg.name}")
+    k, v, _ = synth.make_layer_inputs(cfg)
+    init = synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters)
+    ora = pipeline.prefill_unit(k[0], cfg.n_tokens, init[0], cfg.n_clusters, cfg.iters,
+                                v_bits=v[0], history=True)
+    x = bf16.widen(k[0][16:cfg.n_tokens])
+    for T in (1, 2, 3, 5, 10):
+        L = gpu_layer(k, v, 1, cfg.n_clusters)
+        L.prefill(cfg.n_tokens, T, to_dev(init, torch.int32))
+        torch.cuda.synchronize()
+        a_o, c_o = ora["history"][T]
+        st = dict(assign=a_o, cdir_bits=bf16.round_rne(c_o))
+        if T == cfg.iters:
+            st = ora
+        else:
+            from oracle import kmeans
+            S, M, n = kmeans.unit_sums(x, a_o, cfg.n_clusters)
+            perm, off = kmeans.build_index(a_o, cfg.n_clusters)
+            st.update(csum=S, msum=M, csize=n, offsets=off, perm=perm,
+                      cmean=kmeans.scoring_centroids(M, n), k_clu_bits=k[0][perm], v_clu_bits=v[0][perm])
+        assert check_state(L, 0, st, x, ora["history"][T - 1][1], tag=f"T={T}") == 0
+        assert L.n_total == cfg.n_tokens and L.n_clustered == cfg.n_tokens
+
+
+def test_teacher_forced_lloyd_rounds():
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    say("case: teacher-forced Lloyd rounds, Llama layer shape, units 0-1")
+    k, v, _ = synth.make_layer_inputs(cfg, units=[0, 1])
+    init = synth.make_init_indices(cfg.init_seed, 2, cfg.m, cfg.n_clusters)
+    oras = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, 4, v_bits=v[u],
+                                  history=True) for u in range(2)]
+    xs = [bf16.widen(k[u][16:cfg.n_tokens]) for u in range(2)]
+    from oracle import kmeans
+    for t in (1, 2, 4):
+        L = gpu_layer(k, v, cfg.group, cfg.n_clusters)
+        for u in range(2):
+            L.cdir[u].copy_(dev_bf16(bf16.round_rne(oras[u]["history"][t - 1][1])))
+        L.set_counters(cfg.n_tokens, 16)          # nothing clustered yet: one incremental = one round
+        L.incremental()
+        torch.cuda.synchronize()
+        for u in range(2):
+            a_o, c_o = oras[u]["history"][t]
+            S, M, n = kmeans.unit_sums(xs[u], a_o, cfg.n_clusters)
+            perm, off = kmeans.build_index(a_o, cfg.n_clusters)
+            st = dict(assign=a_o, cdir_bits=bf16.round_rne(c_o), csum=S, msum=M, csize=n,
+                      offsets=off, perm=perm, cmean=kmeans.scoring_centroids(M, n),
+                      k_clu_bits=k[u][perm], v_clu_bits=v[u][perm])
+            assert check_state(L, u, st, xs[u], oras[u]["history"][t - 1][1], tag=f"t={t}") == 0
+
+
+def test_llama_layer_end_to_end():
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    say(f"case: end-to-end {cfg.name}")
+    k, v, cen = synth.make_layer_inputs(cfg)
+    init = synth.make_init_indices(cfg.init_seed, cfg.units, cfg.m, cfg.n_clusters)
+    q = synth.make_queries(cfg.query_seed, cen, cfg.group)
+    L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.budget)
+    L.prefill(cfg.n_tokens, cfg.iters, to_dev(init, torch.int32))
+    qd = dev_bf16(q)
+    sel_pos = torch.zeros((cfg.units, cfg.budget), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((cfg.units,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((cfg.units, cfg.group, D), dtype=torch.float32, device="cuda")
+    L.select(qd, cfg.budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, cfg.budget, out)
+    torch.cuda.synchronize()
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    total_mism = total_diff = 0
+    for u in (0, 3, 7):
+        ora = pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, cfg.iters, v_bits=v[u],
+                                    history=True)
+        x = bf16.widen(k[u][16:cfg.n_tokens])
+        mism = check_state(L, u, ora, x, ora["history"][-2][1], tag="e2e")
+        total_mism += mism
+        if mism:
+            continue
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"],
+                                   cfg.budget)
+        diff = compare_selection(L, u, sp, cn, ora, sel, cfg.budget)
+        total_diff += diff
+        if diff == 0:
+            ref = pipeline.decode_unit(q[u], k[u], v[u], ora["k_clu_bits"], ora["v_clu_bits"],
+                                       sel["positions"], 16, cfg.n_tokens, cfg.n_tokens)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+    assert total_mism <= MISMATCH_FRACTION * 3 * cfg.m
+    assert total_diff <= MISMATCH_FRACTION * 2 * 3 * cfg.budget
+
+
+# ------------------------------------------------------------------ select
+
+
+def test_select_teacher_forced():
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    say("case: teacher-forced recall, Llama layer shape")
+    units = [0, 1, 2, 3]
+    k, v, cen = synth.make_layer_inputs(cfg, units=units)
+    init = synth.make_init_indices(cfg.init_seed, len(units), cfg.m, cfg.n_clusters)
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, 2, v_bits=v[u])
+              for u in range(len(units))]
+    q = synth.make_queries(cfg.query_seed, cen, cfg.group)
+    L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.m + 5)
+    load_state(L, states)
+    L.set_counters(cfg.n_tokens, cfg.n_tokens)
+    qd = dev_bf16(q)
+    for budget in (0, 1, 100, 1024, 4096, cfg.m, cfg.m + 5):
+        sel_pos = torch.full((len(units), max(budget, 1)), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((len(units),), dtype=torch.int32, device="cuda")
+        L.select(qd, budget, sel_pos, cnt)
+        torch.cuda.synchronize()
+        sp, cn = sel_pos.cpu().numpy(), cnt.cpu().numpy()
+        for u in range(len(units)):
+            st = states[u]
+            mu32 = st["cmean"].astype(np.float32).astype(np.float64)
+            sel = pipeline.select_unit(q[u], mu32, st["csize"], st["offsets"], st["k_clu_bits"], budget)
+            c = min(budget, cfg.m)
+            assert cn[u] == c
+            pos_g = sp[u, :c]
+            if not np.array_equal(pos_g, sel["positions"]):
+                gap = selection_boundary_gap(sel, bf16.widen(st["k_clu_bits"]), st["offsets"])
+                nd = len(set(pos_g.tolist()) ^ set(sel["positions"].tolist()))
+                say(f"  budget {budget} unit {u}: {nd} positions differ, boundary gap {gap:.3g}")
+                assert gap <= SELECT_GAP
+        say(f"  budget {budget}: ok")
+
+
+# ------------------------------------------------------------------ decode
+
+
+@pytest.mark.parametrize("G,n_sink,recent,budget,K", [
+    (4, 16, 0, 1024, 48),
+    (4, 16, 37, 2048, 48),
+    (1, 16, 5, 256, 24),
+    (16, 16, 300, 2048, 41),
+    (2, 0, 3, 64, 30),
+    (4, 16, 11, 0, 20),
+    (3, 16, 0, 500, 33),
+    (4, 16, 2, 5000, 48),     # budget > m: full attention over every token
+])
+def test_decode_teacher_forced(G, n_sink, recent, budget, K):
+    say(f"case: decode G={G} n_sink={n_sink} recent={recent} budget={budget} K={K}")
+    units, nc = 3, n_sink + 4000
+    n_total = nc + recent
+    cap = n_total + 8
+    ks, vs, cs = [], [], []
+    for u in range(units):
+        kb, vb, c = synth.make_unit_inputs(77, u, n_total, 64, capacity=cap)
+        ks.append(kb), vs.append(vb), cs.append(c)
+    k, v, cen = np.stack(ks), np.stack(vs), np.stack(cs)
+    init = synth.make_init_indices(78, units, nc - n_sink, K)
+    states = [pipeline.prefill_unit(k[u], nc, init[u], K, 2, n_sink=n_sink, v_bits=v[u])
+              for u in range(units)]
+    q = synth.make_queries(79, cen, G)
+    L = gpu_layer(k, v, G, K, n_sink=n_sink, max_budget=max(budget, 1))
+    load_state(L, states, n_sink=n_sink)
+    L.set_counters(n_total, nc)
+    sel_pos = np.zeros((units, max(budget, 1)), np.int32)
+    cnt = np.zeros(units, np.int32)
+    sels = []
+    for u in range(units):
+        sel = pipeline.select_unit(q[u], states[u]["cmean"], states[u]["csize"], states[u]["offsets"],
+                                   states[u]["k_clu_bits"], budget)
+        sels.append(sel)
+        c = len(sel["positions"])
+        sel_pos[u, :c] = sel["positions"]
+        cnt[u] = c
+    out = torch.zeros((units, G, D), dtype=torch.float32, device="cuda")
+    L.sparse_decode(dev_bf16(q), to_dev(sel_pos, torch.int32), to_dev(cnt, torch.int32), budget, out)
+    torch.cuda.synchronize()
+    og = out.cpu().numpy()
+    for u in range(units):
+        ref = pipeline.decode_unit(q[u], k[u], v[u], states[u]["k_clu_bits"], states[u]["v_clu_bits"],
+                                   sels[u]["positions"], n_sink, nc, n_total)
+        err = np.abs(og[u] - ref).max()
+        say(f"  unit {u}: max abs err {err:.3g}")
+        assert err <= DECODE_ATOL
+
+
+# ------------------------------------------------------------------ incremental
+
+
+def test_incremental_teacher_forced():
+    cfg = synth.CONFIGS["llama8b-incremental-b16"]
+    say(f"case: incremental {cfg.name}, units 0-1")
+    units = [0, 1]
+    cap = cfg.n_tokens + cfg.new_tokens + 4
+    k, v, cen = synth.make_layer_inputs(cfg, units=units, capacity=cap)
+    init = synth.make_init_indices(cfg.init_seed, len(units), cfg.m, cfg.n_clusters)
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, 3, v_bits=v[u])
+              for u in range(len(units))]
+    kn, vn, newc = synth.make_new_tokens(cfg.data_seed, cen, cfg.new_tokens, cfg.new_components,
+                                         cfg.new_fraction)
+    L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.budget)
+    load_state(L, states)
+    L.set_counters(cfg.n_tokens, cfg.n_tokens)
+    kd, vd = dev_bf16(kn), dev_bf16(vn)
+    for i in range(cfg.new_tokens):
+        L.append(kd[:, i].contiguous(), vd[:, i].contiguous())
+    assert L.n_total == cfg.n_tokens + cfg.new_tokens
+    L.incremental()
+    assert L.n_clustered == L.n_total
+    cen_all = np.concatenate([cen, newc], axis=1)
+    q = synth.make_queries(cfg.query_seed, cen_all, cfg.group)
+    qd = dev_bf16(q)
+    sel_pos = torch.zeros((len(units), cfg.budget), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((len(units),), dtype=torch.int32, device="cuda")
+    out = torch.zeros((len(units), cfg.group, D), dtype=torch.float32, device="cuda")
+    L.select(qd, cfg.budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, cfg.budget, out)
+    torch.cuda.synchronize()
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    n_new = cfg.n_tokens + cfg.new_tokens
+    for u in range(len(units)):
+        kf = k[u].copy()
+        vf = v[u].copy()
+        kf[cfg.n_tokens:n_new] = kn[u]
+        vf[cfg.n_tokens:n_new] = vn[u]
+        assert np.array_equal(host_bits(L.k_tok[u, :n_new]), kf[:n_new])
+        ora = pipeline.incremental_unit(states[u], kf, n_new, v_bits=vf)
+        x_new = bf16.widen(kn[u])
+        a_g = L.assign[u, cfg.m:cfg.m + cfg.new_tokens].cpu().numpy()
+        mism, unexc = compare_assign(a_g, ora["new_assign"], x_new, states[u]["cdir"])
+        say(f"  unit {u}: new-token label mismatches {mism} (unexcused {unexc})")
+        assert unexc == 0
+        if mism:
+            continue
+        x_all = bf16.widen(kf[16:n_new])
+        assert check_state(L, u, ora, x_all, states[u]["cdir"], tag="incr") == 0
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"],
+                                   cfg.budget)
+        if compare_selection(L, u, sp, cn, ora, sel, cfg.budget) == 0:
+            ref = pipeline.decode_unit(q[u], kf, vf, ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
+                                       16, n_new, n_new)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+
+
+def test_incremental_noop():
+    say("case: incremental with no recent tokens")
+    cfg = synth.CONFIGS["single-head-2k"]
+    k, v, _ = synth.make_layer_inputs(cfg)
+    init = synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters)
+    L = gpu_layer(k, v, 1, cfg.n_clusters)
+    L.prefill(cfg.n_tokens, 3, to_dev(init, torch.int32))
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (L.cdir, L.csum, L.offsets, L.perm, L.k_clu)]
+    L.incremental()
+    torch.cuda.synchronize()
+    after = (L.cdir, L.csum, L.offsets, L.perm, L.k_clu)
+    for a, b in zip(before, after):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ edge cases
+
+
+@pytest.mark.parametrize("K,T", [(1, 3), (40, 5)])
+def test_edge_zero_and_duplicate_keys(K, T):
+    say(f"case: zero / duplicate keys K={K} T={T}")
+    n = 16 + 700 + 7
+    kb, vb, cen = synth.make_unit_inputs(91, 0, n, 8)
+    kb[40:60] = 0                        # zero keys: score 0 everywhere, label 0
+    kb[100:140] = kb[99]                 # duplicates of one key
+    rng = np.random.default_rng(5)
+    init = rng.choice(n - 16, K, replace=False).astype(np.int32)
+    if K > 3:
+        init[1] = 100 - 16                   # identical init directions -> empty clusters
+        init[2] = 101 - 16
+        init[3] = 45 - 16                    # a zero key as init -> zero direction
+    ora = pipeline.prefill_unit(kb, n, init, K, T, v_bits=vb, history=True)
+    L = gpu_layer(kb[None], vb[None], 1, K)
+    L.prefill(n, T, to_dev(init[None], torch.int32))
+    torch.cuda.synchronize()
+    x = bf16.widen(kb[16:n])
+    assert check_state(L, 0, ora, x, ora["history"][-2][1], tag="edge") == 0
+    if K > 3:
+        assert np.count_nonzero(ora["csize"] == 0) >= 1
+    q = synth.make_queries(92, cen[None], 1)
+    for budget in (0, 50, 723, 800):
+        sel_pos = torch.zeros((1, max(budget, 1)), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        L.select(dev_bf16(q), budget, sel_pos, cnt)
+        torch.cuda.synchronize()
+        sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+        compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
+
+
+def test_determinism():
+    say("case: bitwise determinism of prefill, select, decode")
+    cfg = synth.CONFIGS["single-head-2k"]
+    k, v, cen = synth.make_layer_inputs(cfg)
+    init = to_dev(synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters), torch.int32)
+    q = dev_bf16(synth.make_queries(cfg.query_seed, cen, 4))
+    outs = []
+    for _ in range(2):
+        L = gpu_layer(k, v, 4, cfg.n_clusters)
+        L.prefill(cfg.n_tokens, cfg.iters, init)
+        sel_pos = torch.zeros((1, cfg.budget), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        out = torch.zeros((1, 4, D), dtype=torch.float32, device="cuda")
+        L.select(q, cfg.budget, sel_pos, cnt)
+        L.sparse_decode(q, sel_pos, cnt, cfg.budget, out)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (L.assign, L.cdir, L.csum, L.cmean, L.perm, L.k_clu, sel_pos, out)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ full size
+
+
+def test_llama_stack_layer_full_size_sampled():
+    cfg = synth.CONFIGS["llama8b-stack-32k-b8"]
+    say(f"case: one full-size layer of {cfg.name} ({cfg.units} units), sampled units 5, 42")
+    k, v, cen = synth.make_layer_inputs(cfg)
+    init = synth.make_init_indices(cfg.init_seed, cfg.units, cfg.m, cfg.n_clusters)
+    q = synth.make_queries(cfg.query_seed, cen, cfg.group)
+    L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.budget)
+    del v
+    L.prefill(cfg.n_tokens, cfg.iters, to_dev(init, torch.int32))
+    qd = dev_bf16(q)
+    sel_pos = torch.zeros((cfg.units, cfg.budget), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((cfg.units,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((cfg.units, cfg.group, D), dtype=torch.float32, device="cuda")
+    L.select(qd, cfg.budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, cfg.budget, out)
+    torch.cuda.synchronize()
+    assert np.all(cnt.cpu().numpy() == cfg.budget)
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    for u in (5, 42):
+        _, vu, _ = synth.make_unit_inputs(cfg.data_seed, u, cfg.n_tokens, cfg.components)
+        ora = pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, cfg.iters, v_bits=vu,
+                                    history=True)
+        x = bf16.widen(k[u][16:cfg.n_tokens])
+        if check_state(L, u, ora, x, ora["history"][-2][1], tag="full") > MISMATCH_FRACTION * cfg.m:
+            pytest.fail("too many label mismatches")
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"],
+                                   cfg.budget)
+        if compare_selection(L, u, sp, cn, ora, sel, cfg.budget) == 0:
+            ref = pipeline.decode_unit(q[u], k[u], vu, ora["k_clu_bits"], ora["v_clu_bits"],
+                                       sel["positions"], 16, cfg.n_tokens, cfg.n_tokens)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
