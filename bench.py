@@ -65,7 +65,7 @@ def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
     n_units = n_unit_steps = 0
     deadline = time.perf_counter() + seconds
     u = 0
-    while time.perf_counter() < deadline and u < 4:
+    while time.perf_counter() < deadline and u < 64:
         kb, vb, cen = synth.make_unit_inputs(cfg.data_seed, u, cfg.n_tokens, cfg.components)
         init = synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters, unit_ids=[u])[0]
         t0 = time.perf_counter()
@@ -105,6 +105,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -112,6 +114,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "copies": 5}), flush=True)
+        return 0
 
     import synth
     from synth import device as dgen
@@ -239,7 +251,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "layers": n_layers, "batch": cfg.batch, "kv_heads": cfg.n_kv_heads,
                    "group": G, "context": cfg.n_tokens, "clusters": cfg.n_clusters, "budget": budget,
                    "graphs": not args.no_graph},
-        "roofline": {"bound": "hbm", "kernel": "ckv_sparse_decode (decode_split + decode_combine)",
+        "roofline": {"bound": "hbm", "kernel": "ckv::sparse_decode_kernel<4>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},

@@ -34,11 +34,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   size_t counters;  // reserved, kept zero
   size_t hist;      // prefill / incremental: [units, tiles, K] int32
+  size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
   size_t scores;    // select: [units, K] f32
   size_t cut;       // select: [units, clu_cap] u32 keys of the cut cluster
   size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
   size_t total;
-  size_t off_hist, off_scores, off_cut, off_partials;
+  size_t off_hist, off_invn, off_scores, off_cut, off_partials;
 };
 
 int group_tier(int g) {
@@ -54,14 +55,16 @@ Layout layout_of(const ckv_layer* L) {
   Layout w;
   w.counters = align256(units * 2 * sizeof(uint32_t));
   w.hist = align256(units * tiles * L->n_clusters * sizeof(int32_t));
+  w.invn = align256(units * clu_cap * sizeof(double));
   w.scores = align256(units * L->n_clusters * sizeof(float));
   w.cut = align256(units * clu_cap * sizeof(uint32_t));
   w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
   w.off_hist = w.counters;
+  w.off_invn = w.counters + w.hist;
   w.off_scores = w.counters;
   w.off_cut = w.counters + w.scores;
   w.off_partials = w.counters;
-  size_t body = w.hist;
+  size_t body = w.hist + w.invn;
   if (w.scores + w.cut > body) body = w.scores + w.cut;
   if (w.partials > body) body = w.partials;
   w.total = w.counters + body;
@@ -159,8 +162,12 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
   const Layout w = layout_of(L);
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
 
+  double* invn = (double*)((char*)ws + w.off_invn);
+
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
   if (e != hipSuccess) return hip_status(e, "init");
+  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, 0, m, invn, clu_stride, units, s);
+  if (e != hipSuccess) return hip_status(e, "norms");
   for (int it = 0; it < iters; ++it) {
     e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s);
     if (e != hipSuccess) return hip_status(e, "assign");
@@ -169,8 +176,8 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
     e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
     if (e != hipSuccess) return hip_status(e, "scatter");
     const int mode = (it == iters - 1) ? ckv::kUpdFinal : ckv::kUpdIter;
-    e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->perm, clu_stride, L->offsets, K, L->csum,
-                           L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s);
+    e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K,
+                           invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s);
     if (e != hipSuccess) return hip_status(e, "update");
   }
   L->n_total = n;
@@ -215,15 +222,20 @@ int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* strea
   const Layout w = layout_of(L);
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
 
+  double* invn = (double*)((char*)ws + w.off_invn);
+
   hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
                                     clu_stride, m_old, units, s);
   if (e != hipSuccess) return hip_status(e, "assign");
+  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, m_old, m_new, invn, clu_stride, units, s);
+  if (e != hipSuccess) return hip_status(e, "norms");
   e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
   if (e != hipSuccess) return hip_status(e, "hist");
   e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
   if (e != hipSuccess) return hip_status(e, "scatter");
-  e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->perm, clu_stride, L->offsets, K,
-                         L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu_alt, L->v_clu_alt, units, s);
+  e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets,
+                         K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu_alt, L->v_clu_alt, units,
+                         s);
   if (e != hipSuccess) return hip_status(e, "update");
   uint16_t* tk = L->k_clu;
   uint16_t* tv = L->v_clu;
@@ -276,20 +288,19 @@ int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_
   if (rc) return rc;
   const int units = L->batch * L->n_kv_heads;
   const long long rmax = (long long)L->n_sink + cmax + (L->n_total - L->n_clustered);
-  // Split-K heuristic: about 4 workgroups per CU over the whole launch, at least
-  // 64 rows per chunk, at most kMaxChunks chunks per unit.
-  long long chunk = (rmax * units + 1023) / 1024;
-  if (chunk < 64) chunk = 64;
+  // Split-K: chunks of whole row-group batches (every row group loads all of
+  // its rows of a batch at once), at most kMaxChunks chunks per unit.
+  const long long batch = ckv::decode_rows_per_batch(L->group);
+  long long chunk = batch;
   const long long min_chunk = (rmax + ckv::kMaxChunks - 1) / ckv::kMaxChunks;
-  if (chunk < min_chunk) chunk = min_chunk;
-  chunk = (chunk + 15) / 16 * 16;
+  if (chunk < min_chunk) chunk = (min_chunk + batch - 1) / batch * batch;
   long long n_chunks = (rmax + chunk - 1) / chunk;
   if (n_chunks < 1) n_chunks = 1;
   const Layout w = layout_of(L);
   hipError_t e = ckv::launch_sparse_decode(
       q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
       sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
-      (float*)((char*)ws + w.off_partials), out, units, (hipStream_t)stream);
+      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, out, units, (hipStream_t)stream);
   return hip_status(e, "sparse_decode");
 }
 

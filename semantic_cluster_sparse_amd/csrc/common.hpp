@@ -51,6 +51,37 @@ __device__ __forceinline__ T xor_sum16(T v) {
   return v;
 }
 
+// DPP move within rows of 16 lanes (gfx9 dpp_ctrl encodings).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+// Sum over each row of 16 lanes; every lane of the row gets the same
+// (bitwise identical) value because each step adds commutative pairs.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = (int)__lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 // Exclusive prefix sum over a block of `nthreads` threads (nthreads <= 1024,
 // multiple of 64).  `scratch` needs nthreads/64 + 1 ints of LDS.  Returns the
 // exclusive prefix of `v` and writes the block total to *total.

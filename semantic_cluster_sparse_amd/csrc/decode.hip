@@ -15,37 +15,21 @@
 
 namespace ckv {
 
-template <int DPL>
-struct RowPart;
-template <>
-struct RowPart<8> {
-  typedef uint4 T;
-  __device__ static __forceinline__ void unpack(const T& w, float* x) {
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  }
-};
-template <>
-struct RowPart<4> {
-  typedef uint2 T;
-  __device__ static __forceinline__ void unpack(const T& w, float* x) {
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-  }
-};
-template <>
-struct RowPart<2> {
-  typedef uint32_t T;
-  __device__ static __forceinline__ void unpack(const T& w, float* x) {
-    x[0] = bf16_lo(w); x[1] = bf16_hi(w);
-  }
-};
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
 }
+
+constexpr int kDecThreads = 256;
+constexpr int kDecGroups = kDecThreads / 16;  // row groups of 16 lanes (8 dims per lane)
+
+// Rows per row group per batch: all are loaded before any arithmetic.
+template <int GT>
+struct DecRows {
+  static constexpr int U = GT <= 4 ? 8 : (GT == 8 ? 4 : 2);
+};
 
 __device__ __forceinline__ void merge_state(float& m, float& l, float mo, float lo, float& a_self,
                                             float& a_other) {
@@ -57,132 +41,143 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float mo, float 
   m = M;
 }
 
-constexpr int kDecThreads = 256;
-
-template <int GT, int LPR>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+// One workgroup per (unit, chunk of attended rows).  Row r of the attended
+// sequence is a sink (r < n_sink), a recalled row of the cluster-ordered copy
+// (r < n_sink + cnt, position sel_pos[r - n_sink]) or a recent row.  Each
+// workgroup leaves per head (max, sum, unnormalised output) in `partials`;
+// the last workgroup of the unit to finish (arrival counter in `counters`,
+// reset to 0 by that workgroup) merges them into `out`.
+template <int GT>
+__global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, int G, const uint16_t* __restrict__ k_tok,
     const uint16_t* __restrict__ v_tok, int capacity, const uint16_t* __restrict__ k_clu,
     const uint16_t* __restrict__ v_clu, int clu_stride, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_count, int budget, int m, int n_sink, int n_clustered,
-    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials) {
-  constexpr int DPL = kHeadDim / LPR;
-  constexpr int NG = kDecThreads / LPR;      // row groups per workgroup
-  constexpr int kDecUnroll = (GT >= 8) ? 2 : 4;  // rows in flight per row group
-  typedef typename RowPart<DPL>::T PartT;
-  __shared__ float red[kDecThreads / kWave][GT][kPartialStride];
+    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials,
+    uint32_t* __restrict__ counters, float* __restrict__ out) {
+  constexpr int U = DecRows<GT>::U;
+  constexpr int NW = kDecThreads / kWave;
+  __shared__ float red[NW][GT][kPartialStride];
+  __shared__ int sh_last;
+  __shared__ int rowsrc[kDecGroups * DecRows<GT>::U];
 
   const int u = blockIdx.x / n_chunks;
   const int c = blockIdx.x % n_chunks;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int li = lane % LPR;
-  const int gi = tid / LPR;
+  const int li = tid & 15;
+  const int gi = tid >> 4;
+
+  uint4 qw[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+    qw[h] = h < G ? *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8)
+                  : make_uint4(0, 0, 0, 0);
 
   int cnt = sel_count[u];
   const int cmax = budget < m ? budget : m;
   cnt = cnt < 0 ? 0 : (cnt > cmax ? cmax : cnt);
-  const int R = n_sink + cnt + (n_total - n_clustered);
+  const int sel_end = n_sink + cnt;
+  const int R = sel_end + (n_total - n_clustered);
   const int r0 = c * chunk_rows;
   const int r1 = min(R, r0 + chunk_rows);
 
-  const float qscale = 0.12751743074602468f;  // log2(e) / sqrt(128)
-  float qv[GT][DPL];
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    if (h < G) {
-      const PartT w = *reinterpret_cast<const PartT*>(q + ((size_t)u * G + h) * kHeadDim + li * DPL);
-      RowPart<DPL>::unpack(w, qv[h]);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[h][e] *= qscale;
-    } else {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[h][e] = 0.f;
-    }
-  }
-
-  float mx[GT], ls[GT], acc[GT][DPL];
+  const float qscale = 0.12751743074602468f;  // log2(e) / sqrt(128): scores in the log2 domain
+  float mx[GT], ls[GT], acc[GT][8];
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
     mx[h] = -INFINITY;
     ls[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
-  const size_t tok_base = (size_t)u * capacity * kHeadDim;
-  const size_t clu_base = (size_t)u * clu_stride * kHeadDim;
-  const int32_t* sp = sel_pos + (size_t)u * budget;
-  const int sel_end = n_sink + cnt;
+  const uint16_t* ktu = k_tok + (size_t)u * capacity * kHeadDim + li * 8;
+  const uint16_t* vtu = v_tok + (size_t)u * capacity * kHeadDim + li * 8;
+  const uint16_t* kcu = k_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
+  const uint16_t* vcu = v_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
+  const int32_t* sp = sel_pos + (size_t)u * budget - n_sink;
 
-  for (int base = r0 + gi; base < r1; base += NG * kDecUnroll) {
-    PartT kw[kDecUnroll], vw[kDecUnroll];
-    bool ok[kDecUnroll];
-#pragma unroll
-    for (int k = 0; k < kDecUnroll; ++k) {
-      const int r = base + k * NG;
-      ok[k] = r < r1;
-      size_t off;
-      const uint16_t *kb, *vb;
-      if (!ok[k] || r < n_sink) {
-        off = tok_base + (size_t)(ok[k] ? r : 0) * kHeadDim;
-        kb = k_tok;
-        vb = v_tok;
-      } else if (r < sel_end) {
-        int p = sp[r - n_sink];
-        p = p < 0 ? 0 : (p >= m ? m - 1 : p);
-        off = clu_base + (size_t)p * kHeadDim;
-        kb = k_clu;
-        vb = v_clu;
-      } else {
-        off = tok_base + (size_t)(n_clustered + (r - sel_end)) * kHeadDim;
-        kb = k_tok;
-        vb = v_tok;
+  // Rows of a batch are staged as source indices in LDS (one coalesced load of
+  // sel_pos per batch), so every row load of the batch issues back to back.
+  constexpr int kBatch = kDecGroups * U;
+  constexpr int kCluFlag = 0x40000000;
+  for (int bs = r0; bs < r1; bs += kBatch) {
+    if (tid < kBatch) {
+      const int r = bs + tid;
+      int v = 0;
+      if (r < r1) {
+        if (r < n_sink) {
+          v = r;
+        } else if (r < sel_end) {
+          int p = sp[r];
+          p = p < 0 ? 0 : (p >= m ? m - 1 : p);
+          v = p | kCluFlag;
+        } else {
+          v = n_clustered + (r - sel_end);
+        }
       }
-      kw[k] = *reinterpret_cast<const PartT*>(kb + off + li * DPL);
-      vw[k] = *reinterpret_cast<const PartT*>(vb + off + li * DPL);
+      rowsrc[tid] = v;
     }
-    float s[kDecUnroll][GT];
+    __syncthreads();
+    uint4 kr[U], vr[U];
 #pragma unroll
-    for (int k = 0; k < kDecUnroll; ++k) {
-      float x[DPL];
-      RowPart<DPL>::unpack(kw[k], x);
+    for (int k = 0; k < U; ++k) {
+      const int v = rowsrc[gi + k * kDecGroups];
+      const bool clu = (v & kCluFlag) != 0;
+      const size_t row = (size_t)(v & (kCluFlag - 1)) * kHeadDim;
+      kr[k] = *reinterpret_cast<const uint4*>((clu ? kcu : ktu) + row);
+      vr[k] = *reinterpret_cast<const uint4*>((clu ? vcu : vtu) + row);
+    }
+    __syncthreads();
+    // keep the scheduler from interleaving math between the row loads
+    __builtin_amdgcn_sched_barrier(0);
+    const int b0 = bs + gi;
+    float s[U][GT];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const bool ok = b0 + k * kDecGroups < r1;
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) d = fmaf(qv[h][e], x[e], d);
-        d = row_sum<LPR>(d);
-        s[k][h] = ok[k] ? d : -INFINITY;
+        float d = dot2(kr[k].x, qw[h].x, 0.f);
+        d = dot2(kr[k].y, qw[h].y, d);
+        d = dot2(kr[k].z, qw[h].z, d);
+        d = dot2(kr[k].w, qw[h].w, d);
+        d = sum16(d);
+        s[k][h] = ok ? d * qscale : -INFINITY;
       }
     }
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       float mn = mx[h];
 #pragma unroll
-      for (int k = 0; k < kDecUnroll; ++k) mn = fmaxf(mn, s[k][h]);
+      for (int k = 0; k < U; ++k) mn = fmaxf(mn, s[k][h]);
       const float ms = (mn == -INFINITY) ? 0.f : mn;
       const float alpha = exp2f(mx[h] - ms);
       ls[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
       mx[h] = mn;
 #pragma unroll
-      for (int k = 0; k < kDecUnroll; ++k) {
+      for (int k = 0; k < U; ++k) {
         const float p = exp2f(s[k][h] - ms);
         ls[h] += p;
-        float v[DPL];
-        RowPart<DPL>::unpack(vw[k], v);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+        acc[h][0] = fmaf(p, bf16_lo(vr[k].x), acc[h][0]);
+        acc[h][1] = fmaf(p, bf16_hi(vr[k].x), acc[h][1]);
+        acc[h][2] = fmaf(p, bf16_lo(vr[k].y), acc[h][2]);
+        acc[h][3] = fmaf(p, bf16_hi(vr[k].y), acc[h][3]);
+        acc[h][4] = fmaf(p, bf16_lo(vr[k].z), acc[h][4]);
+        acc[h][5] = fmaf(p, bf16_hi(vr[k].z), acc[h][5]);
+        acc[h][6] = fmaf(p, bf16_lo(vr[k].w), acc[h][6]);
+        acc[h][7] = fmaf(p, bf16_hi(vr[k].w), acc[h][7]);
       }
     }
   }
 
-  // merge the row groups of this wave (lanes differing in the bits above LPR)
+  // merge the 4 row groups of this wave (lane bits 4 and 5)
 #pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1) {
+  for (int o = 16; o < kWave; o <<= 1) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       const float mo = __shfl_xor(mx[h], o);
@@ -190,17 +185,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       float as, ao;
       merge_state(mx[h], ls[h], mo, lo, as, ao);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const float other = __shfl_xor(acc[h][e], o);
         acc[h][e] = acc[h][e] * as + other * ao;
       }
     }
   }
-  if (lane < LPR) {
+  if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) red[wave][h][li * DPL + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) red[wave][h][li * 8 + e] = acc[h][e];
       if (lane == 0) {
         red[wave][h][kHeadDim] = mx[h];
         red[wave][h][kHeadDim + 1] = ls[h];
@@ -208,8 +203,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
   }
   __syncthreads();
-  constexpr int NW = kDecThreads / kWave;
-  float* outp = partials + ((size_t)u * n_chunks + c) * GT * kPartialStride;
+  float* pu = partials + (size_t)u * n_chunks * GT * kPartialStride;
+  float* outp = pu + (size_t)c * GT * kPartialStride;
   for (int t = tid; t < GT * kHeadDim; t += kDecThreads) {
     const int h = t / kHeadDim, d = t % kHeadDim;
     float M = -INFINITY;
@@ -229,38 +224,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       outp[h * kPartialStride + kHeadDim + 1] = L;
     }
   }
-}
 
-// One workgroup of 128 threads per (unit, head): log-sum-exp merge of the chunks.
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ partials,
-                                                             int GT, int G, int n_chunks,
-                                                             float* __restrict__ out) {
-  const int u = blockIdx.x / G;
-  const int h = blockIdx.x % G;
-  const int d = threadIdx.x;
-  const float* p = partials + (size_t)u * n_chunks * GT * kPartialStride + h * kPartialStride;
-  const size_t cs = (size_t)GT * kPartialStride;
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[c * cs + kHeadDim]);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float a = exp2f(p[c * cs + kHeadDim] - Ms);
-    L += p[c * cs + kHeadDim + 1] * a;
-    O += p[c * cs + d] * a;
+  // arrival: the last chunk of this unit merges every chunk's partial
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&counters[u], 1u);
+    sh_last = (prev == (uint32_t)(n_chunks - 1)) ? 1 : 0;
   }
-  out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
-}
-
-template <int GT, int LPR>
-static void launch_split(dim3 grid, hipStream_t s, const uint16_t* q, int G, const uint16_t* k_tok,
-                         const uint16_t* v_tok, int capacity, const uint16_t* k_clu,
-                         const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
-                         const int32_t* sel_count, int budget, int m, int n_sink, int n_clustered,
-                         int n_total, int chunk_rows, int n_chunks, float* partials) {
-  hipLaunchKernelGGL((decode_split_kernel<GT, LPR>), grid, dim3(kDecThreads), 0, s, q, G, k_tok,
-                     v_tok, capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m,
-                     n_sink, n_clustered, n_total, chunk_rows, n_chunks, partials);
+  __syncthreads();
+  if (!sh_last) return;
+  __threadfence();
+  const size_t cs = (size_t)GT * kPartialStride;
+  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
+    const int h = t / kHeadDim, d = t % kHeadDim;
+    const float* p = pu + h * kPartialStride;
+    float M = -INFINITY;
+    for (int cc = 0; cc < n_chunks; ++cc) M = fmaxf(M, __builtin_nontemporal_load(p + cc * cs + kHeadDim));
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+    for (int cc = 0; cc < n_chunks; ++cc) {
+      const float a = exp2f(__builtin_nontemporal_load(p + cc * cs + kHeadDim) - Ms);
+      L += __builtin_nontemporal_load(p + cc * cs + kHeadDim + 1) * a;
+      O += __builtin_nontemporal_load(p + cc * cs + d) * a;
+    }
+    out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  }
+  if (tid == 0) counters[u] = 0u;
 }
 
 static int group_tier(int G) {
@@ -269,30 +259,36 @@ static int group_tier(int G) {
   return gt;
 }
 
+int decode_rows_per_batch(int G) {
+  switch (group_tier(G)) {
+    case 1: return kDecGroups * DecRows<1>::U;
+    case 2: return kDecGroups * DecRows<2>::U;
+    case 4: return kDecGroups * DecRows<4>::U;
+    case 8: return kDecGroups * DecRows<8>::U;
+    default: return kDecGroups * DecRows<16>::U;
+  }
+}
+
 hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
                                 const uint16_t* v_tok, int capacity, const uint16_t* k_clu,
                                 const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
-                                float* partials, float* out, int units, hipStream_t s) {
+                                float* partials, uint32_t* counters, float* out, int units,
+                                hipStream_t s) {
   const dim3 grid((unsigned)(units * n_chunks));
-  const int gt = group_tier(G);
-#define CKV_SPLIT(GTV, LPRV)                                                                      \
-  launch_split<GTV, LPRV>(grid, s, q, G, k_tok, v_tok, capacity, k_clu, v_clu, clu_stride,       \
-                          sel_pos, sel_count, budget, m, n_sink, n_clustered, n_total, chunk_rows, \
-                          n_chunks, partials)
-  switch (gt) {
-    case 1: CKV_SPLIT(1, 16); break;
-    case 2: CKV_SPLIT(2, 16); break;
-    case 4: CKV_SPLIT(4, 16); break;
-    case 8: CKV_SPLIT(8, 32); break;
-    default: CKV_SPLIT(16, 32); break;
+#define CKV_DEC(GTV)                                                                                \
+  hipLaunchKernelGGL(sparse_decode_kernel<GTV>, grid, dim3(kDecThreads), 0, s, q, G, k_tok, v_tok, \
+                     capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m, n_sink,     \
+                     n_clustered, n_total, chunk_rows, n_chunks, partials, counters, out)
+  switch (group_tier(G)) {
+    case 1: CKV_DEC(1); break;
+    case 2: CKV_DEC(2); break;
+    case 4: CKV_DEC(4); break;
+    case 8: CKV_DEC(8); break;
+    default: CKV_DEC(16); break;
   }
-#undef CKV_SPLIT
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(units * G)), dim3(128), 0, s, partials, gt,
-                     G, n_chunks, out);
+#undef CKV_DEC
   return hipGetLastError();
 }
 

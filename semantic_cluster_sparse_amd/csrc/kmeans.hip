@@ -103,27 +103,51 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
       *reinterpret_cast<uint4*>(cs + row * kAsLds + ch * 8) = v;
     }
     __syncthreads();
-    for (int t = 0; t < ntile; ++t) {
+    // Full 16-direction tiles are software-pipelined: the MFMAs of tile t are
+    // issued before the argmax of tile t-1, so the VALU epilogue overlaps them.
+    const int nfull = nc >> 4;
+    f32x4 acc[kAsMt], nxt[kAsMt];
+    auto mfma_tile = [&](int t, f32x4* out) {
       bf16x8 b[4];
       const uint16_t* bp = cs + (t * 16 + r16) * kAsLds + kg * 8;
 #pragma unroll
       for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(bp + s * 32);
-      const int j = c0 + t * 16 + r16;
-      const bool jv = (t * 16 + r16) < nc;
 #pragma unroll
-      for (int mt = 0; mt < kAsMt; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < kAsMt; ++mt) out[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], acc, 0, 0, 0);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt)
+          out[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], out[mt], 0, 0, 0);
+    };
+    auto argmax_tile = [&](const f32x4* in, int j) {
+#pragma unroll
+      for (int mt = 0; mt < kAsMt; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = jv ? acc[i] : -INFINITY;
-          if (v > best[mt][i]) {
-            best[mt][i] = v;
-            bidx[mt][i] = j;
-          }
+          const float v = in[mt][i];
+          const bool gt = v > best[mt][i];
+          best[mt][i] = gt ? v : best[mt][i];
+          bidx[mt][i] = gt ? j : bidx[mt][i];
         }
+    };
+    if (nfull > 0) {
+      mfma_tile(0, acc);
+      for (int t = 1; t < nfull; ++t) {
+        mfma_tile(t, nxt);
+        argmax_tile(acc, c0 + (t - 1) * 16 + r16);
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = nxt[mt];
       }
+      argmax_tile(acc, c0 + (nfull - 1) * 16 + r16);
+    }
+    if (nc & 15) {  // last partial tile: columns past nc are padding
+      mfma_tile(nfull, acc);
+      if (nfull * 16 + r16 >= nc) {
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      argmax_tile(acc, c0 + nfull * 16 + r16);
     }
   }
 
@@ -274,20 +298,48 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Update: one wave per (unit, cluster).  Four rows per step (16 lanes x 8 dims
-// each).  Sums in f64: S_j = sum x/|x|, M_j = sum x.  Iteration mode rebuilds
-// S from scratch and refreshes the direction; final mode also writes M, the
-// mean and the cluster-ordered K/V rows; incremental mode adds only the
-// members past the old size (new tokens sort last in their cluster), keeps
-// the old sums, refreshes touched clusters and rewrites every row.
+// Inverse key norms 1/|x| (f64) of clustered tokens [first, first + count):
+// 16 lanes per row.  Computed once per prefill / incremental call; the
+// update kernels reuse them every Lloyd round.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restrict__ k_tok, int capacity,
+                                                       int n_sink, int first, int count,
+                                                       double* __restrict__ invn, int clu_stride,
+                                                       int rows_per_unit_blocks) {
+  const int u = blockIdx.x / rows_per_unit_blocks;
+  const int b = blockIdx.x % rows_per_unit_blocks;
+  const int li = threadIdx.x & 15;
+  const int i = b * 16 + (threadIdx.x >> 4);
+  const bool ok = i < count;
+  const int tok = n_sink + first + (ok ? i : 0);
+  const uint4 w = *reinterpret_cast<const uint4*>(k_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
+  double x[8];
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  double n2 = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
+  n2 = xor_sum16(n2);
+  if (ok && li == 0) invn[(size_t)u * clu_stride + first + i] = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+}
+
+// ---------------------------------------------------------------------------
+// Update: one wave per (unit, cluster); 16 member rows per step, one row per
+// 16-lane group at a time (8 dims per lane), all 4 row loads of a group issued
+// together.  Sums in f64: S_j = sum x/|x| (with the precomputed 1/|x|),
+// M_j = sum x.  Iteration mode rebuilds S from scratch and refreshes the
+// direction; final mode also writes M, the mean and the cluster-ordered K/V
+// rows; incremental mode adds only the members past the old size (new tokens
+// sort last in their cluster), keeps the old sums, refreshes touched clusters
+// and rewrites every row.
 // ---------------------------------------------------------------------------
 template <int MODE>
 __global__ __launch_bounds__(256) void update_kernel(
-    const uint16_t* __restrict__ k_tok, const uint16_t* __restrict__ v_tok, int capacity,
+    const uint16_t* __restrict__ k_tok, const uint16_t* __restrict__ v_tok, int capacity, int n_sink,
     const int32_t* __restrict__ perm, int clu_stride, const int32_t* __restrict__ offsets, int K,
-    double* __restrict__ csum, double* __restrict__ msum, float* __restrict__ cmean,
-    int32_t* __restrict__ csize, uint16_t* __restrict__ cdir, uint16_t* __restrict__ k_dst,
-    uint16_t* __restrict__ v_dst, int units) {
+    const double* __restrict__ invn, double* __restrict__ csum, double* __restrict__ msum,
+    float* __restrict__ cmean, int32_t* __restrict__ csize, uint16_t* __restrict__ cdir,
+    uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, int units) {
   const int lane = lane_id();
   const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= (long)units * K) return;
@@ -307,29 +359,51 @@ __global__ __launch_bounds__(256) void update_kernel(
   for (int t = 0; t < 8; ++t) s[t] = mm[t] = 0.0;
 
   const int32_t* pu = perm + (size_t)u * clu_stride;
-  for (int p = lo + g; p < hi; p += 4) {
-    int tok = pu[p];
-    tok = tok < 0 ? 0 : (tok >= capacity ? capacity - 1 : tok);
-    const uint4 kx = *reinterpret_cast<const uint4*>(k_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
-    if (MODE != kUpdIter) {
-      const uint4 vx = *reinterpret_cast<const uint4*>(v_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
-      *reinterpret_cast<uint4*>(k_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = kx;
-      *reinterpret_cast<uint4*>(v_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = vx;
+  const double* iu = invn + (size_t)u * clu_stride;
+  const uint16_t* ku = k_tok + (size_t)u * capacity * kHeadDim + li * 8;
+  const uint16_t* vu = v_tok + (size_t)u * capacity * kHeadDim + li * 8;
+  for (int p0 = lo; p0 < hi; p0 += 16) {
+    int tk = 0;
+    double iv = 0.0;
+    const int pl = p0 + lane;
+    if (lane < 16 && pl < hi) {
+      tk = pu[pl];
+      tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
+      if (pl >= acc_from) iv = iu[tk - n_sink];
     }
-    double x[8];
-    x[0] = bf16_lo(kx.x); x[1] = bf16_hi(kx.x);
-    x[2] = bf16_lo(kx.y); x[3] = bf16_hi(kx.y);
-    x[4] = bf16_lo(kx.z); x[5] = bf16_hi(kx.z);
-    x[6] = bf16_lo(kx.w); x[7] = bf16_hi(kx.w);
-    double n2 = 0.0;
+    int tks[4];
+    double ivs[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
-    n2 = xor_sum16(n2);
-    if (p >= acc_from) {
-      const double inv = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+    for (int k = 0; k < 4; ++k) {
+      tks[k] = __shfl(tk, 4 * k + g);
+      ivs[k] = __shfl(iv, 4 * k + g);
+    }
+    uint4 kx[4], vx[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 4 * k + g;
+      if (p < hi) {
+        kx[k] = *reinterpret_cast<const uint4*>(ku + (size_t)tks[k] * kHeadDim);
+        if (MODE != kUpdIter) vx[k] = *reinterpret_cast<const uint4*>(vu + (size_t)tks[k] * kHeadDim);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 4 * k + g;
+      if (p >= hi) continue;
+      if (MODE != kUpdIter) {
+        *reinterpret_cast<uint4*>(k_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = kx[k];
+        *reinterpret_cast<uint4*>(v_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = vx[k];
+      }
+      if (p < acc_from) continue;
+      double x[8];
+      x[0] = bf16_lo(kx[k].x); x[1] = bf16_hi(kx[k].x);
+      x[2] = bf16_lo(kx[k].y); x[3] = bf16_hi(kx[k].y);
+      x[4] = bf16_lo(kx[k].z); x[5] = bf16_hi(kx[k].z);
+      x[6] = bf16_lo(kx[k].w); x[7] = bf16_hi(kx[k].w);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        s[t] += x[t] * inv;
+        s[t] = fma(x[t], ivs[k], s[t]);
         if (MODE != kUpdIter) mm[t] += x[t];
       }
     }
@@ -417,22 +491,31 @@ hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int 
   return hipGetLastError();
 }
 
-hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity,
+hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int first, int count,
+                           double* invn, int clu_stride, int units, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int blocks = (count + 15) / 16;
+  hipLaunchKernelGGL(inv_norm_kernel, dim3((unsigned)(units * blocks)), dim3(256), 0, s, k_tok, capacity,
+                     n_sink, first, count, invn, clu_stride, blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity, int n_sink,
                          const int32_t* perm, int clu_stride, const int32_t* offsets, int K,
-                         double* csum, double* msum, float* cmean, int32_t* csize,
-                         uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units,
-                         hipStream_t s) {
+                         const double* invn, double* csum, double* msum, float* cmean, int32_t* csize,
+                         uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units, hipStream_t s) {
   const long waves = (long)units * K;
   const dim3 grid((unsigned)((waves + 3) / 4));
+#define CKV_UPD(M)                                                                                  \
+  hipLaunchKernelGGL(update_kernel<M>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, n_sink, perm, \
+                     clu_stride, offsets, K, invn, csum, msum, cmean, csize, cdir, k_dst, v_dst, units)
   if (mode == kUpdIter)
-    hipLaunchKernelGGL(update_kernel<kUpdIter>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
-                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+    CKV_UPD(kUpdIter);
   else if (mode == kUpdFinal)
-    hipLaunchKernelGGL(update_kernel<kUpdFinal>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
-                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+    CKV_UPD(kUpdFinal);
   else
-    hipLaunchKernelGGL(update_kernel<kUpdIncr>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, perm,
-                       clu_stride, offsets, K, csum, msum, cmean, csize, cdir, k_dst, v_dst, units);
+    CKV_UPD(kUpdIncr);
+#undef CKV_UPD
   return hipGetLastError();
 }
 

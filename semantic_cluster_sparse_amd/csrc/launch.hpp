@@ -35,12 +35,16 @@ hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int 
                           const int32_t* hist, int tiles, int n_sink, int32_t* perm,
                           int32_t* offsets, int units, hipStream_t s);
 
+// 1/|x| (f64) of clustered tokens [first, first + count) into invn[u, first + i].
+hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int first, int count,
+                           double* invn, int clu_stride, int units, hipStream_t s);
+
 // Per-cluster segmented reduction over the members listed by perm/offsets.
-hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
-                         int capacity, const int32_t* perm, int clu_stride,
-                         const int32_t* offsets, int K, double* csum, double* msum,
-                         float* cmean, int32_t* csize, uint16_t* cdir, uint16_t* k_dst,
-                         uint16_t* v_dst, int units, hipStream_t s);
+hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity,
+                         int n_sink, const int32_t* perm, int clu_stride, const int32_t* offsets,
+                         int K, const double* invn, double* csum, double* msum, float* cmean,
+                         int32_t* csize, uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst,
+                         int units, hipStream_t s);
 
 // Recall: cluster scores, then rank / prefix / cut / partial top-k per unit.
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
@@ -48,13 +52,16 @@ hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
                          int budget, int32_t* sel_pos, int32_t* sel_count, float* scores_ws,
                          uint32_t* cut_ws, int units, hipStream_t s);
 
-// Split-K sparse decode plus the log-sum-exp merge of the chunk partials.
+// Split-K sparse decode with the log-sum-exp merge of the chunk partials
+// fused in (per-unit arrival counters, zero before and after every launch).
+int decode_rows_per_batch(int group);
 hipError_t launch_sparse_decode(const uint16_t* q, int group, const uint16_t* k_tok,
                                 const uint16_t* v_tok, int capacity, const uint16_t* k_clu,
                                 const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
-                                float* partials, float* out, int units, hipStream_t s);
+                                float* partials, uint32_t* counters, float* out, int units,
+                                hipStream_t s);
 
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok,
                          uint16_t* v_tok, int capacity, int row, int units, hipStream_t s);

@@ -2,31 +2,80 @@
 // ClusterKV的语义空间优化", §3.3; §3.1 motivates ranking clusters by q.mu).
 //
 // Per unit (one KV head of one sequence): q_bar = sum of the group's query
-// heads; cluster score s_j = q_bar . mu_j (-inf for an empty cluster);
+// heads; cluster score s_j = q_bar . mu_j (an empty cluster never scores);
 // clusters in descending score (ties: smaller j) are taken whole while they
 // fit; the first that does not fit contributes its highest q_bar.k tokens
 // (ties: smaller position) so exactly min(budget, m) tokens are recalled.
 //
-// Two kernels: a wide scoring pass (16 lanes per centroid row, many
-// workgroups per unit) and one workgroup per unit for rank, prefix sum, cut
-// and a 4-pass radix select inside the cut cluster.
+// The walk in score order is a weighted selection: the cut cluster is the one
+// whose score key T splits the clusters into those above T (taken whole,
+// total size <= budget) and the rest.  It is found without sorting by a
+// wave-synchronous radix select on order-preserving 32-bit score keys with
+// cluster sizes as weights (4 passes of 8 bits); the partial fill inside the
+// cut cluster is the same select with unit weights.  One workgroup of 512
+// threads per unit, three block barriers.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ckv {
 
-constexpr int kScorePerWg = 64;
+constexpr int kSelThreads = 512;
+constexpr int kSelGroups = kSelThreads / 16;  // 16-lane row groups
+constexpr int kCutLds = 4096;                 // cut-cluster keys kept in LDS up to this size
 
-__global__ __launch_bounds__(256) void select_score_kernel(const uint16_t* __restrict__ q, int G,
-                                                           const float* __restrict__ cmean,
-                                                           const int32_t* __restrict__ offsets,
-                                                           int K, float* __restrict__ scores,
-                                                           int tiles) {
-  const int u = blockIdx.x / tiles;
-  const int t = blockIdx.x % tiles;
-  const int li = threadIdx.x & 15;
-  const int grp = threadIdx.x >> 4;
-  float qb[8];
+// Order-preserving map of an f32 score to u32 (larger score -> larger key);
+// -0 maps as +0.  Every finite or infinite score maps above 0, which is kept
+// for empty clusters.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Wave-synchronous weighted radix select over n keys (descending).
+// Precondition: the total weight exceeds `rem`.  Returns the key T of the
+// element at which the running weight (in descending key order) first
+// exceeds `rem`, and rem minus the weight of all keys above T.
+__device__ void wave_radix_select(const uint32_t* keys, const int* weights, int n, int rem,
+                                  int* hist, uint32_t* T_out, int* rem_out) {
+  const int lane = lane_id();
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = lane; b < 256; b += kWave) hist[b] = 0;
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t k = keys[i];
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], weights ? weights[i] : 1);
+    }
+    // lane l owns bins 255-4l .. 252-4l, i.e. the bins in descending order
+    const int h0 = hist[255 - 4 * lane], h1 = hist[254 - 4 * lane];
+    const int h2 = hist[253 - 4 * lane], h3 = hist[252 - 4 * lane];
+    const int tot = h0 + h1 + h2 + h3;
+    const int c0 = wave_incl_scan(tot) - tot;
+    const int c1 = c0 + h0, c2 = c1 + h1, c3 = c2 + h2, c4 = c3 + h3;
+    int bsel = -1, above = 0;
+    if (c0 <= rem && rem < c1) {
+      bsel = 255 - 4 * lane; above = c0;
+    } else if (c1 <= rem && rem < c2) {
+      bsel = 254 - 4 * lane; above = c1;
+    } else if (c2 <= rem && rem < c3) {
+      bsel = 253 - 4 * lane; above = c2;
+    } else if (c3 <= rem && rem < c4) {
+      bsel = 252 - 4 * lane; above = c3;
+    }
+    const unsigned long long bal = __ballot(bsel >= 0);
+    const int src = bal ? (int)__ffsll((long long)bal) - 1 : 0;
+    bsel = __shfl(bsel, src);
+    above = __shfl(above, src);
+    if (bsel < 0) bsel = 0;  // unreachable under the precondition; keeps the result defined
+    prefix |= (uint32_t)bsel << shift;
+    mask |= 255u << shift;
+    rem -= above;
+  }
+  *T_out = prefix;
+  *rem_out = rem;
+}
+
+__device__ __forceinline__ void qbar8(const uint16_t* q, int u, int G, int li, float* qb) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) qb[e] = 0.f;
   for (int h = 0; h < G; ++h) {
@@ -36,198 +85,174 @@ __global__ __launch_bounds__(256) void select_score_kernel(const uint16_t* __res
     qb[4] += bf16_lo(w.z); qb[5] += bf16_hi(w.z);
     qb[6] += bf16_lo(w.w); qb[7] += bf16_hi(w.w);
   }
-  for (int jj = grp; jj < kScorePerWg; jj += 16) {
-    const int j = t * kScorePerWg + jj;
-    if (j >= K) break;
-    const float* mp = cmean + ((size_t)u * K + j) * kHeadDim + li * 8;
-    const float4 m0 = *reinterpret_cast<const float4*>(mp);
-    const float4 m1 = *reinterpret_cast<const float4*>(mp + 4);
-    float d = qb[0] * m0.x;
-    d = fmaf(qb[1], m0.y, d); d = fmaf(qb[2], m0.z, d); d = fmaf(qb[3], m0.w, d);
-    d = fmaf(qb[4], m1.x, d); d = fmaf(qb[5], m1.y, d); d = fmaf(qb[6], m1.z, d);
-    d = fmaf(qb[7], m1.w, d);
-    d = xor_sum16(d);
-    if (li == 0) {
-      const int n = offsets[(size_t)u * (K + 1) + j + 1] - offsets[(size_t)u * (K + 1) + j];
-      scores[(size_t)u * K + j] = n > 0 ? d : -INFINITY;
-    }
-  }
 }
 
-// Order-preserving map of an f32 score to u32 (larger score -> larger key); -0 maps as +0.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  const uint32_t b = __float_as_uint(f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Block-wide exclusive scan over arbitrary length arrays processed in chunks
-// of blockDim.x; `running` carries the sum of earlier chunks.
-__global__ __launch_bounds__(256) void select_finish_kernel(
-    const uint16_t* __restrict__ q, int G, const float* __restrict__ scores,
-    const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ k_clu,
-    int clu_stride, int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count,
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const uint16_t* __restrict__ q, int G, const float* __restrict__ cmean,
+    const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ k_clu, int clu_stride,
+    int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count,
     uint32_t* __restrict__ cut_ws) {
-  __shared__ float sc[kMaxClusters];
+  __shared__ uint32_t key[kMaxClusters];
   __shared__ int sz[kMaxClusters];
-  __shared__ int rk[kMaxClusters];
-  __shared__ int pre[kMaxClusters];
   __shared__ int ost[kMaxClusters];
+  __shared__ int take[kMaxClusters];
   __shared__ int hist[256];
-  __shared__ int scan_scratch[8];
-  __shared__ int sh_rcut, sh_jcut, sh_need, sh_prefix, sh_rem;
+  __shared__ uint32_t tkey[kCutLds];
+  __shared__ int sh_cut, sh_need;
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int li = tid & 15;
+  const int grp = tid >> 4;
   const int32_t* off = offsets + (size_t)u * (K + 1);
   const int m = off[K];
   const int beff = budget < m ? budget : m;
 
-  for (int j = tid; j < K; j += blockDim.x) {
-    sc[j] = scores[(size_t)u * K + j];
-    sz[j] = off[j + 1] - off[j];
-  }
-  if (tid == 0) {
-    sh_rcut = K;
-    sh_jcut = -1;
-  }
-  __syncthreads();
-  // rank_j = #{i : s_i > s_j or (s_i == s_j and i < j)}
-  for (int j = tid; j < K; j += blockDim.x) {
-    const float s = sc[j];
-    int r = 0;
-    for (int i = 0; i < K; ++i) {
-      const float si = sc[i];
-      r += (si > s) || (si == s && i < j);
+  float qb[8];
+  qbar8(q, u, G, li, qb);
+
+  // ---- cluster score keys: 16 lanes per centroid row, 4 rows in flight per group
+  const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
+  for (int j0 = grp; j0 < K; j0 += kSelGroups * 4) {
+    float4 a[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = j0 + t * kSelGroups;
+      if (j < K) {
+        a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
+        a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
+      } else {
+        a[t][0] = a[t][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-    rk[j] = r;
-  }
-  __syncthreads();
-  for (int j = tid; j < K; j += blockDim.x) pre[rk[j]] = sz[j];
-  __syncthreads();
-  // inclusive prefix over ranks
-  {
-    int running = 0;
-    for (int c0 = 0; c0 < K; c0 += blockDim.x) {
-      const int r = c0 + tid;
-      const int v = r < K ? pre[r] : 0;
-      int tot;
-      const int ex = block_exclusive_scan(v, scan_scratch, &tot);
-      if (r < K) pre[r] = running + ex + v;
-      running += tot;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = j0 + t * kSelGroups;
+      float d = qb[0] * a[t][0].x;
+      d = fmaf(qb[1], a[t][0].y, d); d = fmaf(qb[2], a[t][0].z, d); d = fmaf(qb[3], a[t][0].w, d);
+      d = fmaf(qb[4], a[t][1].x, d); d = fmaf(qb[5], a[t][1].y, d); d = fmaf(qb[6], a[t][1].z, d);
+      d = fmaf(qb[7], a[t][1].w, d);
+      d = sum16(d);
+      if (li == 0 && j < K) {
+        const int n = off[j + 1] - off[j];
+        sz[j] = n;
+        key[j] = n > 0 ? score_key(d) : 0u;
+      }
     }
   }
   __syncthreads();
-  for (int r = tid; r < K; r += blockDim.x) {
-    const int below = r == 0 ? 0 : pre[r - 1];
-    if (pre[r] > beff && below <= beff) {
-      sh_rcut = r;
-      sh_need = beff - below;
+
+  // ---- wave 0: cut cluster, whole-cluster takes and output offsets (index order)
+  if (wave == 0) {
+    int cut = -1, need = 0;
+    uint32_t T = 0;
+    if (m > budget) {
+      int rem;
+      wave_radix_select(key, sz, K, beff, hist, &T, &rem);
+      // clusters with key == T are visited in index order: the cut is the first
+      // whose running size exceeds what is left
+      int run = 0;
+      for (int j0 = 0; j0 < K; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool eq = j < K && key[j] == T;
+        const int w = eq ? sz[j] : 0;
+        const int incl = run + wave_incl_scan(w);
+        const bool hit = eq && incl > rem && incl - w <= rem;
+        const unsigned long long b = __ballot(hit);
+        if (b) {
+          const int src = (int)__ffsll((long long)b) - 1;
+          cut = __shfl(j, src);
+          need = rem - __shfl(incl - w, src);
+          break;
+        }
+        run = __shfl(incl, kWave - 1);
+      }
+    }
+    int run = 0;
+    for (int j0 = 0; j0 < K; j0 += kWave) {
+      const int j = j0 + lane;
+      int t = 0;
+      if (j < K) {
+        if (cut < 0) {
+          t = sz[j];
+        } else {
+          const uint32_t k = key[j];
+          t = (k > T || (k == T && j < cut)) ? sz[j] : (j == cut ? need : 0);
+        }
+      }
+      const int incl = wave_incl_scan(t);
+      if (j < K) {
+        ost[j] = run + incl - t;
+        take[j] = t;
+      }
+      run += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) {
+      sh_cut = cut;
+      sh_need = need;
     }
   }
   __syncthreads();
-  const int rcut = sh_rcut;
-  for (int j = tid; j < K; j += blockDim.x)
-    if (rk[j] == rcut) sh_jcut = j;
-  __syncthreads();
-  const int jcut = rcut < K ? sh_jcut : -1;
-  const int need = rcut < K ? sh_need : 0;
-  // output start of every cluster in index (= position) order
-  {
-    int running = 0;
-    for (int c0 = 0; c0 < K; c0 += blockDim.x) {
-      const int j = c0 + tid;
-      int take = 0;
-      if (j < K) take = rk[j] < rcut ? sz[j] : (j == jcut ? need : 0);
-      int tot;
-      const int ex = block_exclusive_scan(take, scan_scratch, &tot);
-      if (j < K) ost[j] = running + ex;
-      running += tot;
-    }
-  }
-  __syncthreads();
+  const int cut = sh_cut;
+  const int need = sh_need;
+
+  // ---- whole clusters: positions off_j .. off_j + n_j - 1 at ost_j
   int32_t* out = sel_pos + (size_t)u * budget;
-  for (int j = wave; j < K; j += blockDim.x / kWave) {
-    if (rk[j] < rcut) {
-      const int lo = off[j], o = ost[j], n = sz[j];
-      for (int t = lane; t < n; t += kWave) out[o + t] = lo + t;
+  for (int j = tid; j < K; j += kSelThreads) {
+    const int t = take[j];
+    if (j != cut && t > 0) {
+      const int o = ost[j], lo = off[j];
+      for (int i = 0; i < t; ++i) out[o + i] = lo + i;
     }
   }
 
-  if (jcut >= 0 && need > 0) {
-    const int lo = off[jcut];
-    const int n = sz[jcut];
-    uint32_t* keys = cut_ws + (size_t)u * clu_stride;
-    // scores of the cut cluster's tokens: 16 lanes per row
-    const int li = tid & 15, grp = tid >> 4;
-    float qb[8];
+  // ---- partial fill of the cut cluster
+  if (cut >= 0 && need > 0) {
+    const int lo = off[cut];
+    const int n = sz[cut];
+    uint32_t* tk = n <= kCutLds ? tkey : cut_ws + (size_t)u * clu_stride;
+    const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo) * kHeadDim + li * 8;
+    for (int i0 = grp; i0 < n; i0 += kSelGroups * 4) {
+      uint4 w[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qb[e] = 0.f;
-    for (int h = 0; h < G; ++h) {
-      const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8);
-      qb[0] += bf16_lo(w.x); qb[1] += bf16_hi(w.x);
-      qb[2] += bf16_lo(w.y); qb[3] += bf16_hi(w.y);
-      qb[4] += bf16_lo(w.z); qb[5] += bf16_hi(w.z);
-      qb[6] += bf16_lo(w.w); qb[7] += bf16_hi(w.w);
-    }
-    for (int i = grp; i < n; i += blockDim.x / 16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(k_clu + ((size_t)u * clu_stride + lo + i) * kHeadDim + li * 8);
-      float d = qb[0] * bf16_lo(w.x);
-      d = fmaf(qb[1], bf16_hi(w.x), d); d = fmaf(qb[2], bf16_lo(w.y), d);
-      d = fmaf(qb[3], bf16_hi(w.y), d); d = fmaf(qb[4], bf16_lo(w.z), d);
-      d = fmaf(qb[5], bf16_hi(w.z), d); d = fmaf(qb[6], bf16_lo(w.w), d);
-      d = fmaf(qb[7], bf16_hi(w.w), d);
-      d = xor_sum16(d);
-      if (li == 0) keys[i] = score_key(d);
-    }
-    if (tid == 0) {
-      sh_prefix = 0;
-      sh_rem = need;
+      for (int t = 0; t < 4; ++t) {
+        const int i = i0 + t * kSelGroups;
+        w[t] = i < n ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = i0 + t * kSelGroups;
+        float d = qb[0] * bf16_lo(w[t].x);
+        d = fmaf(qb[1], bf16_hi(w[t].x), d); d = fmaf(qb[2], bf16_lo(w[t].y), d);
+        d = fmaf(qb[3], bf16_hi(w[t].y), d); d = fmaf(qb[4], bf16_lo(w[t].z), d);
+        d = fmaf(qb[5], bf16_hi(w[t].z), d); d = fmaf(qb[6], bf16_lo(w[t].w), d);
+        d = fmaf(qb[7], bf16_hi(w[t].w), d);
+        d = sum16(d);
+        if (li == 0 && i < n) tk[i] = score_key(d);
+      }
     }
     __syncthreads();
-    // radix select of the need-th largest key, 8 bits per pass from the top
-    uint32_t mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      const uint32_t prefix = (uint32_t)sh_prefix;
-      for (int i = tid; i < n; i += blockDim.x) {
-        const uint32_t k = keys[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    if (wave == 0) {
+      uint32_t T2;
+      int rem2;
+      wave_radix_select(tk, nullptr, n, need, hist, &T2, &rem2);
+      // rem2 = how many of the key == T2 tokens to take, smallest positions first
+      const int o = ost[cut];
+      int run_eq = 0, run_sel = 0;
+      const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      for (int i0 = 0; i0 < n; i0 += kWave) {
+        const int i = i0 + lane;
+        const uint32_t k = i < n ? tk[i] : 0u;
+        const int eq = (i < n && k == T2) ? 1 : 0;
+        const int eq_incl = wave_incl_scan(eq);
+        const bool sel = i < n && (k > T2 || (eq && run_eq + eq_incl - 1 < rem2));
+        const unsigned long long sb = __ballot(sel);
+        if (sel) out[o + run_sel + __popcll(sb & lt)] = lo + i;
+        run_sel += __popcll(sb);
+        run_eq += __shfl(eq_incl, kWave - 1);
       }
-      __syncthreads();
-      if (tid == 0) {
-        int rem = sh_rem, cum = 0;
-        for (int b = 255; b >= 0; --b) {
-          if (cum + hist[b] >= rem) {
-            sh_prefix = (int)(prefix | ((uint32_t)b << shift));
-            sh_rem = rem - cum;
-            break;
-          }
-          cum += hist[b];
-        }
-      }
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-    const uint32_t T = (uint32_t)sh_prefix;
-    const int rem_eq = sh_rem;  // how many of the key == T tokens to take (smallest positions)
-    int run_eq = 0, run_sel = 0;
-    const int o = ost[jcut];
-    for (int c0 = 0; c0 < n; c0 += blockDim.x) {
-      const int i = c0 + tid;
-      const uint32_t k = i < n ? keys[i] : 0u;
-      const int eq = (i < n && k == T) ? 1 : 0;
-      int tot_eq;
-      const int ex_eq = block_exclusive_scan(eq, scan_scratch, &tot_eq);
-      const int sel = (i < n) && (k > T || (eq && run_eq + ex_eq < rem_eq)) ? 1 : 0;
-      int tot_sel;
-      const int ex_sel = block_exclusive_scan(sel, scan_scratch, &tot_sel);
-      if (sel) out[o + run_sel + ex_sel] = lo + i;
-      run_eq += tot_eq;
-      run_sel += tot_sel;
     }
   }
   if (tid == 0) sel_count[u] = beff;
@@ -237,13 +262,9 @@ hipError_t launch_select(const uint16_t* q, int group, const float* cmean, const
                          int K, const uint16_t* k_clu, int clu_stride, int budget, int32_t* sel_pos,
                          int32_t* sel_count, float* scores_ws, uint32_t* cut_ws, int units,
                          hipStream_t s) {
-  const int tiles = (K + kScorePerWg - 1) / kScorePerWg;
-  hipLaunchKernelGGL(select_score_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, q, group,
-                     cmean, offsets, K, scores_ws, tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)units), dim3(256), 0, s, q, group,
-                     scores_ws, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, cut_ws);
+  (void)scores_ws;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, s, q, group, cmean,
+                     offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, cut_ws);
   return hipGetLastError();
 }
 
