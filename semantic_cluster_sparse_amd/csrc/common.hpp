@@ -71,14 +71,22 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// DPP move of an int with explicit row / bank masks; lanes whose source is
+// outside the row (or rows not in row_mask) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave (DPP row shifts, then
+// row broadcasts of lanes 15 and 31).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = (int)__lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  v += dpp_i32<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_i32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_i32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_i32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_i32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

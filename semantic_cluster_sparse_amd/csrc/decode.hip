@@ -218,39 +218,46 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       L += red[w][h][kHeadDim + 1] * a;
       O += red[w][h][d] * a;
     }
-    outp[h * kPartialStride + d] = O;
+    // device-scope stores: written through to the coherence point shared by all
+    // XCDs, so the merging workgroup sees them without a cache-wide flush
+    __hip_atomic_store(&outp[h * kPartialStride + d], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      outp[h * kPartialStride + kHeadDim] = M;
-      outp[h * kPartialStride + kHeadDim + 1] = L;
+      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim + 1], L, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // arrival: the last chunk of this unit merges every chunk's partial
+  // Arrival: every thread waits until its device-scope partial stores are
+  // acknowledged (vmcnt covers stores on gfx9), then the barrier, then one
+  // relaxed device-scope increment; the last chunk of the unit merges.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(&counters[u], 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = (prev == (uint32_t)(n_chunks - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
-  __threadfence();
   const size_t cs = (size_t)GT * kPartialStride;
   for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
     const int h = t / kHeadDim, d = t % kHeadDim;
     const float* p = pu + h * kPartialStride;
-    float M = -INFINITY;
-    for (int cc = 0; cc < n_chunks; ++cc) M = fmaxf(M, __builtin_nontemporal_load(p + cc * cs + kHeadDim));
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int cc = 0; cc < n_chunks; ++cc) {
-      const float a = exp2f(__builtin_nontemporal_load(p + cc * cs + kHeadDim) - Ms);
-      L += __builtin_nontemporal_load(p + cc * cs + kHeadDim + 1) * a;
-      O += __builtin_nontemporal_load(p + cc * cs + d) * a;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int cc = 0; cc < n_chunks; ++cc) {  // online merge: one pass over the chunks
+      const float mc = __hip_atomic_load(p + cc * cs + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float lc = __hip_atomic_load(p + cc * cs + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float oc = __hip_atomic_load(p + cc * cs + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float Mn = fmaxf(M, mc);
+      const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+      const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
+      L = L * a0 + lc * a1;
+      O = O * a0 + oc * a1;
+      M = Mn;
     }
     out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
   }
-  if (tid == 0) counters[u] = 0u;
+  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static int group_tier(int G) {

@@ -113,12 +113,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   float qb[8];
   qbar8(q, u, G, li, qb);
 
-  // ---- cluster score keys: 16 lanes per centroid row, 4 rows in flight per group
+  // ---- cluster score keys: 16 lanes per centroid row, 8 rows in flight per group
+  constexpr int kRowsInFlight = 8;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
-  for (int j0 = grp; j0 < K; j0 += kSelGroups * 4) {
-    float4 a[4][2];
+  for (int j0 = grp; j0 < K; j0 += kSelGroups * kRowsInFlight) {
+    float4 a[kRowsInFlight][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j0 + t * kSelGroups;
       if (j < K) {
         a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j0 + t * kSelGroups;
       float d = qb[0] * a[t][0].x;
       d = fmaf(qb[1], a[t][0].y, d); d = fmaf(qb[2], a[t][0].z, d); d = fmaf(qb[3], a[t][0].w, d);
