@@ -288,19 +288,24 @@ int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_
   if (rc) return rc;
   const int units = L->batch * L->n_kv_heads;
   const long long rmax = (long long)L->n_sink + cmax + (L->n_total - L->n_clustered);
-  // Split-K: chunks of whole row-group batches (every row group loads all of
-  // its rows of a batch at once), at most kMaxChunks chunks per unit.
-  const long long batch = ckv::decode_rows_per_batch(L->group);
-  long long chunk = batch;
+  // Split-K: about kDecodeTargetWgs workgroups per launch (all resident at once
+  // on 256 CUs), chunks of whole 16-row steps, at most kMaxChunks per unit.
+#ifndef CKV_DEC_TARGET_WGS
+#define CKV_DEC_TARGET_WGS 256
+#endif
+  const long long target = CKV_DEC_TARGET_WGS;
+  long long chunk = (rmax * units + target - 1) / target;
   const long long min_chunk = (rmax + ckv::kMaxChunks - 1) / ckv::kMaxChunks;
-  if (chunk < min_chunk) chunk = (min_chunk + batch - 1) / batch * batch;
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (chunk < 64) chunk = 64;
+  chunk = (chunk + 15) / 16 * 16;
   long long n_chunks = (rmax + chunk - 1) / chunk;
   if (n_chunks < 1) n_chunks = 1;
   const Layout w = layout_of(L);
   hipError_t e = ckv::launch_sparse_decode(
       q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
       sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
-      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, out, units, (hipStream_t)stream);
+      (float*)((char*)ws + w.off_partials), out, units, (hipStream_t)stream);
   return hip_status(e, "sparse_decode");
 }
 

@@ -5,11 +5,15 @@
 // §3.1 attention formula; §4.1 cluster-contiguous storage; ClusterKV
 // abstract, arXiv 2412.03213: recall at semantic-cluster granularity).
 //
-// Split-K flash decode: a workgroup takes one chunk of the attended rows of
-// one unit; LPR lanes share a row (DPL = 128/LPR dims each), every row is
-// read once for all G heads; scores live in the log2 domain (q pre-scaled by
-// log2(e)/sqrt(128)); each workgroup leaves (max, sum, unnormalised output)
-// per head, merged by a small log-sum-exp kernel.
+// Split-K flash decode built as an HBM stream.  A workgroup (4 waves) takes
+// one chunk of one unit's attended rows.  Each wave streams "stages" of 4
+// rows (K and V, 2 KB) straight from HBM into its own LDS ring with
+// global_load_lds_dwordx4, kStages stages ahead of the math, so every CU keeps
+// ~100 KB of row data in flight without spending VGPRs on it.  A 16-lane group
+// owns one row of a stage (8 dims per lane) and reads back exactly the bytes
+// its lanes DMA'd.  Scores: bf16 dot2 + DPP row sums, log2 domain (q scaled
+// by log2(e)/sqrt(128)); softmax updated once per two stages.  Each chunk
+// leaves (max, sum, unnormalised output) per head; a small kernel merges them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,59 +26,83 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+#ifndef CKV_DEC_STAGES
+#define CKV_DEC_STAGES 8
+#endif
 constexpr int kDecThreads = 256;
-constexpr int kDecGroups = kDecThreads / 16;  // row groups of 16 lanes (8 dims per lane)
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kStages = CKV_DEC_STAGES;     // ring depth per wave (even)
+constexpr int kStageBytes = 2048;           // 4 rows x 256 B of K, then of V
+constexpr int kRingBytes = kDecWaves * kStages * kStageBytes;
+constexpr int kRowSegment = 1024;           // row sources staged in LDS per segment
+constexpr int kCluFlag = 0x40000000;        // row source is the cluster-ordered copy
+static_assert(kStages % 2 == 0 && kStages >= 4, "stages are consumed two at a time");
+constexpr float kLazy = 8.0f;              // log2-domain slack before the reference max moves
 
-// Rows per row group per batch: all are loaded before any arithmetic.
-template <int GT>
-struct DecRows {
-  static constexpr int U = GT <= 4 ? 8 : (GT == 8 ? 4 : 2);
-};
+// gfx9 s_waitcnt immediate with only vmcnt constrained.
+#define CKV_VMCNT(N) ((((N) & 15) | (((N) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-__device__ __forceinline__ void merge_state(float& m, float& l, float mo, float lo, float& a_self,
-                                            float& a_other) {
-  const float M = fmaxf(m, mo);
-  const float Ms = (M == -INFINITY) ? 0.f : M;
-  a_self = exp2f(m - Ms);
-  a_other = exp2f(mo - Ms);
-  l = l * a_self + lo * a_other;
-  m = M;
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// LDS reads the compiler does not see (so it does not wait for the in-flight
+// LDS DMA of other ring stages); each waits for its own result.
+__device__ __forceinline__ uint4 lds_read_b128(uint32_t addr) {
+  uint4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ int lds_read_b32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// The two stages consumed by one step (K and V of each) plus the row sources
+// of the two stages issued next, with a single wait.
+__device__ __forceinline__ void lds_read_step(uint32_t a0, uint32_t a1, uint32_t r0, uint32_t r1, uint4& k0,
+                                              uint4& v0, uint4& k1, uint4& v1, int& s0, int& s1) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %7 offset:1024\n\t"
+      "ds_read_b32 %4, %8\n\t"
+      "ds_read_b32 %5, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k0), "=&v"(v0), "=&v"(k1), "=&v"(v1), "=&v"(s0), "=&v"(s1)
+      : "v"(a0), "v"(a1), "v"(r0), "v"(r1)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// One workgroup per (unit, chunk of attended rows).  Row r of the attended
-// sequence is a sink (r < n_sink), a recalled row of the cluster-ordered copy
-// (r < n_sink + cnt, position sel_pos[r - n_sink]) or a recent row.  Each
-// workgroup leaves per head (max, sum, unnormalised output) in `partials`;
-// the last workgroup of the unit to finish (arrival counter in `counters`,
-// reset to 0 by that workgroup) merges them into `out`.
 template <int GT>
 __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ q, int G, const uint16_t* __restrict__ k_tok,
     const uint16_t* __restrict__ v_tok, int capacity, const uint16_t* __restrict__ k_clu,
     const uint16_t* __restrict__ v_clu, int clu_stride, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_count, int budget, int m, int n_sink, int n_clustered,
-    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials,
-    uint32_t* __restrict__ counters, float* __restrict__ out) {
-  constexpr int U = DecRows<GT>::U;
-  constexpr int NW = kDecThreads / kWave;
-  __shared__ float red[NW][GT][kPartialStride];
-  __shared__ int sh_last;
-  __shared__ int rowsrc[kDecGroups * DecRows<GT>::U];
+    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials) {
+  // ring | row sources; the per-wave merge area reuses the ring afterwards
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kRingBytes + kRowSegment * 4];
+  static_assert(kDecWaves * GT * kPartialStride * 4 <= kRingBytes, "merge area must fit in the ring");
+  int* rowsrc = reinterpret_cast<int*>(smem + kRingBytes);
+  float* red = reinterpret_cast<float*>(smem);
 
   const int u = blockIdx.x / n_chunks;
   const int c = blockIdx.x % n_chunks;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int li = tid & 15;
-  const int gi = tid >> 4;
+  const int li = lane & 15;
+  const int grp = lane >> 4;  // row of the stage this lane's group owns
 
   uint4 qw[GT];
 #pragma unroll
   for (int h = 0; h < GT; ++h)
     qw[h] = h < G ? *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8)
                   : make_uint4(0, 0, 0, 0);
-
   int cnt = sel_count[u];
   const int cmax = budget < m ? budget : m;
   cnt = cnt < 0 ? 0 : (cnt > cmax ? cmax : cnt);
@@ -98,81 +126,105 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   const uint16_t* kcu = k_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
   const uint16_t* vcu = v_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
   const int32_t* sp = sel_pos + (size_t)u * budget - n_sink;
+  unsigned char* ring = smem + wave * kStages * kStageBytes;
+  const uint32_t ring_lane = lds_addr(ring) + lane * 16;
+  const uint32_t rows_lds = lds_addr(rowsrc);
 
-  // Rows of a batch are staged as source indices in LDS (one coalesced load of
-  // sel_pos per batch), so every row load of the batch issues back to back.
-  constexpr int kBatch = kDecGroups * U;
-  constexpr int kCluFlag = 0x40000000;
-  for (int bs = r0; bs < r1; bs += kBatch) {
-    if (tid < kBatch) {
-      const int r = bs + tid;
-      int v = 0;
-      if (r < r1) {
-        if (r < n_sink) {
-          v = r;
-        } else if (r < sel_end) {
-          int p = sp[r];
-          p = p < 0 ? 0 : (p >= m ? m - 1 : p);
-          v = p | kCluFlag;
-        } else {
-          v = n_clustered + (r - sel_end);
-        }
+  for (int seg = r0; seg < r1; seg += kRowSegment) {
+    const int seg_end = min(r1, seg + kRowSegment);
+    // row sources of this segment: row index, flagged when it lives in the cluster copy
+    __syncthreads();
+    for (int i = tid; i < seg_end - seg; i += kDecThreads) {
+      const int r = seg + i;
+      int v;
+      if (r < n_sink) {
+        v = r;
+      } else if (r < sel_end) {
+        int p = sp[r];
+        p = p < 0 ? 0 : (p >= m ? m - 1 : p);
+        v = p | kCluFlag;
+      } else {
+        v = n_clustered + (r - sel_end);
       }
-      rowsrc[tid] = v;
+      rowsrc[i] = v;
     }
     __syncthreads();
-    uint4 kr[U], vr[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int v = rowsrc[gi + k * kDecGroups];
+
+    // this wave's stages: 4 consecutive rows each, waves interleaved
+    const int nrows = seg_end - seg;
+    const int n_st = (nrows + 4 * kDecWaves - 1) / (4 * kDecWaves);  // stages per wave (upper bound)
+    // stage st of this wave covers rows 4 * (st * kDecWaves + wave) .. +3 of the segment;
+    // a row index past the segment reads entry 0 (its stage is masked out)
+    auto src_slot = [&](int st) -> uint32_t {
+      const int ri = 4 * (st * kDecWaves + wave) + grp;
+      return rows_lds + (ri < nrows ? ri : 0) * 4;
+    };
+    auto issue = [&](int v, int slot) {
       const bool clu = (v & kCluFlag) != 0;
       const size_t row = (size_t)(v & (kCluFlag - 1)) * kHeadDim;
-      kr[k] = *reinterpret_cast<const uint4*>((clu ? kcu : ktu) + row);
-      vr[k] = *reinterpret_cast<const uint4*>((clu ? vcu : vtu) + row);
-    }
-    __syncthreads();
-    // keep the scheduler from interleaving math between the row loads
-    __builtin_amdgcn_sched_barrier(0);
-    const int b0 = bs + gi;
-    float s[U][GT];
+      unsigned char* dst = ring + slot * kStageBytes;
+      __builtin_amdgcn_global_load_lds((gptr_t)((clu ? kcu : ktu) + row), (lptr_t)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)((clu ? vcu : vtu) + row), (lptr_t)(dst + 1024), 16, 0, 0);
+    };
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const bool ok = b0 + k * kDecGroups < r1;
+    for (int st = 0; st < kStages; ++st) issue(lds_read_b32(src_slot(st)), st);
+
+    for (int st = 0; st < n_st; st += 2) {
+      const int slot = st % kStages;
+      // the two oldest stages (4 DMA ops) must have landed; 2 * (kStages - 2) may stay in flight
+      __builtin_amdgcn_s_waitcnt(CKV_VMCNT(2 * (kStages - 2)));
+      uint4 kr[2], vr[2];
+      int nx0, nx1;
+      lds_read_step(ring_lane + slot * kStageBytes, ring_lane + (slot + 1) * kStageBytes,
+                    src_slot(st + kStages), src_slot(st + kStages + 1), kr[0], vr[0], kr[1], vr[1], nx0,
+                    nx1);
+      issue(nx0, slot);
+      issue(nx1, slot + 1);
+
+      float s[2][GT];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bool ok = 4 * ((st + k) * kDecWaves + wave) + grp < nrows;
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float d = dot2(kr[k].x, qw[h].x, 0.f);
+          d = dot2(kr[k].y, qw[h].y, d);
+          d = dot2(kr[k].z, qw[h].z, d);
+          d = dot2(kr[k].w, qw[h].w, d);
+          d = sum16(d);
+          s[k][h] = ok ? d * qscale : -INFINITY;
+        }
+      }
+      // Lazy rescaling: the reference max only moves (and the accumulators
+      // are rescaled) when a score exceeds it by more than kLazy in log2
+      // units, so p = 2^(s - ref) stays <= 2^kLazy; the merge divides it out.
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float d = dot2(kr[k].x, qw[h].x, 0.f);
-        d = dot2(kr[k].y, qw[h].y, d);
-        d = dot2(kr[k].z, qw[h].z, d);
-        d = dot2(kr[k].w, qw[h].w, d);
-        d = sum16(d);
-        s[k][h] = ok ? d * qscale : -INFINITY;
+        const float mn = fmaxf(s[0][h], s[1][h]);
+        if (mn > mx[h] + kLazy) {
+          const float alpha = mx[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx[h] - mn);
+          ls[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+          mx[h] = mn;
+        }
+        // mx is -inf only while every score seen is -inf (masked rows): p = 0 then
+        const float ms = mx[h] == -INFINITY ? 0.f : mx[h];
+        const float p0 = __builtin_amdgcn_exp2f(s[0][h] - ms);
+        const float p1 = __builtin_amdgcn_exp2f(s[1][h] - ms);
+        ls[h] += p0 + p1;
+        acc[h][0] = fmaf(p1, bf16_lo(vr[1].x), fmaf(p0, bf16_lo(vr[0].x), acc[h][0]));
+        acc[h][1] = fmaf(p1, bf16_hi(vr[1].x), fmaf(p0, bf16_hi(vr[0].x), acc[h][1]));
+        acc[h][2] = fmaf(p1, bf16_lo(vr[1].y), fmaf(p0, bf16_lo(vr[0].y), acc[h][2]));
+        acc[h][3] = fmaf(p1, bf16_hi(vr[1].y), fmaf(p0, bf16_hi(vr[0].y), acc[h][3]));
+        acc[h][4] = fmaf(p1, bf16_lo(vr[1].z), fmaf(p0, bf16_lo(vr[0].z), acc[h][4]));
+        acc[h][5] = fmaf(p1, bf16_hi(vr[1].z), fmaf(p0, bf16_hi(vr[0].z), acc[h][5]));
+        acc[h][6] = fmaf(p1, bf16_lo(vr[1].w), fmaf(p0, bf16_lo(vr[0].w), acc[h][6]));
+        acc[h][7] = fmaf(p1, bf16_hi(vr[1].w), fmaf(p0, bf16_hi(vr[0].w), acc[h][7]));
       }
     }
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float mn = mx[h];
-#pragma unroll
-      for (int k = 0; k < U; ++k) mn = fmaxf(mn, s[k][h]);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = exp2f(mx[h] - ms);
-      ls[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-      mx[h] = mn;
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const float p = exp2f(s[k][h] - ms);
-        ls[h] += p;
-        acc[h][0] = fmaf(p, bf16_lo(vr[k].x), acc[h][0]);
-        acc[h][1] = fmaf(p, bf16_hi(vr[k].x), acc[h][1]);
-        acc[h][2] = fmaf(p, bf16_lo(vr[k].y), acc[h][2]);
-        acc[h][3] = fmaf(p, bf16_hi(vr[k].y), acc[h][3]);
-        acc[h][4] = fmaf(p, bf16_lo(vr[k].z), acc[h][4]);
-        acc[h][5] = fmaf(p, bf16_hi(vr[k].z), acc[h][5]);
-        acc[h][6] = fmaf(p, bf16_lo(vr[k].w), acc[h][6]);
-        acc[h][7] = fmaf(p, bf16_hi(vr[k].w), acc[h][7]);
-      }
-    }
+    // drain the DMA issued past the end of this wave's stages before the ring is reused
+    __builtin_amdgcn_s_waitcnt(CKV_VMCNT(0));
   }
 
   // merge the 4 row groups of this wave (lane bits 4 and 5)
@@ -182,8 +234,11 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     for (int h = 0; h < GT; ++h) {
       const float mo = __shfl_xor(mx[h], o);
       const float lo = __shfl_xor(ls[h], o);
-      float as, ao;
-      merge_state(mx[h], ls[h], mo, lo, as, ao);
+      const float M = fmaxf(mx[h], mo);
+      const float Ms = (M == -INFINITY) ? 0.f : M;
+      const float as = exp2f(mx[h] - Ms), ao = exp2f(mo - Ms);
+      ls[h] = ls[h] * as + lo * ao;
+      mx[h] = M;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float other = __shfl_xor(acc[h][e], o);
@@ -191,73 +246,66 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       }
     }
   }
+  __syncthreads();  // every wave is done with the ring before it becomes the merge area
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
+      float* rw = red + (wave * GT + h) * kPartialStride;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][h][li * 8 + e] = acc[h][e];
+      for (int e = 0; e < 8; ++e) rw[li * 8 + e] = acc[h][e];
       if (lane == 0) {
-        red[wave][h][kHeadDim] = mx[h];
-        red[wave][h][kHeadDim + 1] = ls[h];
+        rw[kHeadDim] = mx[h];
+        rw[kHeadDim + 1] = ls[h];
       }
     }
   }
   __syncthreads();
-  float* pu = partials + (size_t)u * n_chunks * GT * kPartialStride;
-  float* outp = pu + (size_t)c * GT * kPartialStride;
+  float* outp = partials + ((size_t)u * n_chunks + c) * GT * kPartialStride;
   for (int t = tid; t < GT * kHeadDim; t += kDecThreads) {
     const int h = t / kHeadDim, d = t % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w][h][kHeadDim]);
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GT + h) * kPartialStride + kHeadDim]);
     const float Ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float a = exp2f(red[w][h][kHeadDim] - Ms);
-      L += red[w][h][kHeadDim + 1] * a;
-      O += red[w][h][d] * a;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* rw = red + (w * GT + h) * kPartialStride;
+      const float a = exp2f(rw[kHeadDim] - Ms);
+      L += rw[kHeadDim + 1] * a;
+      O += rw[d] * a;
     }
-    // device-scope stores: written through to the coherence point shared by all
-    // XCDs, so the merging workgroup sees them without a cache-wide flush
-    __hip_atomic_store(&outp[h * kPartialStride + d], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    outp[h * kPartialStride + d] = O;
     if (d == 0) {
-      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim + 1], L, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      outp[h * kPartialStride + kHeadDim] = M;
+      outp[h * kPartialStride + kHeadDim + 1] = L;
     }
   }
+}
 
-  // Arrival: every thread waits until its device-scope partial stores are
-  // acknowledged (vmcnt covers stores on gfx9), then the barrier, then one
-  // relaxed device-scope increment; the last chunk of the unit merges.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (prev == (uint32_t)(n_chunks - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!sh_last) return;
+// Log-sum-exp merge of the chunk partials: one workgroup of 128 threads per
+// (unit, head), one pass over the chunks with every load independent.
+__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ partials, int GT,
+                                                           int G, int n_chunks, float* __restrict__ out) {
+  const int u = blockIdx.x / G;
+  const int h = blockIdx.x % G;
+  const int d = threadIdx.x;
   const size_t cs = (size_t)GT * kPartialStride;
-  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
-    const int h = t / kHeadDim, d = t % kHeadDim;
-    const float* p = pu + h * kPartialStride;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int cc = 0; cc < n_chunks; ++cc) {  // online merge: one pass over the chunks
-      const float mc = __hip_atomic_load(p + cc * cs + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float lc = __hip_atomic_load(p + cc * cs + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float oc = __hip_atomic_load(p + cc * cs + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float Mn = fmaxf(M, mc);
-      const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
-      const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
-      L = L * a0 + lc * a1;
-      O = O * a0 + oc * a1;
-      M = Mn;
-    }
-    out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  const float* p = partials + (size_t)u * n_chunks * cs + h * kPartialStride;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int cc = 0; cc < n_chunks; ++cc) {
+    const float mc = p[cc * cs + kHeadDim];
+    const float lc = p[cc * cs + kHeadDim + 1];
+    const float oc = p[cc * cs + d];
+    const float Mn = fmaxf(M, mc);
+    const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+    const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
+    L = L * a0 + lc * a1;
+    O = O * a0 + oc * a1;
+    M = Mn;
   }
-  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
 }
 
 static int group_tier(int G) {
@@ -266,28 +314,17 @@ static int group_tier(int G) {
   return gt;
 }
 
-int decode_rows_per_batch(int G) {
-  switch (group_tier(G)) {
-    case 1: return kDecGroups * DecRows<1>::U;
-    case 2: return kDecGroups * DecRows<2>::U;
-    case 4: return kDecGroups * DecRows<4>::U;
-    case 8: return kDecGroups * DecRows<8>::U;
-    default: return kDecGroups * DecRows<16>::U;
-  }
-}
-
 hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
                                 const uint16_t* v_tok, int capacity, const uint16_t* k_clu,
                                 const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
-                                float* partials, uint32_t* counters, float* out, int units,
-                                hipStream_t s) {
+                                float* partials, float* out, int units, hipStream_t s) {
   const dim3 grid((unsigned)(units * n_chunks));
 #define CKV_DEC(GTV)                                                                                \
   hipLaunchKernelGGL(sparse_decode_kernel<GTV>, grid, dim3(kDecThreads), 0, s, q, G, k_tok, v_tok, \
                      capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m, n_sink,     \
-                     n_clustered, n_total, chunk_rows, n_chunks, partials, counters, out)
+                     n_clustered, n_total, chunk_rows, n_chunks, partials)
   switch (group_tier(G)) {
     case 1: CKV_DEC(1); break;
     case 2: CKV_DEC(2); break;
@@ -296,6 +333,10 @@ hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
     default: CKV_DEC(16); break;
   }
 #undef CKV_DEC
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(units * G)), dim3(128), 0, s, partials,
+                     group_tier(G), G, n_chunks, out);
   return hipGetLastError();
 }
 

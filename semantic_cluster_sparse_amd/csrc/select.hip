@@ -12,14 +12,15 @@
 // total size <= budget) and the rest.  It is found without sorting by a
 // wave-synchronous radix select on order-preserving 32-bit score keys with
 // cluster sizes as weights (4 passes of 8 bits); the partial fill inside the
-// cut cluster is the same select with unit weights.  One workgroup of 512
-// threads per unit, three block barriers.
+// cut cluster is the same select with unit weights.  One workgroup of 1024
+// threads per unit, three block barriers; recalled positions are written by
+// whole waves so every store instruction covers 64 consecutive slots.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ckv {
 
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSelGroups = kSelThreads / 16;  // 16-lane row groups
 constexpr int kCutLds = 4096;                 // cut-cluster keys kept in LDS up to this size
 
@@ -199,13 +200,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int cut = sh_cut;
   const int need = sh_need;
 
-  // ---- whole clusters: positions off_j .. off_j + n_j - 1 at ost_j
+  // ---- whole clusters: positions off_j .. off_j + n_j - 1 at ost_j.  Each wave
+  // takes 64 clusters at a time into registers and walks them with readlane,
+  // writing one cluster's run with coalesced stores.
   int32_t* out = sel_pos + (size_t)u * budget;
-  for (int j = tid; j < K; j += kSelThreads) {
-    const int t = take[j];
-    if (j != cut && t > 0) {
-      const int o = ost[j], lo = off[j];
-      for (int i = 0; i < t; ++i) out[o + i] = lo + i;
+  constexpr int kSelWaves = kSelThreads / kWave;
+  for (int jb = wave * kWave; jb < K; jb += kSelWaves * kWave) {
+    const int j = jb + lane;
+    const int t = (j < K && j != cut) ? take[j] : 0;
+    const int o = j < K ? ost[j] : 0;
+    const int lo = j < K ? off[j] : 0;
+    unsigned long long live = __ballot(t > 0);
+    while (live) {
+      const int l = (int)__ffsll((long long)live) - 1;
+      live &= live - 1;
+      const int tl = __shfl(t, l), ol = __shfl(o, l), ll = __shfl(lo, l);
+      for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
     }
   }
 
