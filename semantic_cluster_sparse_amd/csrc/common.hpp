@@ -90,6 +90,32 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Bitwise AND / OR over the 64 lanes of a wave (DPP within rows of 16, then
+// the four row results through readlane); the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  int x = (int)v;
+  x &= __builtin_amdgcn_mov_dpp(x, kDppXor1, 0xF, 0xF, true);
+  x &= __builtin_amdgcn_mov_dpp(x, kDppXor2, 0xF, 0xF, true);
+  x &= __builtin_amdgcn_mov_dpp(x, kDppHalfMirror, 0xF, 0xF, true);
+  x &= __builtin_amdgcn_mov_dpp(x, kDppMirror, 0xF, 0xF, true);
+  return (uint32_t)(__builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
+                    __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48));
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  int x = (int)v;
+  x |= __builtin_amdgcn_mov_dpp(x, kDppXor1, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_mov_dpp(x, kDppXor2, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_mov_dpp(x, kDppHalfMirror, 0xF, 0xF, true);
+  x |= __builtin_amdgcn_mov_dpp(x, kDppMirror, 0xF, 0xF, true);
+  return (uint32_t)(__builtin_amdgcn_readlane(x, 0) | __builtin_amdgcn_readlane(x, 16) |
+                    __builtin_amdgcn_readlane(x, 32) | __builtin_amdgcn_readlane(x, 48));
+}
+
 // Exclusive prefix sum over a block of `nthreads` threads (nthreads <= 1024,
 // multiple of 64).  `scratch` needs nthreads/64 + 1 ints of LDS.  Returns the
 // exclusive prefix of `v` and writes the block total to *total.

@@ -180,6 +180,143 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Assignment with every direction resident in LDS (K <= 512): one workgroup of
+// 8 waves per CU walks a range of 64-key tiles of one unit; each wave keeps
+// the MFMA A-operands of its current tile in registers and loads the next
+// tile's while the MFMAs of the current one run.  The directions are loaded
+// into LDS once per workgroup instead of once per 256 keys.
+// ---------------------------------------------------------------------------
+constexpr int kAsResWaves = 8;
+constexpr int kAsResMaxK = 512;
+
+__global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
+    const uint16_t* __restrict__ k_tok, int capacity, int row0, int count,
+    const uint16_t* __restrict__ cdir, int K, int32_t* __restrict__ assign, int clu_stride, int first,
+    int wg_per_unit, int tiles_per_wg) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t csr[];
+  const int u = blockIdx.x / wg_per_unit;
+  const int part = blockIdx.x % wg_per_unit;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int kg = lane >> 4;
+  const int ntiles = (count + 63) >> 6;
+  const int t0 = part * tiles_per_wg;
+  const int t1 = min(ntiles, t0 + tiles_per_wg);
+  if (t0 >= t1) return;  // uniform over the workgroup
+
+  // all K directions (rows padded to a multiple of 16 with zeros)
+  const int kpad = (K + 15) & ~15;
+  const uint16_t* cbase = cdir + (size_t)u * K * kHeadDim;
+  for (int e = threadIdx.x; e < kpad * 16; e += blockDim.x) {
+    const int row = e >> 4, ch = e & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < K) v = *reinterpret_cast<const uint4*>(cbase + (size_t)row * kHeadDim + ch * 8);
+    *reinterpret_cast<uint4*>(csr + row * kAsLds + ch * 8) = v;
+  }
+  __syncthreads();
+
+  const uint16_t* kbase = k_tok + ((size_t)u * capacity + row0) * kHeadDim;
+  int32_t* out = assign + (size_t)u * clu_stride + first;
+  auto load_tile = [&](bf16x8 (&a)[kAsMt][4], int t) {
+#pragma unroll
+    for (int mt = 0; mt < kAsMt; ++mt) {
+      int r = t * 64 + mt * 16 + r16;
+      r = r < count ? r : count - 1;
+      const uint16_t* src = kbase + (size_t)r * kHeadDim + kg * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[mt][s] = *reinterpret_cast<const bf16x8*>(src + s * 32);
+    }
+  };
+  auto compute_tile = [&](const bf16x8 (&a)[kAsMt][4], int t) {
+    float best[kAsMt][4];
+    int bidx[kAsMt][4];
+#pragma unroll
+    for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        best[mt][i] = -INFINITY;
+        bidx[mt][i] = 0;
+      }
+    auto mfma_tile = [&](int ct, f32x4* o) {
+      bf16x8 b[4];
+      const uint16_t* bp = csr + (ct * 16 + r16) * kAsLds + kg * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(bp + s * 32);
+#pragma unroll
+      for (int mt = 0; mt < kAsMt; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt)
+          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], o[mt], 0, 0, 0);
+    };
+    auto argmax_tile = [&](const f32x4* in, int j) {
+#pragma unroll
+      for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = in[mt][i];
+          const bool gt = v > best[mt][i];
+          best[mt][i] = gt ? v : best[mt][i];
+          bidx[mt][i] = gt ? j : bidx[mt][i];
+        }
+    };
+    const int nfull = K >> 4;
+    f32x4 acc[kAsMt], nxt[kAsMt];
+    if (nfull > 0) {
+      mfma_tile(0, acc);
+      for (int ct = 1; ct < nfull; ++ct) {
+        mfma_tile(ct, nxt);
+        argmax_tile(acc, (ct - 1) * 16 + r16);
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = nxt[mt];
+      }
+      argmax_tile(acc, (nfull - 1) * 16 + r16);
+    }
+    if (K & 15) {
+      mfma_tile(nfull, acc);
+      if (nfull * 16 + r16 >= K) {
+#pragma unroll
+        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      argmax_tile(acc, nfull * 16 + r16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < kAsMt; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float bv = best[mt][i];
+        int bi = bidx[mt][i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        const int r = t * 64 + mt * 16 + kg * 4 + i;
+        if (r16 == i && r < count) out[r] = bi;
+      }
+  };
+
+  // tiles of this wave: t0 + wave, t0 + wave + 8, ...; two register sets alternate
+  bf16x8 a0[kAsMt][4], a1[kAsMt][4];
+  int t = t0 + wave;
+  if (t < t1) load_tile(a0, t);
+  for (; t < t1; t += 2 * kAsResWaves) {
+    const int tn = t + kAsResWaves;
+    if (tn < t1) load_tile(a1, tn);
+    compute_tile(a0, t);
+    if (tn >= t1) break;
+    if (tn + kAsResWaves < t1) load_tile(a0, tn + kAsResWaves);
+    compute_tile(a1, tn);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Counting sort by cluster label, stable in token order.
 // hist: per (unit, tile of kSortTile tokens) label counts.
 // ---------------------------------------------------------------------------
@@ -470,6 +607,27 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
                          int first, int units, hipStream_t s) {
   if (count <= 0) return hipSuccess;
+  if (K <= kAsResMaxK) {
+    // about one 8-wave workgroup per CU, each on one unit's range of 64-key tiles
+    const int ntiles = (count + 63) / 64;
+    int wpu = (256 + units - 1) / units;
+    const int max_wpu = (ntiles + kAsResWaves - 1) / kAsResWaves;
+    if (wpu > max_wpu) wpu = max_wpu;
+    if (wpu < 1) wpu = 1;
+    const int tpw = (ntiles + wpu - 1) / wpu;
+    const size_t lds = (size_t)((K + 15) & ~15) * kAsLds * sizeof(uint16_t);
+    static bool lds_attr = false;  // dynamic LDS above 64 KiB must be allowed explicitly
+    if (!lds_attr) {
+      const hipError_t e = hipFuncSetAttribute((const void*)assign_resident_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(kAsResMaxK * kAsLds * sizeof(uint16_t)));
+      if (e != hipSuccess) return e;
+      lds_attr = true;
+    }
+    hipLaunchKernelGGL(assign_resident_kernel, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds, s,
+                       k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw);
+    return hipGetLastError();
+  }
   const int tiles = (count + kAsRows - 1) / kAsRows;
   hipLaunchKernelGGL(assign_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, k_tok,
                      capacity, row0, count, cdir, K, assign, clu_stride, first, tiles);

@@ -33,41 +33,103 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+constexpr int kRegKeys = 16;
+constexpr int kHistBins = 256 + 4;  // one dummy bin (index 256) takes keys outside the prefix
+constexpr int kHistCopies = 8;      // lane % 8 picks a copy: same-bin LDS atomics conflict 8x less
+
+// Pick the digit bin where the descending running weight crosses `rem`.
+// Lane l owns bins 255-4l .. 252-4l (one 16-byte LDS load per histogram copy).
+__device__ __forceinline__ int radix_pick_bin(const int* hist, int rem, int* above_out) {
+  const int lane = lane_id();
+  int4 hb = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c) {
+    const int4 v = *reinterpret_cast<const int4*>(hist + c * kHistBins + 252 - 4 * lane);
+    hb.x += v.x; hb.y += v.y; hb.z += v.z; hb.w += v.w;
+  }
+  const int h0 = hb.w, h1 = hb.z, h2 = hb.y, h3 = hb.x;
+  const int tot = h0 + h1 + h2 + h3;
+  const int c0 = wave_incl_scan(tot) - tot;
+  const int c1 = c0 + h0, c2 = c1 + h1, c3 = c2 + h2, c4 = c3 + h3;
+  const bool in = c0 <= rem && rem < c4;
+  const int sub = rem < c1 ? 0 : (rem < c2 ? 1 : (rem < c3 ? 2 : 3));
+  const int above = sub == 0 ? c0 : (sub == 1 ? c1 : (sub == 2 ? c2 : c3));
+  const unsigned long long bal = __ballot(in);
+  const int src = bal ? (int)__ffsll((long long)bal) - 1 : 0;
+  *above_out = __builtin_amdgcn_readlane(above, src);
+  const int bsel = 255 - 4 * src - __builtin_amdgcn_readlane(sub, src);
+  return bal ? bsel : 0;  // no bin only if the precondition fails; keeps the result defined
+}
+
 // Wave-synchronous weighted radix select over n keys (descending).
 // Precondition: the total weight exceeds `rem`.  Returns the key T of the
 // element at which the running weight (in descending key order) first
-// exceeds `rem`, and rem minus the weight of all keys above T.
-__device__ void wave_radix_select(const uint32_t* keys, const int* weights, int n, int rem,
-                                  int* hist, uint32_t* T_out, int* rem_out) {
+// exceeds `rem`, and rem minus the weight of all keys above T.  Zero-weight
+// keys never count.  CACHED: n <= 64 * kRegKeys, keys and weights held in
+// registers; otherwise they are re-read from memory every pass.  The leading
+// bits every counted key shares are skipped (often only 2-3 passes of 8 bits).
+template <bool CACHED>
+__device__ __forceinline__ void wave_radix_select(const uint32_t* keys, const int* weights, int n, int rem,
+                                                  int* hist, uint32_t* T_out, int* rem_out) {
   const int lane = lane_id();
-  uint32_t prefix = 0, mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = lane; b < 256; b += kWave) hist[b] = 0;
+  const int live = (n + kWave - 1) / kWave;
+  uint32_t rk[CACHED ? kRegKeys : 1];
+  int rw[CACHED ? kRegKeys : 1];
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+  if (CACHED) {
+#pragma unroll
+    for (int t = 0; t < kRegKeys; ++t) {
+      const int i = lane + t * kWave;
+      // keys / weights arrays hold at least 64 * kRegKeys entries: read unconditionally
+      const bool ok = t < live && i < n;
+      const uint32_t kv = keys[i];
+      const int wv = weights ? weights[i] : 1;
+      rk[t] = ok ? kv : 0u;
+      rw[t] = ok ? wv : 0;
+      kand &= rw[t] > 0 ? rk[t] : 0xFFFFFFFFu;
+      kor |= rw[t] > 0 ? rk[t] : 0u;
+    }
+  } else {
     for (int i = lane; i < n; i += kWave) {
-      const uint32_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], weights ? weights[i] : 1);
+      if ((weights ? weights[i] : 1) > 0) {
+        kand &= keys[i];
+        kor |= keys[i];
+      }
     }
-    // lane l owns bins 255-4l .. 252-4l, i.e. the bins in descending order
-    const int h0 = hist[255 - 4 * lane], h1 = hist[254 - 4 * lane];
-    const int h2 = hist[253 - 4 * lane], h3 = hist[252 - 4 * lane];
-    const int tot = h0 + h1 + h2 + h3;
-    const int c0 = wave_incl_scan(tot) - tot;
-    const int c1 = c0 + h0, c2 = c1 + h1, c3 = c2 + h2, c4 = c3 + h3;
-    int bsel = -1, above = 0;
-    if (c0 <= rem && rem < c1) {
-      bsel = 255 - 4 * lane; above = c0;
-    } else if (c1 <= rem && rem < c2) {
-      bsel = 254 - 4 * lane; above = c1;
-    } else if (c2 <= rem && rem < c3) {
-      bsel = 253 - 4 * lane; above = c2;
-    } else if (c3 <= rem && rem < c4) {
-      bsel = 252 - 4 * lane; above = c3;
+  }
+  kand = wave_and(kand);
+  kor = wave_or(kor);
+  const uint32_t diff = kand ^ kor;
+  if (!diff) {  // every counted key is equal
+    *T_out = kand;
+    *rem_out = rem;
+    return;
+  }
+  const int top = (31 - __clz((int)diff)) >> 3;  // byte holding the highest differing bit
+  uint32_t mask = top == 3 ? 0u : (0xFFFFFFFFu << (8 * (top + 1)));
+  uint32_t prefix = kand & mask;
+  for (int shift = 8 * top; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c)
+      *reinterpret_cast<int4*>(hist + c * kHistBins + 4 * lane) = make_int4(0, 0, 0, 0);
+    int* hc = hist + (lane % kHistCopies) * kHistBins;
+    if (CACHED) {
+#pragma unroll
+      for (int t = 0; t < kRegKeys; ++t) {
+        if (t >= live) break;
+        const bool in = rw[t] > 0 && (rk[t] & mask) == prefix;
+        atomicAdd(&hc[in ? (int)((rk[t] >> shift) & 255) : 256], rw[t]);
+      }
+    } else {
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t k = keys[i];
+        const int w = weights ? weights[i] : 1;
+        const bool in = w > 0 && (k & mask) == prefix;
+        atomicAdd(&hc[in ? (int)((k >> shift) & 255) : 256], w);
+      }
     }
-    const unsigned long long bal = __ballot(bsel >= 0);
-    const int src = bal ? (int)__ffsll((long long)bal) - 1 : 0;
-    bsel = __shfl(bsel, src);
-    above = __shfl(above, src);
-    if (bsel < 0) bsel = 0;  // unreachable under the precondition; keeps the result defined
+    int above;
+    const int bsel = radix_pick_bin(hist, rem, &above);
     prefix |= (uint32_t)bsel << shift;
     mask |= 255u << shift;
     rem -= above;
@@ -88,6 +150,33 @@ __device__ __forceinline__ void qbar8(const uint16_t* q, int u, int G, int li, f
   }
 }
 
+// Partial fill of the cut cluster by one wave: the `need` highest token keys
+// (ties: smaller position first), written in position order at `o`.
+__device__ __forceinline__ void fill_cut(const uint32_t* tk, int n, int need, int lo, int o, int* hist,
+                                         int32_t* out) {
+  const int lane = lane_id();
+  uint32_t T2;
+  int rem2;
+  if (n <= kWave * kRegKeys)
+    wave_radix_select<true>(tk, nullptr, n, need, hist, &T2, &rem2);
+  else
+    wave_radix_select<false>(tk, nullptr, n, need, hist, &T2, &rem2);
+  // rem2 = how many of the key == T2 tokens to take, smallest positions first
+  int run_eq = 0, run_sel = 0;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + lane;
+    const uint32_t k = i < n ? tk[i] : 0u;
+    const int eq = (i < n && k == T2) ? 1 : 0;
+    const int eq_incl = wave_incl_scan(eq);
+    const bool sel = i < n && (k > T2 || (eq && run_eq + eq_incl - 1 < rem2));
+    const unsigned long long sb = __ballot(sel);
+    if (sel) out[o + run_sel + __popcll(sb & lt)] = lo + i;
+    run_sel += __popcll(sb);
+    run_eq += __builtin_amdgcn_readlane(eq_incl, kWave - 1);
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint16_t* __restrict__ q, int G, const float* __restrict__ cmean,
     const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ k_clu, int clu_stride,
@@ -95,11 +184,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t* __restrict__ cut_ws) {
   __shared__ uint32_t key[kMaxClusters];
   __shared__ int sz[kMaxClusters];
-  __shared__ int ost[kMaxClusters];
+  __shared__ int ost[kMaxClusters + 1];
   __shared__ int take[kMaxClusters];
-  __shared__ int hist[256];
+  __shared__ __attribute__((aligned(16))) int hist[kHistCopies * kHistBins];
   __shared__ uint32_t tkey[kCutLds];
   __shared__ int sh_cut, sh_need;
+  __shared__ uint32_t sh_T;
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -119,9 +209,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
   for (int j0 = grp; j0 < K; j0 += kSelGroups * kRowsInFlight) {
     float4 a[kRowsInFlight][2];
+    int nsz[kRowsInFlight];
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j0 + t * kSelGroups;
+      const int jc = j < K ? j : K - 1;
+      nsz[t] = off[jc + 1] - off[jc];
       if (j < K) {
         a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
         a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
@@ -138,21 +231,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       d = fmaf(qb[7], a[t][1].w, d);
       d = sum16(d);
       if (li == 0 && j < K) {
-        const int n = off[j + 1] - off[j];
-        sz[j] = n;
-        key[j] = n > 0 ? score_key(d) : 0u;
+        sz[j] = nsz[t];
+        key[j] = nsz[t] > 0 ? score_key(d) : 0u;  // empty clusters rank below every score
       }
     }
   }
   __syncthreads();
 
-  // ---- wave 0: cut cluster, whole-cluster takes and output offsets (index order)
+  // ---- phase 2, wave 0: the cut cluster (weighted radix select on the score keys)
   if (wave == 0) {
     int cut = -1, need = 0;
     uint32_t T = 0;
     if (m > budget) {
       int rem;
-      wave_radix_select(key, sz, K, beff, hist, &T, &rem);
+      wave_radix_select<true>(key, sz, K, beff, hist, &T, &rem);
       // clusters with key == T are visited in index order: the cut is the first
       // whose running size exceeds what is left
       int run = 0;
@@ -165,13 +257,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const unsigned long long b = __ballot(hit);
         if (b) {
           const int src = (int)__ffsll((long long)b) - 1;
-          cut = __shfl(j, src);
-          need = rem - __shfl(incl - w, src);
+          cut = __builtin_amdgcn_readlane(j, src);
+          need = rem - __builtin_amdgcn_readlane(incl - w, src);
           break;
         }
-        run = __shfl(incl, kWave - 1);
+        run = __builtin_amdgcn_readlane(incl, kWave - 1);
       }
     }
+    if (lane == 0) {
+      sh_cut = cut;
+      sh_need = need;
+      sh_T = T;
+    }
+  }
+  __syncthreads();
+  const int cut = sh_cut;
+  const int need = sh_need;
+  const int n_cut = cut >= 0 ? sz[cut] : 0;
+  const int lo_cut = cut >= 0 ? off[cut] : 0;
+  const bool fill = cut >= 0 && need > 0;
+  uint32_t* cut_keys_g = cut_ws + (size_t)u * clu_stride;
+
+  // ---- phase 3: waves 1.. score the cut cluster's tokens while wave 0 lays out
+  // the output (take_j and its exclusive scan over clusters in index order)
+  if (wave == 0) {
+    const uint32_t T = sh_T;
     int run = 0;
     for (int j0 = 0; j0 < K; j0 += kWave) {
       const int j = j0 + lane;
@@ -189,82 +299,63 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         ost[j] = run + incl - t;
         take[j] = t;
       }
-      run += __shfl(incl, kWave - 1);
+      run += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    if (lane == 0) {
-      sh_cut = cut;
-      sh_need = need;
-    }
-  }
-  __syncthreads();
-  const int cut = sh_cut;
-  const int need = sh_need;
-
-  // ---- whole clusters: positions off_j .. off_j + n_j - 1 at ost_j.  Each wave
-  // takes 64 clusters at a time into registers and walks them with readlane,
-  // writing one cluster's run with coalesced stores.
-  int32_t* out = sel_pos + (size_t)u * budget;
-  constexpr int kSelWaves = kSelThreads / kWave;
-  for (int jb = wave * kWave; jb < K; jb += kSelWaves * kWave) {
-    const int j = jb + lane;
-    const int t = (j < K && j != cut) ? take[j] : 0;
-    const int o = j < K ? ost[j] : 0;
-    const int lo = j < K ? off[j] : 0;
-    unsigned long long live = __ballot(t > 0);
-    while (live) {
-      const int l = (int)__ffsll((long long)live) - 1;
-      live &= live - 1;
-      const int tl = __shfl(t, l), ol = __shfl(o, l), ll = __shfl(lo, l);
-      for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
-    }
-  }
-
-  // ---- partial fill of the cut cluster
-  if (cut >= 0 && need > 0) {
-    const int lo = off[cut];
-    const int n = sz[cut];
-    uint32_t* tk = n <= kCutLds ? tkey : cut_ws + (size_t)u * clu_stride;
-    const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo) * kHeadDim + li * 8;
-    for (int i0 = grp; i0 < n; i0 += kSelGroups * 4) {
+  } else if (fill) {
+    constexpr int kGroups = kSelGroups - kWave / 16;  // row groups outside wave 0
+    const int g = grp - kWave / 16;
+    const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo_cut) * kHeadDim + li * 8;
+    for (int i0 = g; i0 < n_cut; i0 += kGroups * 4) {
       uint4 w[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int i = i0 + t * kSelGroups;
-        w[t] = i < n ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
+        const int i = i0 + t * kGroups;
+        w[t] = i < n_cut ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int i = i0 + t * kSelGroups;
+        const int i = i0 + t * kGroups;
         float d = qb[0] * bf16_lo(w[t].x);
         d = fmaf(qb[1], bf16_hi(w[t].x), d); d = fmaf(qb[2], bf16_lo(w[t].y), d);
         d = fmaf(qb[3], bf16_hi(w[t].y), d); d = fmaf(qb[4], bf16_lo(w[t].z), d);
         d = fmaf(qb[5], bf16_hi(w[t].z), d); d = fmaf(qb[6], bf16_lo(w[t].w), d);
         d = fmaf(qb[7], bf16_hi(w[t].w), d);
         d = sum16(d);
-        if (li == 0 && i < n) tk[i] = score_key(d);
+        if (li == 0 && i < n_cut) {
+          if (n_cut <= kCutLds)
+            tkey[i] = score_key(d);
+          else
+            cut_keys_g[i] = score_key(d);
+        }
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t T2;
-      int rem2;
-      wave_radix_select(tk, nullptr, n, need, hist, &T2, &rem2);
-      // rem2 = how many of the key == T2 tokens to take, smallest positions first
-      const int o = ost[cut];
-      int run_eq = 0, run_sel = 0;
-      const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      for (int i0 = 0; i0 < n; i0 += kWave) {
-        const int i = i0 + lane;
-        const uint32_t k = i < n ? tk[i] : 0u;
-        const int eq = (i < n && k == T2) ? 1 : 0;
-        const int eq_incl = wave_incl_scan(eq);
-        const bool sel = i < n && (k > T2 || (eq && run_eq + eq_incl - 1 < rem2));
-        const unsigned long long sb = __ballot(sel);
-        if (sel) out[o + run_sel + __popcll(sb & lt)] = lo + i;
-        run_sel += __popcll(sb);
-        run_eq += __shfl(eq_incl, kWave - 1);
+  }
+  __syncthreads();
+
+  // ---- phase 4: waves 1.. write whole clusters (positions off_j .. off_j + n_j - 1
+  // at ost_j, 64 slots per store instruction); wave 0 fills the cut cluster
+  int32_t* out = sel_pos + (size_t)u * budget;
+  if (wave != 0) {
+    constexpr int kWriters = kSelThreads / kWave - 1;
+    for (int jb = (wave - 1) * kWave; jb < K; jb += kWriters * kWave) {
+      const int j = jb + lane;
+      const int t = (j < K && j != cut) ? take[j] : 0;
+      const int o = j < K ? ost[j] : 0;
+      const int lo = j < K ? off[j] : 0;
+      unsigned long long live = __ballot(t > 0);
+      while (live) {
+        const int l = (int)__ffsll((long long)live) - 1;
+        live &= live - 1;
+        const int tl = __builtin_amdgcn_readlane(t, l), ol = __builtin_amdgcn_readlane(o, l);
+        const int ll = __builtin_amdgcn_readlane(lo, l);
+        for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
       }
     }
+  } else if (fill) {
+    if (n_cut <= kCutLds)
+      fill_cut(tkey, n_cut, need, lo_cut, ost[cut], hist, out);
+    else
+      fill_cut(cut_keys_g, n_cut, need, lo_cut, ost[cut], hist, out);
   }
   if (tid == 0) sel_count[u] = beff;
 }
