@@ -49,6 +49,32 @@ def select_bytes(units: int, K: int, c: int, group: int, cut_rows: int) -> int:
     return units * (4 * K * d + 8 * K + 4 + 2 * group * d + cut_rows * (2 * d + 4) + 4 * c)
 
 
+# HBM bytes per ckv_sparse_decode launch on this workload, from two rocprofv3
+# --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by what the
+# same counters read for a plain 1 GiB device copy (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0).  Valid only for the kernel sources they were taken on:
+# when the hash of those sources differs, traffic is reported as null.
+TRAFFIC_SOURCES = ("decode.hip", "common.hpp", "launch.hpp")
+TRAFFIC = {"sha256": "2e3481af3cbdf2acea02bd50589170d85a293bdf57859e5d638664446b9d672b",
+           "fetch_kib": 34165.47, "write_kib": 762.0}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "semantic_cluster_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    if TRAFFIC["sha256"] is None or TRAFFIC["sha256"] != kernel_source_hash():
+        return None
+    return TRAFFIC["fetch_kib"] * 1024 * 2.0 + TRAFFIC["write_kib"] * 1024 * 1.0
+
+
 def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
     """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -215,25 +241,39 @@ def main() -> int:
     log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.1f} tokens/s")
 
     # ---------------------------------------------------------------- kernel timing for the roofline
-    # A backlog of replayed steps keeps the GPU busy while the host enqueues the
-    # event-bracketed decode calls, so each pair of events brackets GPU work only.
-    for s in range(W, W + K):
-        run(s)
-    pairs = []
-    for li, L in enumerate(layers):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        L.sparse_decode(qs[li][W + K - 1], sel_pos[li], cnt[li], budget, outs[li])
-        b.record(stream)
-        pairs.append((a, b))
+    # ckv_sparse_decode is one kernel per call.  The calls of all layers are
+    # captured once more as a graph and replayed back to back between two
+    # events on the stream they run on; the average is per launch.
+    qlast = W + K - 1
+
+    def decode_all() -> None:
+        for li, L in enumerate(layers):
+            L.sparse_decode(qs[li][qlast], sel_pos[li], cnt[li], budget, outs[li])
+
+    if graphs:
+        dg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dg, stream=cs):
+            decode_all()
+        launch_all = dg.replay
+    else:
+        launch_all = decode_all
+    launch_all()
     torch.cuda.synchronize()
-    dec_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    reps = 5
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        launch_all()
+    b.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = a.elapsed_time(b) / (reps * n_layers)
     r_now = layers[0].n_total - layers[0].n_clustered
     dbytes = decode_bytes(units, 16, budget, r_now, G)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
     step_bytes = n_layers * (decode_bytes(units, 16, budget, (W + K) // 2, G)
                              + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
     log(f"[bench] ckv_sparse_decode {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+    traffic = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -253,7 +293,7 @@ def main() -> int:
                    "graphs": not args.no_graph},
         "roofline": {"bound": "hbm", "kernel": "ckv::sparse_decode_kernel<4>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},
         "step_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kmeans_keys_per_s": keys / prefill_ev_s,

@@ -171,6 +171,8 @@ int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* s
  * rows [n_clustered, n_total) of k_tok/v_tok.  out is f32
  * [batch, n_kv_heads * group, 128] (device, written); an empty S gives 0.
  * sel_count[u] must be <= min(budget, m) and every listed position < m.
+ * The first 4 * units bytes of the workspace are per-unit arrival counters of
+ * the split-K merge; a call leaves them zero, as ckv_workspace_init does.
  */
 int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos,
                       const int32_t* sel_count, int32_t budget, float* out, void* ws,

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters;  // reserved, kept zero
+  size_t counters;  // [units] u32 decode arrival counters (then reserved); zero between calls
   size_t hist;      // prefill / incremental: [units, tiles, K] int32
   size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
   size_t scores;    // select: [units, K] f32
@@ -305,7 +305,7 @@ int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_
   hipError_t e = ckv::launch_sparse_decode(
       q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
       sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
-      (float*)((char*)ws + w.off_partials), out, units, (hipStream_t)stream);
+      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, out, units, (hipStream_t)stream);
   return hip_status(e, "sparse_decode");
 }
 

@@ -13,7 +13,8 @@
 // owns one row of a stage (8 dims per lane) and reads back exactly the bytes
 // its lanes DMA'd.  Scores: bf16 dot2 + DPP row sums, log2 domain (q scaled
 // by log2(e)/sqrt(128)); softmax updated once per two stages.  Each chunk
-// leaves (max, sum, unnormalised output) per head; a small kernel merges them.
+// leaves (max, sum, unnormalised output) per head; the last chunk of a unit
+// to finish merges them (log-sum-exp) and writes the normalised output.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ v_tok, int capacity, const uint16_t* __restrict__ k_clu,
     const uint16_t* __restrict__ v_clu, int clu_stride, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_count, int budget, int m, int n_sink, int n_clustered,
-    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials) {
+    int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials, uint32_t* __restrict__ counters,
+    float* __restrict__ out) {
   // ring | row sources; the per-wave merge area reuses the ring afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kRingBytes + kRowSegment * 4];
   static_assert(kDecWaves * GT * kPartialStride * 4 <= kRingBytes, "merge area must fit in the ring");
@@ -260,8 +262,32 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     }
   }
   __syncthreads();
-  float* outp = partials + ((size_t)u * n_chunks + c) * GT * kPartialStride;
-  for (int t = tid; t < GT * kHeadDim; t += kDecThreads) {
+  if (n_chunks == 1) {  // the whole unit in one workgroup: normalise directly
+    for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
+      const int h = t / kHeadDim, d = t % kHeadDim;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GT + h) * kPartialStride + kHeadDim]);
+      const float Ms = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float* rw = red + (w * GT + h) * kPartialStride;
+        const float a = exp2f(rw[kHeadDim] - Ms);
+        L += rw[kHeadDim + 1] * a;
+        O += rw[d] * a;
+      }
+      out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+    }
+    return;
+  }
+  // Chunk partial (max, sum, unnormalised output) per head.  Stores and loads
+  // of partials and the arrival counter are device-scope (they bypass the
+  // per-XCD L2), so the workgroup that merges may run on any XCD; the wait
+  // before the counter increment makes this chunk's stores complete first.
+  const size_t cs = (size_t)GT * kPartialStride;
+  float* outp = partials + ((size_t)u * n_chunks + c) * cs;
+  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
     const int h = t / kHeadDim, d = t % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
@@ -275,37 +301,42 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       L += rw[kHeadDim + 1] * a;
       O += rw[d] * a;
     }
-    outp[h * kPartialStride + d] = O;
+    __hip_atomic_store(&outp[h * kPartialStride + d], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0) {
-      outp[h * kPartialStride + kHeadDim] = M;
-      outp[h * kPartialStride + kHeadDim + 1] = L;
+      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim + 1], L, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-// Log-sum-exp merge of the chunk partials: one workgroup of 128 threads per
-// (unit, head), one pass over the chunks with every load independent.
-__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ partials, int GT,
-                                                           int G, int n_chunks, float* __restrict__ out) {
-  const int u = blockIdx.x / G;
-  const int h = blockIdx.x % G;
-  const int d = threadIdx.x;
-  const size_t cs = (size_t)GT * kPartialStride;
-  const float* p = partials + (size_t)u * n_chunks * cs + h * kPartialStride;
-  float M = -INFINITY, L = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int cc = 0; cc < n_chunks; ++cc) {
-    const float mc = p[cc * cs + kHeadDim];
-    const float lc = p[cc * cs + kHeadDim + 1];
-    const float oc = p[cc * cs + d];
-    const float Mn = fmaxf(M, mc);
-    const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
-    const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
-    L = L * a0 + lc * a1;
-    O = O * a0 + oc * a1;
-    M = Mn;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int sh_last;
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == (uint32_t)(n_chunks - 1) ? 1 : 0;
   }
-  out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  __syncthreads();
+  if (!sh_last) return;
+  // last chunk of the unit to arrive: log-sum-exp merge over all chunks, every load independent
+  const float* p = partials + (size_t)u * n_chunks * cs;
+  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
+    const int h = t / kHeadDim, d = t % kHeadDim;
+    const float* ph = p + h * kPartialStride;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int cc = 0; cc < n_chunks; ++cc) {
+      const float mc = __hip_atomic_load(ph + cc * cs + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float lc = __hip_atomic_load(ph + cc * cs + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float oc = __hip_atomic_load(ph + cc * cs + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float Mn = fmaxf(M, mc);
+      const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+      const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
+      L = L * a0 + lc * a1;
+      O = O * a0 + oc * a1;
+      M = Mn;
+    }
+    out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  }
+  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static int group_tier(int G) {
@@ -319,12 +350,12 @@ hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
                                 const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
-                                float* partials, float* out, int units, hipStream_t s) {
+                                float* partials, uint32_t* counters, float* out, int units, hipStream_t s) {
   const dim3 grid((unsigned)(units * n_chunks));
 #define CKV_DEC(GTV)                                                                                \
   hipLaunchKernelGGL(sparse_decode_kernel<GTV>, grid, dim3(kDecThreads), 0, s, q, G, k_tok, v_tok, \
                      capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m, n_sink,     \
-                     n_clustered, n_total, chunk_rows, n_chunks, partials)
+                     n_clustered, n_total, chunk_rows, n_chunks, partials, counters, out)
   switch (group_tier(G)) {
     case 1: CKV_DEC(1); break;
     case 2: CKV_DEC(2); break;
@@ -333,10 +364,6 @@ hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
     default: CKV_DEC(16); break;
   }
 #undef CKV_DEC
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(units * G)), dim3(128), 0, s, partials,
-                     group_tier(G), G, n_chunks, out);
   return hipGetLastError();
 }
 
