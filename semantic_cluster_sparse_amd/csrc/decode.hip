@@ -5,77 +5,125 @@
 // §3.1 attention formula; §4.1 cluster-contiguous storage; ClusterKV
 // abstract, arXiv 2412.03213: recall at semantic-cluster granularity).
 //
-// Split-K flash decode built as an HBM stream.  A workgroup (4 waves) takes
-// one chunk of one unit's attended rows.  Each wave streams "stages" of 4
-// rows (K and V, 2 KB) straight from HBM into its own LDS ring with
-// global_load_lds_dwordx4, kStages stages ahead of the math, so every CU keeps
-// ~100 KB of row data in flight without spending VGPRs on it.  A 16-lane group
-// owns one row of a stage (8 dims per lane) and reads back exactly the bytes
-// its lanes DMA'd.  Scores: bf16 dot2 + DPP row sums, log2 domain (q scaled
-// by log2(e)/sqrt(128)); softmax updated once per two stages.  Each chunk
-// leaves (max, sum, unnormalised output) per head; the last chunk of a unit
-// to finish merges them (log-sum-exp) and writes the normalised output.
+// Split-K flash decode built as an HBM stream with the arithmetic on MFMA.
+// A workgroup (8 waves, two per SIMD) takes one chunk of one unit's attended
+// rows, in tiles of 16 rows.  Each wave DMAs its tiles (16 K rows, then 16 V rows,
+// 8 KB) straight from HBM into its own LDS ring with global_load_lds_dwordx4,
+// up to kSlots tiles ahead of the math, with an XOR swizzle of the 16-byte
+// chunks of every row so that both MFMA operand reads below are free of bank
+// conflicts.  Per tile:
+//   S = K Q^T     4 x v_mfma_f32_16x16x32_bf16 (M = rows, N = query heads,
+//                 K = head dim); lane (h + 16 g) gets rows 4g..4g+3 of head h;
+//   softmax       in the log2 domain (q scaled by log2(e)/sqrt(128)) with a
+//                 lazily moved reference max per head;
+//   O^T += V^T P^T  8 d-blocks x v_mfma_f32_16x16x16_bf16 with V^T read by
+//                 ds_read_b64_tr_b16 and P in the layout S left it in (the
+//                 contraction index k = 4g + j is row 4g + j of the tile), P
+//                 split into bf16 high and low parts (two MFMAs) so that it
+//                 keeps ~16 significant bits.
+// Each chunk leaves (max, sum, unnormalised output) per head; the last chunk
+// of a unit to finish merges them (log-sum-exp) and writes the normalised
+// output.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ckv {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
-                                         false);
-}
-
-#ifndef CKV_DEC_STAGES
-#define CKV_DEC_STAGES 8
+#ifndef CKV_DEC_SLOTS
+#define CKV_DEC_SLOTS 2
 #endif
-constexpr int kDecThreads = 256;
+#ifndef CKV_DEC_THREADS
+#define CKV_DEC_THREADS 512
+#endif
+constexpr int kDecThreads = CKV_DEC_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kStages = CKV_DEC_STAGES;     // ring depth per wave (even)
-constexpr int kStageBytes = 2048;           // 4 rows x 256 B of K, then of V
-constexpr int kRingBytes = kDecWaves * kStages * kStageBytes;
-constexpr int kRowSegment = 1024;           // row sources staged in LDS per segment
-constexpr int kCluFlag = 0x40000000;        // row source is the cluster-ordered copy
-static_assert(kStages % 2 == 0 && kStages >= 4, "stages are consumed two at a time");
-constexpr float kLazy = 8.0f;              // log2-domain slack before the reference max moves
+constexpr int kSlots = CKV_DEC_SLOTS;          // tiles per wave ring (kSlots - 1 in flight)
+constexpr int kTileBytes = 8192;               // 16 K rows then 16 V rows, 256 B each
+constexpr int kRingBytes = kDecWaves * kSlots * kTileBytes;
+constexpr int kRowSegment = 1024;              // row sources staged in LDS per segment
+constexpr int kCluFlag = 0x40000000;           // row source is the cluster-ordered copy
+static_assert(kSlots >= 2 && 8 * (kSlots - 1) <= 63, "ring depth");
+constexpr float kLazy = 8.0f;                  // log2-domain slack before the reference max moves
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // gfx9 s_waitcnt immediate with only vmcnt constrained.
 #define CKV_VMCNT(N) ((((N) & 15) | (((N) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
+// Wait until at most 8 * min(ahead, N) DMA ops (the 8 ops of each of `ahead`
+// younger tiles) are still in flight; ahead <= 0 waits for all.  s_waitcnt
+// takes an immediate, hence the unrolled chain over the uniform value.
+template <int N>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (N <= 0) {
+    __builtin_amdgcn_s_waitcnt(CKV_VMCNT(0));
+  } else {
+    if (ahead >= N)
+      __builtin_amdgcn_s_waitcnt(CKV_VMCNT(8 * N));
+    else
+      wait_tiles<N - 1>(ahead);
+  }
+}
+
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// LDS reads the compiler does not see (so it does not wait for the in-flight
-// LDS DMA of other ring stages); each waits for its own result.
-__device__ __forceinline__ uint4 lds_read_b128(uint32_t addr) {
-  uint4 v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-__device__ __forceinline__ int lds_read_b32(uint32_t addr) {
-  int v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-// The two stages consumed by one step (K and V of each) plus the row sources
-// of the two stages issued next, with a single wait.
-__device__ __forceinline__ void lds_read_step(uint32_t a0, uint32_t a1, uint32_t r0, uint32_t r1, uint4& k0,
-                                              uint4& v0, uint4& k1, uint4& v1, int& s0, int& s1) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %6 offset:1024\n\t"
-      "ds_read_b128 %2, %7\n\t"
-      "ds_read_b128 %3, %7 offset:1024\n\t"
-      "ds_read_b32 %4, %8\n\t"
-      "ds_read_b32 %5, %9\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k0), "=&v"(v0), "=&v"(k1), "=&v"(v1), "=&v"(s0), "=&v"(s1)
-      : "v"(a0), "v"(a1), "v"(r0), "v"(r1)
-      : "memory");
-}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// XOR swizzle of the 16-byte chunks of tile row n (0..15): chunk c of row n
+// lives at chunk slot c ^ swz(n).  swz is a permutation of 0..15 (so the 16
+// rows of one chunk column fall in 16 different bank groups) and every 4
+// consecutive rows map a chunk pair {2k, 2k+1} to 4 different pairs (so the
+// transposed 4-row reads of V are conflict-free too).
+__device__ __forceinline__ int swz(int n) { return ((n << 1) | (n >> 3)) & 15; }
+
+// The row sources of the 4 rows this lane DMAs for a tile (one per 4-row
+// group), read from LDS without the compiler seeing it (it would otherwise
+// wait for the in-flight LDS DMA of other ring slots).
+__device__ __forceinline__ void lds_read_rows4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, int& v0,
+                                               int& v1, int& v2, int& v3) {
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %5\n\t"
+      "ds_read_b32 %2, %6\n\t"
+      "ds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// MFMA operands of one tile: the 4 K blocks (A of S = K Q^T, 16 B per lane)
+// and the 8 transposed V blocks (A of O^T = V^T P^T, 8 B per lane).
+__device__ __forceinline__ void lds_read_tile(uint32_t base, const uint32_t (&ok)[4], const uint32_t (&ov)[8],
+                                              uint4 (&k)[4], uint2 (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]),
+        "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(base + ok[0]), "v"(base + ok[1]), "v"(base + ok[2]), "v"(base + ok[3]), "v"(base + ov[0]),
+        "v"(base + ov[1]), "v"(base + ov[2]), "v"(base + ov[3]), "v"(base + ov[4]), "v"(base + ov[5]),
+        "v"(base + ov[6]), "v"(base + ov[7])
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // RNE; x finite
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 template <int GT>
@@ -86,9 +134,10 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const int32_t* __restrict__ sel_count, int budget, int m, int n_sink, int n_clustered,
     int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials, uint32_t* __restrict__ counters,
     float* __restrict__ out) {
-  // ring | row sources; the per-wave merge area reuses the ring afterwards
+  // ring | row sources; the per-wave merge area reuses both afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kRingBytes + kRowSegment * 4];
-  static_assert(kDecWaves * GT * kPartialStride * 4 <= kRingBytes, "merge area must fit in the ring");
+  static_assert(kDecWaves * GT * kPartialStride * 4 <= kRingBytes + kRowSegment * 4,
+                "merge area must fit in the ring and row sources");
   int* rowsrc = reinterpret_cast<int*>(smem + kRingBytes);
   float* red = reinterpret_cast<float*>(smem);
 
@@ -97,168 +146,203 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int li = lane & 15;
-  const int grp = lane >> 4;  // row of the stage this lane's group owns
+  const int hl = lane & 15;  // query head of this lane in the MFMA outputs
+  const int g = lane >> 4;   // row group: rows 4g..4g+3 of a tile
 
-  uint4 qw[GT];
+  // B operand of S = K Q^T: head hl, head-dim block 32 kb + 8 g .. +7
+  bf16x8 qb[4];
 #pragma unroll
-  for (int h = 0; h < GT; ++h)
-    qw[h] = h < G ? *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8)
-                  : make_uint4(0, 0, 0, 0);
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint4 w = hl < G ? *reinterpret_cast<const uint4*>(q + ((size_t)u * G + hl) * kHeadDim + kb * 32 + g * 8)
+                           : make_uint4(0, 0, 0, 0);
+    qb[kb] = __builtin_bit_cast(bf16x8, w);
+  }
   int cnt = sel_count[u];
   const int cmax = budget < m ? budget : m;
-  cnt = cnt < 0 ? 0 : (cnt > cmax ? cmax : cnt);
-  const int sel_end = n_sink + cnt;
-  const int R = sel_end + (n_total - n_clustered);
+  // Row range of this chunk, bounded without sel_count so that the recalled
+  // positions can be fetched while sel_count is still in flight.
+  const int R_max = n_sink + cmax + (n_total - n_clustered);
   const int r0 = c * chunk_rows;
-  const int r1 = min(R, r0 + chunk_rows);
+  const int r1_max = min(R_max, r0 + chunk_rows);
 
   const float qscale = 0.12751743074602468f;  // log2(e) / sqrt(128): scores in the log2 domain
-  float mx[GT], ls[GT], acc[GT][8];
+  float M = -INFINITY, lsum = 0.f;  // reference max (the same in the 4 lanes of a head) and row sum
+  f32x4 o[8];                       // O[hl][16 nb + 4 g + j]
 #pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    mx[h] = -INFINITY;
-    ls[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* ktu = k_tok + (size_t)u * capacity * kHeadDim + li * 8;
-  const uint16_t* vtu = v_tok + (size_t)u * capacity * kHeadDim + li * 8;
-  const uint16_t* kcu = k_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
-  const uint16_t* vcu = v_clu + (size_t)u * clu_stride * kHeadDim + li * 8;
-  const int32_t* sp = sel_pos + (size_t)u * budget - n_sink;
-  unsigned char* ring = smem + wave * kStages * kStageBytes;
-  const uint32_t ring_lane = lds_addr(ring) + lane * 16;
+  const uint16_t* ktu = k_tok + (size_t)u * capacity * kHeadDim;
+  const uint16_t* vtu = v_tok + (size_t)u * capacity * kHeadDim;
+  const uint16_t* kcu = k_clu + (size_t)u * clu_stride * kHeadDim;
+  const uint16_t* vcu = v_clu + (size_t)u * clu_stride * kHeadDim;
+  const int32_t* sp = sel_pos + (size_t)u * budget;
+  unsigned char* ring = smem + wave * kSlots * kTileBytes;
+  const uint32_t ring_base = lds_addr(ring);
   const uint32_t rows_lds = lds_addr(rowsrc);
+  constexpr int kSegPerThread = kRowSegment / kDecThreads;
 
-  for (int seg = r0; seg < r1; seg += kRowSegment) {
-    const int seg_end = min(r1, seg + kRowSegment);
+  // per-lane operand offsets inside a tile slot
+  uint32_t offk[4], offv[8];
+  {
+    const int fn = swz(hl);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) offk[kb] = hl * 256 + 16 * ((4 * kb + g) ^ fn);
+    const int s = hl;
+    const int nr = 4 * g + (s >> 2);
+    const int fr = swz(nr);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      offv[nb] = 4096 + nr * 256 + 16 * ((2 * nb + ((s & 3) >> 1)) ^ fr) + 8 * (s & 1);
+  }
+  // DMA lane mapping: op i of a tile covers rows 4i..4i+3; this lane fills
+  // chunk slot (lane & 15) of row 4i + (lane >> 4), i.e. global chunk slot ^ swz(row)
+  const int dma_slot = lane & 15;
+
+  for (int seg = r0; seg < r1_max; seg += kRowSegment) {
+    const int seg_len_max = min(r1_max, seg + kRowSegment) - seg;
+    // recalled positions this thread may need (clamped into sel_pos[u, 0:budget))
+    int pos[kSegPerThread];
+#pragma unroll
+    for (int k = 0; k < kSegPerThread; ++k) {
+      const int r = seg + tid + k * kDecThreads;
+      const int pi = min(max(r - n_sink, 0), cmax - 1);
+      pos[k] = cmax > 0 ? sp[pi] : 0;
+    }
+    cnt = cnt < 0 ? 0 : (cnt > cmax ? cmax : cnt);
+    const int sel_end = n_sink + cnt;
+    const int R = sel_end + (n_total - n_clustered);
+    const int nrows = max(0, min(min(R, r0 + chunk_rows), seg + kRowSegment) - seg);
     // row sources of this segment: row index, flagged when it lives in the cluster copy
     __syncthreads();
-    for (int i = tid; i < seg_end - seg; i += kDecThreads) {
-      const int r = seg + i;
-      int v;
-      if (r < n_sink) {
-        v = r;
-      } else if (r < sel_end) {
-        int p = sp[r];
-        p = p < 0 ? 0 : (p >= m ? m - 1 : p);
-        v = p | kCluFlag;
-      } else {
-        v = n_clustered + (r - sel_end);
+#pragma unroll
+    for (int k = 0; k < kSegPerThread; ++k) {
+      const int i = tid + k * kDecThreads;
+      if (i < seg_len_max) {
+        const int r = seg + i;
+        int v;
+        if (r < n_sink) {
+          v = r;
+        } else if (r < sel_end) {
+          const int p = pos[k] < 0 ? 0 : (pos[k] >= m ? m - 1 : pos[k]);
+          v = p | kCluFlag;
+        } else {
+          v = r < R ? n_clustered + (r - sel_end) : 0;
+        }
+        rowsrc[i] = v;
       }
-      rowsrc[i] = v;
     }
     __syncthreads();
 
-    // this wave's stages: 4 consecutive rows each, waves interleaved
-    const int nrows = seg_end - seg;
-    const int n_st = (nrows + 4 * kDecWaves - 1) / (4 * kDecWaves);  // stages per wave (upper bound)
-    // stage st of this wave covers rows 4 * (st * kDecWaves + wave) .. +3 of the segment;
-    // a row index past the segment reads entry 0 (its stage is masked out)
-    auto src_slot = [&](int st) -> uint32_t {
-      const int ri = 4 * (st * kDecWaves + wave) + grp;
-      return rows_lds + (ri < nrows ? ri : 0) * 4;
-    };
-    auto issue = [&](int v, int slot) {
-      const bool clu = (v & kCluFlag) != 0;
-      const size_t row = (size_t)(v & (kCluFlag - 1)) * kHeadDim;
-      unsigned char* dst = ring + slot * kStageBytes;
-      __builtin_amdgcn_global_load_lds((gptr_t)((clu ? kcu : ktu) + row), (lptr_t)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr_t)((clu ? vcu : vtu) + row), (lptr_t)(dst + 1024), 16, 0, 0);
-    };
+    // tiles of 16 rows; this wave takes tiles wave, wave + kDecWaves, ...
+    const int n_tiles = (nrows + 15) >> 4;
+    const int n_tw = n_tiles > wave ? (n_tiles - wave + kDecWaves - 1) / kDecWaves : 0;
+    auto issue = [&](int j) {
+      const int trow0 = 16 * (wave + j * kDecWaves);
+      const uint32_t slot = ring_base + (uint32_t)((j % kSlots) * kTileBytes);
+      int v[4];
+      uint32_t ra[4];
 #pragma unroll
-    for (int st = 0; st < kStages; ++st) issue(lds_read_b32(src_slot(st)), st);
-
-    for (int st = 0; st < n_st; st += 2) {
-      const int slot = st % kStages;
-      // the two oldest stages (4 DMA ops) must have landed; 2 * (kStages - 2) may stay in flight
-      __builtin_amdgcn_s_waitcnt(CKV_VMCNT(2 * (kStages - 2)));
-      uint4 kr[2], vr[2];
-      int nx0, nx1;
-      lds_read_step(ring_lane + slot * kStageBytes, ring_lane + (slot + 1) * kStageBytes,
-                    src_slot(st + kStages), src_slot(st + kStages + 1), kr[0], vr[0], kr[1], vr[1], nx0,
-                    nx1);
-      issue(nx0, slot);
-      issue(nx1, slot + 1);
-
-      float s[2][GT];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const bool ok = 4 * ((st + k) * kDecWaves + wave) + grp < nrows;
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          float d = dot2(kr[k].x, qw[h].x, 0.f);
-          d = dot2(kr[k].y, qw[h].y, d);
-          d = dot2(kr[k].z, qw[h].z, d);
-          d = dot2(kr[k].w, qw[h].w, d);
-          d = sum16(d);
-          s[k][h] = ok ? d * qscale : -INFINITY;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int ri = trow0 + 4 * i + g;
+        ra[i] = rows_lds + (ri < nrows ? ri : 0) * 4;
       }
-      // Lazy rescaling: the reference max only moves (and the accumulators
-      // are rescaled) when a score exceeds it by more than kLazy in log2
-      // units, so p = 2^(s - ref) stays <= 2^kLazy; the merge divides it out.
+      lds_read_rows4(ra[0], ra[1], ra[2], ra[3], v[0], v[1], v[2], v[3]);
 #pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        const float mn = fmaxf(s[0][h], s[1][h]);
-        if (mn > mx[h] + kLazy) {
-          const float alpha = mx[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx[h] - mn);
-          ls[h] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        const bool clu = (v[i] & kCluFlag) != 0;
+        const int n = 4 * i + g;
+        const size_t off = (size_t)(v[i] & (kCluFlag - 1)) * kHeadDim + 8 * (dma_slot ^ swz(n));
+        __builtin_amdgcn_global_load_lds((gptr_t)((clu ? kcu : ktu) + off),
+                                         (lptr_t)(uintptr_t)(slot + 1024 * i), 16, 0, 0);
+      }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-          mx[h] = mn;
-        }
-        // mx is -inf only while every score seen is -inf (masked rows): p = 0 then
-        const float ms = mx[h] == -INFINITY ? 0.f : mx[h];
-        const float p0 = __builtin_amdgcn_exp2f(s[0][h] - ms);
-        const float p1 = __builtin_amdgcn_exp2f(s[1][h] - ms);
-        ls[h] += p0 + p1;
-        acc[h][0] = fmaf(p1, bf16_lo(vr[1].x), fmaf(p0, bf16_lo(vr[0].x), acc[h][0]));
-        acc[h][1] = fmaf(p1, bf16_hi(vr[1].x), fmaf(p0, bf16_hi(vr[0].x), acc[h][1]));
-        acc[h][2] = fmaf(p1, bf16_lo(vr[1].y), fmaf(p0, bf16_lo(vr[0].y), acc[h][2]));
-        acc[h][3] = fmaf(p1, bf16_hi(vr[1].y), fmaf(p0, bf16_hi(vr[0].y), acc[h][3]));
-        acc[h][4] = fmaf(p1, bf16_lo(vr[1].z), fmaf(p0, bf16_lo(vr[0].z), acc[h][4]));
-        acc[h][5] = fmaf(p1, bf16_hi(vr[1].z), fmaf(p0, bf16_hi(vr[0].z), acc[h][5]));
-        acc[h][6] = fmaf(p1, bf16_lo(vr[1].w), fmaf(p0, bf16_lo(vr[0].w), acc[h][6]));
-        acc[h][7] = fmaf(p1, bf16_hi(vr[1].w), fmaf(p0, bf16_hi(vr[0].w), acc[h][7]));
+      for (int i = 0; i < 4; ++i) {
+        const bool clu = (v[i] & kCluFlag) != 0;
+        const int n = 4 * i + g;
+        const size_t off = (size_t)(v[i] & (kCluFlag - 1)) * kHeadDim + 8 * (dma_slot ^ swz(n));
+        __builtin_amdgcn_global_load_lds((gptr_t)((clu ? vcu : vtu) + off),
+                                         (lptr_t)(uintptr_t)(slot + 4096 + 1024 * i), 16, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+      if (j < n_tw) issue(j);
+
+    for (int j = 0; j < n_tw; ++j) {
+      // this tile's 8 DMA ops must have landed; younger tiles may stay in flight
+      wait_tiles<kSlots - 1>(n_tw - 1 - j);
+      uint4 kop[4];
+      uint2 vop[8];
+      lds_read_tile(ring_base + (uint32_t)((j % kSlots) * kTileBytes), offk, offv, kop, vop);
+      if (j + kSlots < n_tw) issue(j + kSlots);
+
+      // S = K Q^T: lane (hl + 16 g) gets rows 4g..4g+3 of head hl
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[kb]), qb[kb], sacc, 0, 0, 0);
+      const int trow = 16 * (wave + j * kDecWaves) + 4 * g;
+      float sv[4];
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = hl < G && trow + e < nrows;
+        sv[e] = ok ? sacc[e] * qscale : -INFINITY;
+        lmax = fmaxf(lmax, sv[e]);
+      }
+      // Lazy rescaling: the reference max of a head only moves (and its
+      // accumulators are rescaled) when a score exceeds it by more than
+      // kLazy log2 units, so p = 2^(s - M) stays <= 2^kLazy.  The new max is
+      // taken over the head's 4 lanes, so they keep one reference.
+      if (__ballot(lmax > M + kLazy)) {
+        float gm = fmaxf(lmax, __shfl_xor(lmax, 16));
+        gm = fmaxf(gm, __shfl_xor(gm, 32));
+        const float Mn = gm > M + kLazy ? gm : M;
+        const float alpha = Mn == M ? 1.f : __builtin_amdgcn_exp2f(M - Mn);  // M = -inf -> 0
+        lsum *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
+        M = Mn;
+      }
+      // M is -inf only while every score of the head is -inf: p = 0 then
+      const float ms = M == -INFINITY ? 0.f : M;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[e] - ms);
+        const float p1 = __builtin_amdgcn_exp2f(sv[e + 1] - ms);
+        lsum += p0 + p1;
+        const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+        const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
+        hi[e >> 1] = h0 | (h1 << 16);
+        lo[e >> 1] = l0 | (l1 << 16);
+      }
+      const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0], hi[1]));
+      const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0], lo[1]));
+      // O^T += V^T P^T, contraction over the tile's rows (k = 4g + j)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const s16x4 vt = __builtin_bit_cast(s16x4, vop[nb]);
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, phi, o[nb], 0, 0, 0);
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, plo, o[nb], 0, 0, 0);
       }
     }
-    // drain the DMA issued past the end of this wave's stages before the ring is reused
-    __builtin_amdgcn_s_waitcnt(CKV_VMCNT(0));
   }
 
-  // merge the 4 row groups of this wave (lane bits 4 and 5)
-#pragma unroll
-  for (int o = 16; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const float mo = __shfl_xor(mx[h], o);
-      const float lo = __shfl_xor(ls[h], o);
-      const float M = fmaxf(mx[h], mo);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      const float as = exp2f(mx[h] - Ms), ao = exp2f(mo - Ms);
-      ls[h] = ls[h] * as + lo * ao;
-      mx[h] = M;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(acc[h][e], o);
-        acc[h][e] = acc[h][e] * as + other * ao;
-      }
-    }
-  }
+  // this wave's row sums over its 4 row groups; M is already common to them
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
   __syncthreads();  // every wave is done with the ring before it becomes the merge area
-  if (lane < 16) {
+  if (hl < G) {
+    float* rw = red + (wave * GT + hl) * kPartialStride;
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float* rw = red + (wave * GT + h) * kPartialStride;
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rw[li * 8 + e] = acc[h][e];
-      if (lane == 0) {
-        rw[kHeadDim] = mx[h];
-        rw[kHeadDim + 1] = ls[h];
-      }
+      for (int e = 0; e < 4; ++e) rw[16 * nb + 4 * g + e] = o[nb][e];
+    if (g == 0) {
+      rw[kHeadDim] = M;
+      rw[kHeadDim + 1] = lsum;
     }
   }
   __syncthreads();
@@ -323,16 +407,27 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const int h = t / kHeadDim, d = t % kHeadDim;
     const float* ph = p + h * kPartialStride;
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int cc = 0; cc < n_chunks; ++cc) {
-      const float mc = __hip_atomic_load(ph + cc * cs + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float lc = __hip_atomic_load(ph + cc * cs + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float oc = __hip_atomic_load(ph + cc * cs + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float Mn = fmaxf(M, mc);
-      const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
-      const float a0 = exp2f(M - Ms), a1 = exp2f(mc - Ms);
-      L = L * a0 + lc * a1;
-      O = O * a0 + oc * a1;
-      M = Mn;
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+      // all loads of 8 chunks in flight together (indices clamped, extras ignored)
+      float mc[8], lc[8], oc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* pc = ph + min(c0 + k, n_chunks - 1) * cs;
+        mc[k] = __hip_atomic_load(pc + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lc[k] = __hip_atomic_load(pc + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        oc[k] = __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (c0 + k < n_chunks) {
+          const float Mn = fmaxf(M, mc[k]);
+          const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
+          const float a0 = exp2f(M - Ms), a1 = exp2f(mc[k] - Ms);
+          L = L * a0 + lc[k] * a1;
+          O = O * a0 + oc[k] * a1;
+          M = Mn;
+        }
+      }
     }
     out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
   }
