@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counters;  // [units] u32 decode arrival counters (then reserved); zero between calls
+  size_t counters;  // [2 units] u32 arrival counters: decode, then select; zero between calls
   size_t hist;      // prefill / incremental: [units, tiles, K] int32
   size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
   size_t scores;    // select: [units, K] f32
@@ -265,7 +265,7 @@ int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* s
   hipError_t e = ckv::launch_select(q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_clu,
                                     L->capacity - L->n_sink, budget, sel_pos, sel_count,
                                     (float*)((char*)ws + w.off_scores), (uint32_t*)((char*)ws + w.off_cut),
-                                    units, (hipStream_t)stream);
+                                    (uint32_t*)ws + units, units, (hipStream_t)stream);
   return hip_status(e, "select");
 }
 

@@ -7,20 +7,27 @@
 // fit; the first that does not fit contributes its highest q_bar.k tokens
 // (ties: smaller position) so exactly min(budget, m) tokens are recalled.
 //
-// The walk in score order is a weighted selection: the cut cluster is the one
-// whose score key T splits the clusters into those above T (taken whole,
-// total size <= budget) and the rest.  It is found without sorting by a
-// wave-synchronous radix select on order-preserving 32-bit score keys with
-// cluster sizes as weights (4 passes of 8 bits); the partial fill inside the
-// cut cluster is the same select with unit weights.  One workgroup of 1024
-// threads per unit, three block barriers; recalled positions are written by
-// whole waves so every store instruction covers 64 consecutive slots.
+// The walk in score order is a weighted selection: the clusters before the
+// cut (in descending score) are taken whole, the cut cluster gives what is
+// left of the budget.  It is found without sorting.  Scores are bucketed
+// linearly between their min and max (1024 buckets, a monotone map); a block
+// scan of the bucket weights in descending order finds the bucket where the
+// running size crosses the budget; only the few clusters inside that bucket
+// are ranked exactly (order-preserving 32-bit score keys, ties to the smaller
+// index).  The partial fill inside the cut cluster is the same selection with
+// unit weights over the q_bar.k scores of its tokens.  A crossing bucket with
+// more than 64 members, or a degenerate score range, falls back to a
+// wave-synchronous weighted radix select on the keys.  One workgroup of 1024
+// threads per unit; the barriers wait on LDS only, so global loads stay in
+// flight across them.  Recalled positions are written by whole waves, 64
+// consecutive slots per store instruction.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ckv {
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelSplit = 4;                  // workgroups per unit for the cluster scores
 constexpr int kSelGroups = kSelThreads / 16;  // 16-lane row groups
 constexpr int kCutLds = 4096;                 // cut-cluster keys kept in LDS up to this size
 
@@ -177,21 +184,221 @@ __device__ __forceinline__ void fill_cut(const uint32_t* tk, int n, int need, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block-level pieces (1024 threads).
+// ---------------------------------------------------------------------------
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBuckets = 1024;
+constexpr int kMaxCand = 64;
+
+// Barrier that waits for this thread's LDS operations only: global loads stay
+// in flight across it.  The memory clobbers keep the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // convergent: never duplicated into divergent code
+  asm volatile("" ::: "memory");
+}
+
+// Inclusive prefix sum over the 1024 threads; scr needs kSelWaves ints.  The
+// caller separates two uses of scr with a barrier.
+__device__ __forceinline__ int block_incl_scan(int v, int* scr, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == kWave - 1) scr[wave] = x;
+  lds_barrier();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int t = scr[w];
+    pre += w < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  return pre + x;
+}
+
+// Min / max over the 64 lanes of a wave (DPP within rows of 16, then the four
+// row results through readlane); the result is wave-uniform.
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_f32<kDppXor1>(v));
+  v = fminf(v, dpp_f32<kDppXor2>(v));
+  v = fminf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fminf(v, dpp_f32<kDppMirror>(v));
+  const int x = __float_as_int(v);
+  return fminf(fminf(__int_as_float(__builtin_amdgcn_readlane(x, 0)), __int_as_float(__builtin_amdgcn_readlane(x, 16))),
+               fminf(__int_as_float(__builtin_amdgcn_readlane(x, 32)), __int_as_float(__builtin_amdgcn_readlane(x, 48))));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  const int x = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 0)), __int_as_float(__builtin_amdgcn_readlane(x, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(x, 32)), __int_as_float(__builtin_amdgcn_readlane(x, 48))));
+}
+
+// LDS scratch of one block selection.
+struct SelScratch {
+  int bw[kBuckets];                 // bucket weights  } zero between selections
+  int bc[kBuckets];                 // bucket counts   }
+  float rmin[kSelWaves], rmax[kSelWaves];
+  int scr[kSelWaves];
+  int cand[kMaxCand];
+  int rs_w[kMaxCand], rs_i[kMaxCand];
+  int hdr[8];                       // crossing bucket, weight above it, its count, candidates, cut, need
+  unsigned char dec[kCutLds];       // state of the crossing bucket's members (several-member case)
+};
+
+// Monotone map of a score in [lo, lo + range] to a bucket in [0, kBuckets).
+__device__ __forceinline__ int score_bucket(float v, float lo, float scale) {
+  const float x = (v - lo) * scale;
+  return x < (float)(kBuckets - 1) ? (int)x : kBuckets - 1;
+}
+
+// Score range from the per-wave partials in ws.rmin / ws.rmax; false if it is
+// degenerate (all equal, or not finite).
+__device__ __forceinline__ bool score_range(const SelScratch& ws, float* lo, float* scale) {
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kSelWaves; ++v) {
+    mn = fminf(mn, ws.rmin[v]);
+    mx = fmaxf(mx, ws.rmax[v]);
+  }
+  const float range = mx - mn;
+  const float sc = (float)kBuckets / range;
+  *lo = mn;
+  *scale = sc;
+  return range > 0.f && range < INFINITY && sc > 0.f && sc < INFINITY;
+}
+
+// Descending weighted selection by the whole block over n <= E * 1024
+// elements held in LDS: scores sc[i] (finite), order-preserving keys key[i],
+// weights w[i] (unit if UNIT; weight 0 never counts); thread t owns elements
+// E t .. E t + E - 1.  Walking the elements by (key desc, index asc) with
+// running weight R before element e, the state of e is 2 if R + w_e <=
+// budget, 1 if R < budget < R + w_e (it gets budget - R), 0 otherwise.
+// Requires total counted weight > budget >= 0, a non-degenerate score range
+// (lo, scale from score_range) and ws.bw / ws.bc zero; leaves them zero.
+// The scores are bucketed linearly; a block scan over the buckets in
+// descending order finds the bucket where the running weight crosses the
+// budget.  When that bucket has a single member (the usual case) its state
+// follows at once; otherwise its members (at most kMaxCand) are ranked
+// exactly by wave 0.  st[e] receives the states of this thread's elements; the
+// state-1 element and its share land in ws.hdr[4], ws.hdr[5] (-1 / 0 if
+// none), readable after the caller's next barrier.  Returns false
+// (block-uniform) when the crossing bucket has more than kMaxCand members.
+template <int E, bool UNIT>
+__device__ __forceinline__ bool block_select(const float* sc, const uint32_t* key, const int* w, int n,
+                                             int budget, float lo, float scale, SelScratch& ws, int (&st)[E]) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  int b[E], wt[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    const int wi = i < n ? (UNIT ? 1 : w[i]) : 0;
+    wt[e] = wi > 0 ? wi : 0;
+    b[e] = wt[e] > 0 ? score_bucket(sc[i], lo, scale) : -1;
+    if (wt[e] > 0) {
+      atomicAdd(&ws.bw[b[e]], wt[e]);
+      atomicAdd(&ws.bc[b[e]], 1);
+    }
+  }
+  if (tid == 0) {
+    ws.hdr[4] = -1;
+    ws.hdr[5] = 0;
+  }
+  lds_barrier();
+  // descending scan: thread t holds bucket kBuckets-1-t
+  const int bt = kBuckets - 1 - tid;
+  const int v = ws.bw[bt];
+  const int cb = ws.bc[bt];
+  int total;
+  const int incl = block_incl_scan(v, ws.scr, &total);
+  if (v > 0 && incl - v <= budget && budget < incl) {
+    ws.hdr[0] = bt;
+    ws.hdr[1] = incl - v;
+    ws.hdr[2] = cb;
+    ws.hdr[3] = 0;
+  }
+  ws.bw[bt] = 0;  // re-arm for the next selection
+  ws.bc[bt] = 0;
+  lds_barrier();
+  const int bstar = ws.hdr[0], above = ws.hdr[1], nb = ws.hdr[2];
+  if (nb == 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (b[e] != bstar) {
+        st[e] = b[e] > bstar ? 2 : 0;
+      } else {
+        st[e] = above + wt[e] <= budget ? 2 : (above < budget ? 1 : 0);
+        if (st[e] == 1) {
+          ws.hdr[4] = tid * E + e;
+          ws.hdr[5] = budget - above;
+        }
+      }
+    }
+    return true;
+  }
+  if (nb > kMaxCand) return false;
+  // several members: exact order inside the crossing bucket, rank by (key desc, index asc)
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (b[e] == bstar) ws.cand[atomicAdd(&ws.hdr[3], 1)] = tid * E + e;
+  lds_barrier();
+  if (wave == 0) {
+    const int ci = lane < nb ? ws.cand[lane] : 0;
+    const uint32_t ck = lane < nb ? key[ci] : 0u;
+    int rank = 0;
+    for (int l = 0; l < nb; ++l) {
+      const uint32_t kl = (uint32_t)__builtin_amdgcn_readlane((int)ck, l);
+      const int il = __builtin_amdgcn_readlane(ci, l);
+      rank += (kl > ck || (kl == ck && il < ci)) ? 1 : 0;
+    }
+    if (lane < nb) {
+      ws.rs_w[rank] = UNIT ? 1 : w[ci];
+      ws.rs_i[rank] = ci;
+    }
+    const int wr = lane < nb ? ws.rs_w[lane] : 0;
+    const int ir = lane < nb ? ws.rs_i[lane] : 0;
+    const int rrun = above + wave_incl_scan(wr) - wr;  // weight before this rank
+    if (lane < nb) {
+      const int s2 = rrun + wr <= budget ? 2 : (rrun < budget ? 1 : 0);
+      ws.dec[ir] = (unsigned char)s2;
+      if (s2 == 1) {
+        ws.hdr[4] = ir;
+        ws.hdr[5] = budget - rrun;
+      }
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int e = 0; e < E; ++e) st[e] = b[e] != bstar ? (b[e] > bstar ? 2 : 0) : (int)ws.dec[tid * E + e];
+  return true;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint16_t* __restrict__ q, int G, const float* __restrict__ cmean,
     const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ k_clu, int clu_stride,
-    int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count,
-    uint32_t* __restrict__ cut_ws) {
-  __shared__ uint32_t key[kMaxClusters];
-  __shared__ int sz[kMaxClusters];
-  __shared__ int ost[kMaxClusters + 1];
+    int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count, float* __restrict__ scores_ws,
+    uint32_t* __restrict__ cut_ws, uint32_t* __restrict__ counters) {
+  __shared__ __attribute__((aligned(16))) uint32_t key[kMaxClusters];
+  __shared__ __attribute__((aligned(16))) float csc[kMaxClusters];
+  __shared__ __attribute__((aligned(16))) int sz[kMaxClusters];
+  __shared__ int ost[kMaxClusters];
   __shared__ int take[kMaxClusters];
   __shared__ __attribute__((aligned(16))) int hist[kHistCopies * kHistBins];
-  __shared__ uint32_t tkey[kCutLds];
-  __shared__ int sh_cut, sh_need;
-  __shared__ uint32_t sh_T;
+  __shared__ __attribute__((aligned(16))) uint32_t tkey[kCutLds];
+  __shared__ __attribute__((aligned(16))) float tsc[kCutLds];
+  __shared__ __attribute__((aligned(16))) SelScratch ws;
+  __shared__ int sh_cut, sh_need, sh_last;
 
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / kSelSplit;
+  const int part = blockIdx.x % kSelSplit;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
@@ -204,18 +411,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   float qb[8];
   qbar8(q, u, G, li, qb);
 
-  // ---- cluster score keys: 16 lanes per centroid row, 8 rows in flight per group
-  constexpr int kRowsInFlight = 8;
+  // ---- phase 1: this workgroup's share of the cluster scores (16 lanes per
+  // centroid row, every row of the share in flight at once), stored
+  // device-scope; the last workgroup of the unit to finish goes on
+  constexpr int kRowsInFlight = 4;
+  static_assert(kSelGroups * kRowsInFlight * kSelSplit >= kMaxClusters, "one round covers K");
+  const int j_lo = part * K / kSelSplit, j_hi = (part + 1) * K / kSelSplit;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
-  for (int j0 = grp; j0 < K; j0 += kSelGroups * kRowsInFlight) {
+  float* sc_u = scores_ws + (size_t)u * K;
+  {
     float4 a[kRowsInFlight][2];
-    int nsz[kRowsInFlight];
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
-      const int j = j0 + t * kSelGroups;
-      const int jc = j < K ? j : K - 1;
-      nsz[t] = off[jc + 1] - off[jc];
-      if (j < K) {
+      const int j = j_lo + grp + t * kSelGroups;
+      if (j < j_hi) {
         a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
         a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
       } else {
@@ -224,149 +433,207 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
-      const int j = j0 + t * kSelGroups;
+      const int j = j_lo + grp + t * kSelGroups;
       float d = qb[0] * a[t][0].x;
       d = fmaf(qb[1], a[t][0].y, d); d = fmaf(qb[2], a[t][0].z, d); d = fmaf(qb[3], a[t][0].w, d);
       d = fmaf(qb[4], a[t][1].x, d); d = fmaf(qb[5], a[t][1].y, d); d = fmaf(qb[6], a[t][1].z, d);
       d = fmaf(qb[7], a[t][1].w, d);
       d = sum16(d);
-      if (li == 0 && j < K) {
-        sz[j] = nsz[t];
-        key[j] = nsz[t] > 0 ? score_key(d) : 0u;  // empty clusters rank below every score
-      }
+      if (li == 0 && j < j_hi) __hip_atomic_store(&sc_u[j], d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();
-
-  // ---- phase 2, wave 0: the cut cluster (weighted radix select on the score keys)
-  if (wave == 0) {
-    int cut = -1, need = 0;
-    uint32_t T = 0;
-    if (m > budget) {
-      int rem;
-      wave_radix_select<true>(key, sz, K, beff, hist, &T, &rem);
-      // clusters with key == T are visited in index order: the cut is the first
-      // whose running size exceeds what is left
-      int run = 0;
-      for (int j0 = 0; j0 < K; j0 += kWave) {
-        const int j = j0 + lane;
-        const bool eq = j < K && key[j] == T;
-        const int w = eq ? sz[j] : 0;
-        const int incl = run + wave_incl_scan(w);
-        const bool hit = eq && incl > rem && incl - w <= rem;
-        const unsigned long long b = __ballot(hit);
-        if (b) {
-          const int src = (int)__ffsll((long long)b) - 1;
-          cut = __builtin_amdgcn_readlane(j, src);
-          need = rem - __builtin_amdgcn_readlane(incl - w, src);
-          break;
-        }
-        run = __builtin_amdgcn_readlane(incl, kWave - 1);
-      }
+  // this workgroup's stores are complete before the arrival count moves
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = prev == (uint32_t)(kSelSplit - 1) ? 1 : 0;
+  }
+  lds_barrier();
+  if (!sh_last) return;
+  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ws.bw[tid] = 0;
+  ws.bc[tid] = 0;
+  {
+    float mn = INFINITY, mx = -INFINITY;
+    if (tid < K) {
+      const float d = __hip_atomic_load(&sc_u[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int nsz = off[tid + 1] - off[tid];
+      sz[tid] = nsz;
+      csc[tid] = d;
+      key[tid] = nsz > 0 ? score_key(d) : 0u;  // empty clusters rank below every score
+      if (nsz > 0) mn = mx = d;
     }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
     if (lane == 0) {
-      sh_cut = cut;
-      sh_need = need;
-      sh_T = T;
+      ws.rmin[wave] = mn;
+      ws.rmax[wave] = mx;
     }
   }
-  __syncthreads();
-  const int cut = sh_cut;
-  const int need = sh_need;
-  const int n_cut = cut >= 0 ? sz[cut] : 0;
-  const int lo_cut = cut >= 0 ? off[cut] : 0;
-  const bool fill = cut >= 0 && need > 0;
-  uint32_t* cut_keys_g = cut_ws + (size_t)u * clu_stride;
+  lds_barrier();
 
-  // ---- phase 3: waves 1.. score the cut cluster's tokens while wave 0 lays out
-  // the output (take_j and its exclusive scan over clusters in index order)
-  if (wave == 0) {
-    const uint32_t T = sh_T;
-    int run = 0;
-    for (int j0 = 0; j0 < K; j0 += kWave) {
-      const int j = j0 + lane;
-      int t = 0;
-      if (j < K) {
-        if (cut < 0) {
-          t = sz[j];
-        } else {
+  // ---- phase 2: which clusters are taken whole, the cut, and the output
+  // layout (exclusive scan of the taken amounts in index order)
+  {
+    int st[1] = {2};
+    bool fast = true;
+    if (m > budget) {
+      float lo, scale;
+      fast = score_range(ws, &lo, &scale) && block_select<1, false>(csc, key, sz, K, beff, lo, scale, ws, st);
+    } else if (tid == 0) {
+      ws.hdr[4] = -1;
+      ws.hdr[5] = 0;
+    }
+    if (!fast) {
+      // degenerate scores or a crowded crossing bucket: weighted radix select
+      // on the keys by wave 0, then the walk among equal keys
+      if (wave == 0) {
+        uint32_t T = 0;
+        int rem, cut = -1, need = 0;
+        wave_radix_select<true>(key, sz, K, beff, hist, &T, &rem);
+        int run = 0;
+        for (int j0 = 0; j0 < K; j0 += kWave) {
+          const int j = j0 + lane;
+          const bool eq = j < K && key[j] == T;
+          const int w = eq ? sz[j] : 0;
+          const int incl = run + wave_incl_scan(w);
+          const bool hit = eq && incl > rem && incl - w <= rem;
+          const unsigned long long bb = __ballot(hit);
+          if (bb) {
+            const int src = (int)__ffsll((long long)bb) - 1;
+            cut = __builtin_amdgcn_readlane(j, src);
+            need = rem - __builtin_amdgcn_readlane(incl - w, src);
+            break;
+          }
+          run = __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        for (int j = lane; j < K; j += kWave) {
           const uint32_t k = key[j];
-          t = (k > T || (k == T && j < cut)) ? sz[j] : (j == cut ? need : 0);
+          take[j] = sz[j] > 0 && (k > T || (k == T && j < cut)) ? 2 : (j == cut && need > 0 ? 1 : 0);
+        }
+        if (lane == 0) {
+          ws.hdr[4] = need > 0 ? cut : -1;
+          ws.hdr[5] = need;
         }
       }
-      const int incl = wave_incl_scan(t);
-      if (j < K) {
-        ost[j] = run + incl - t;
-        take[j] = t;
-      }
-      run += __builtin_amdgcn_readlane(incl, kWave - 1);
+      lds_barrier();
+      st[0] = tid < K ? take[tid] : 0;
     }
-  } else if (fill) {
-    constexpr int kGroups = kSelGroups - kWave / 16;  // row groups outside wave 0
-    const int g = grp - kWave / 16;
-    const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo_cut) * kHeadDim + li * 8;
-    for (int i0 = g; i0 < n_cut; i0 += kGroups * 4) {
-      uint4 w[4];
+    // the amounts: whole clusters, and the cut's share (known to its owner)
+    const int j = tid;
+    int amt = 0;
+    if (j < K) amt = st[0] == 2 ? sz[j] : (st[0] == 1 ? ws.hdr[5] : 0);
+    int total;
+    const int incl = block_incl_scan(amt, ws.scr, &total);
+    if (j < K) {
+      ost[j] = incl - amt;
+      take[j] = st[0] == 2 ? amt : 0;
+    }
+  }
+  lds_barrier();
+  const int cut = ws.hdr[4];
+  const int need = ws.hdr[5];
+  const bool fill = cut >= 0;
+  const int n_cut = fill ? sz[cut] : 0;
+  const int lo_cut = fill ? off[cut] : 0;
+
+  // ---- phase 3: scores q_bar . k of the cut cluster's tokens (and their range)
+  constexpr int kCutRows = 4;
+  const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo_cut) * kHeadDim + li * 8;
+  uint32_t* cut_keys_g = cut_ws + (size_t)u * clu_stride;
+  {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int r0 = 0; r0 < n_cut; r0 += kCutRows * kSelGroups) {
+      uint4 cw[kCutRows];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int i = i0 + t * kGroups;
-        w[t] = i < n_cut ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
+      for (int t = 0; t < kCutRows; ++t) {
+        const int i = r0 + grp + t * kSelGroups;
+        cw[t] = i < n_cut ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int i = i0 + t * kGroups;
-        float d = qb[0] * bf16_lo(w[t].x);
-        d = fmaf(qb[1], bf16_hi(w[t].x), d); d = fmaf(qb[2], bf16_lo(w[t].y), d);
-        d = fmaf(qb[3], bf16_hi(w[t].y), d); d = fmaf(qb[4], bf16_lo(w[t].z), d);
-        d = fmaf(qb[5], bf16_hi(w[t].z), d); d = fmaf(qb[6], bf16_lo(w[t].w), d);
-        d = fmaf(qb[7], bf16_hi(w[t].w), d);
+      for (int t = 0; t < kCutRows; ++t) {
+        const int i = r0 + grp + t * kSelGroups;
+        float d = qb[0] * bf16_lo(cw[t].x);
+        d = fmaf(qb[1], bf16_hi(cw[t].x), d); d = fmaf(qb[2], bf16_lo(cw[t].y), d);
+        d = fmaf(qb[3], bf16_hi(cw[t].y), d); d = fmaf(qb[4], bf16_lo(cw[t].z), d);
+        d = fmaf(qb[5], bf16_hi(cw[t].z), d); d = fmaf(qb[6], bf16_lo(cw[t].w), d);
+        d = fmaf(qb[7], bf16_hi(cw[t].w), d);
         d = sum16(d);
         if (li == 0 && i < n_cut) {
-          if (n_cut <= kCutLds)
+          mn = fminf(mn, d);
+          mx = fmaxf(mx, d);
+          if (n_cut <= kCutLds) {
             tkey[i] = score_key(d);
-          else
+            tsc[i] = d;
+          } else {
             cut_keys_g[i] = score_key(d);
+          }
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- phase 4: waves 1.. write whole clusters (positions off_j .. off_j + n_j - 1
-  // at ost_j, 64 slots per store instruction); wave 0 fills the cut cluster
-  int32_t* out = sel_pos + (size_t)u * budget;
-  if (wave != 0) {
-    constexpr int kWriters = kSelThreads / kWave - 1;
-    for (int jb = (wave - 1) * kWave; jb < K; jb += kWriters * kWave) {
-      const int j = jb + lane;
-      const int t = (j < K && j != cut) ? take[j] : 0;
-      const int o = j < K ? ost[j] : 0;
-      const int lo = j < K ? off[j] : 0;
-      unsigned long long live = __ballot(t > 0);
-      while (live) {
-        const int l = (int)__ffsll((long long)live) - 1;
-        live &= live - 1;
-        const int tl = __builtin_amdgcn_readlane(t, l), ol = __builtin_amdgcn_readlane(o, l);
-        const int ll = __builtin_amdgcn_readlane(lo, l);
-        for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
-      }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      ws.rmin[wave] = mn;
+      ws.rmax[wave] = mx;
     }
-  } else if (fill) {
-    if (n_cut <= kCutLds)
-      fill_cut(tkey, n_cut, need, lo_cut, ost[cut], hist, out);
-    else
-      fill_cut(cut_keys_g, n_cut, need, lo_cut, ost[cut], hist, out);
+  }
+  if (n_cut > kCutLds) __threadfence_block();  // the wave-0 fallback below re-reads cut_keys_g
+  lds_barrier();
+
+  // ---- phase 4: the need highest-scoring tokens of the cut cluster, written
+  // in position order (4 consecutive tokens per thread)
+  int32_t* out = sel_pos + (size_t)u * budget;
+  if (fill) {
+    constexpr int E = kCutLds / kSelThreads;
+    int st[E];
+    float lo, scale;
+    const bool tok_fast = n_cut <= kCutLds && score_range(ws, &lo, &scale) &&
+                          block_select<E, true>(tsc, tkey, nullptr, n_cut, need, lo, scale, ws, st);
+    if (tok_fast) {
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += st[e] == 2 ? 1 : 0;
+      int total;
+      int o = ost[cut] + block_incl_scan(cnt, ws.scr, &total) - cnt;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (st[e] == 2) out[o++] = lo_cut + tid * E + e;
+    } else if (wave == 0) {
+      if (n_cut <= kCutLds)
+        fill_cut(tkey, n_cut, need, lo_cut, ost[cut], hist, out);
+      else
+        fill_cut(cut_keys_g, n_cut, need, lo_cut, ost[cut], hist, out);
+    }
+  }
+
+  // ---- phase 5: whole clusters (positions off_j .. off_j + n_j - 1 at ost_j,
+  // 64 consecutive slots per store instruction)
+  for (int jb = wave * kWave; jb < K; jb += kSelThreads) {
+    const int j = jb + lane;
+    const int t = j < K ? take[j] : 0;
+    const int o = j < K ? ost[j] : 0;
+    const int lo2 = j < K ? off[j] : 0;
+    unsigned long long live = __ballot(t > 0);
+    while (live) {
+      const int l = (int)__ffsll((long long)live) - 1;
+      live &= live - 1;
+      const int tl = __builtin_amdgcn_readlane(t, l), ol = __builtin_amdgcn_readlane(o, l);
+      const int ll = __builtin_amdgcn_readlane(lo2, l);
+      for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
+    }
   }
   if (tid == 0) sel_count[u] = beff;
 }
 
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean, const int32_t* offsets,
                          int K, const uint16_t* k_clu, int clu_stride, int budget, int32_t* sel_pos,
-                         int32_t* sel_count, float* scores_ws, uint32_t* cut_ws, int units,
-                         hipStream_t s) {
-  (void)scores_ws;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(kSelThreads), 0, s, q, group, cmean,
-                     offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, cut_ws);
+                         int32_t* sel_count, float* scores_ws, uint32_t* cut_ws, uint32_t* counters,
+                         int units, hipStream_t s) {
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * kSelSplit)), dim3(kSelThreads), 0, s, q, group,
+                     cmean, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, scores_ws, cut_ws,
+                     counters);
   return hipGetLastError();
 }
 
