@@ -4,8 +4,8 @@ Workload (``llama8b-stack-32k-b8``): 32 Llama-3.1-8B-shaped layers, batch 8,
 8 KV heads x 4 query heads, head_dim 128, 32768-token context per sequence
 (16 sinks + 32752 clustered keys, 400 clusters per KV head, 10 Lloyd
 rounds), recall budget 2048.  One *step* is one decode token for the whole
-batch through all 32 layers: per layer ckv_append + ckv_select +
-ckv_sparse_decode.  Prefill clustering is timed separately (K-means keys/s).
+batch through all 32 layers: per layer ckv_append_select (the new token's
+K/V row written and the recall, one launch) + ckv_sparse_decode.  Prefill clustering is timed separately (K-means keys/s).
 
 Inputs are synthetic (seeded Gaussian-mixture keys on the GPU) and resident
 in HBM before the timed region.  Each step is captured once as a HIP graph
@@ -206,8 +206,7 @@ def main() -> int:
 
     def step(s: int) -> None:
         for li, L in enumerate(layers):
-            L.append(k_new[s], v_new[s])
-            L.select(qs[li][s], budget, sel_pos[li], cnt[li])
+            L.append_select(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li])
             L.sparse_decode(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
 
     graphs = []

@@ -163,6 +163,17 @@ int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* s
                int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ckv_append followed by ckv_select in one launch (one decode step's token
+ * write and recall): writes k_new / v_new (bf16 [units, 128], device) into
+ * row n_total of k_tok / v_tok, recalls exactly as ckv_select does (recall
+ * never reads the token-order rows), and advances n_total.  Errors as for
+ * either call; nothing is enqueued on error.
+ */
+int ckv_append_select(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t budget, int32_t* sel_pos, int32_t* sel_count, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
  * Sparse decode (ClusterKV article §3.1 attention; §4.1 cluster-contiguous
  * rows): for every query head g of unit u,
  *   out[b, h * group + g, :] = softmax(q_g . K_S^T / sqrt(128)) V_S

@@ -13,6 +13,7 @@ from .ckv import (  # noqa: F401
     CkvLayerStruct,
     ckv_abi_layer_bytes,
     ckv_append,
+    ckv_append_select,
     ckv_cluster_incremental,
     ckv_cluster_prefill,
     ckv_last_error,

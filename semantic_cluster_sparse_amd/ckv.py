@@ -81,6 +81,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_cluster_incremental.argtypes = [LP, c_void_p, c_size_t, c_void_p]
     lib.ckv_select.restype = c_int
     lib.ckv_select.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ckv_append_select.restype = c_int
+    lib.ckv_append_select.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]
     lib.ckv_sparse_decode.restype = c_int
     lib.ckv_sparse_decode.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
@@ -139,6 +142,12 @@ def ckv_select(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_cou
     _check("ckv_select",
            load_library().ckv_select(_ref(layer), q, budget, sel_pos, sel_count, ws, ws_bytes, stream))
 
+
+def ckv_append_select(layer: CkvLayerStruct, k_new: int, v_new: int, q: int, budget: int, sel_pos: int,
+                      sel_count: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_append_select",
+           load_library().ckv_append_select(_ref(layer), k_new, v_new, q, budget, sel_pos, sel_count, ws,
+                                            ws_bytes, stream))
 
 def ckv_sparse_decode(layer: CkvLayerStruct, q: int, sel_pos: int, sel_count: int, budget: int,
                       out: int, ws: int, ws_bytes: int, stream: int = 0) -> None:

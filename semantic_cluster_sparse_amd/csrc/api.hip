@@ -247,8 +247,12 @@ int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* strea
   return CKV_OK;
 }
 
-int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
-               void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int select_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
+                void* ws, size_t ws_bytes, void* stream, const uint16_t* k_new, const uint16_t* v_new) {
   int rc = check_layer(L);
   if (rc) return rc;
   if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
@@ -258,6 +262,11 @@ int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* s
   rc = check_ptrs("q,cmean,offsets,k_clu,sel_count", 5, q, L->cmean, L->offsets, L->k_clu, sel_count);
   if (rc) return rc;
   if (budget > 0 && !aligned16(sel_pos)) return fail(CKV_EINVAL, "sel_pos is NULL or not 16-byte aligned");
+  if (k_new != nullptr) {
+    rc = check_ptrs("k_tok,v_tok,k_new,v_new", 4, L->k_tok, L->v_tok, k_new, v_new);
+    if (rc) return rc;
+    if (L->n_total >= L->capacity) return fail(CKV_ENOSPACE, "cache full (capacity %d)", L->capacity);
+  }
   rc = check_ws(L, ws, ws_bytes);
   if (rc) return rc;
   const Layout w = layout_of(L);
@@ -265,8 +274,28 @@ int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* s
   hipError_t e = ckv::launch_select(q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_clu,
                                     L->capacity - L->n_sink, budget, sel_pos, sel_count,
                                     (float*)((char*)ws + w.off_scores), (uint32_t*)((char*)ws + w.off_cut),
-                                    (uint32_t*)ws + units, units, (hipStream_t)stream);
+                                    (uint32_t*)ws + units, k_new, v_new, L->k_tok, L->v_tok, L->capacity,
+                                    L->n_total, units, (hipStream_t)stream);
   return hip_status(e, "select");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
+               void* ws, size_t ws_bytes, void* stream) {
+  return select_impl(L, q, budget, sel_pos, sel_count, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+int ckv_append_select(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t budget, int32_t* sel_pos, int32_t* sel_count, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return fail(CKV_EINVAL, "k_new / v_new is NULL");
+  const int rc = select_impl(L, q, budget, sel_pos, sel_count, ws, ws_bytes, stream, k_new, v_new);
+  if (rc) return rc;
+  L->n_total += 1;
+  return CKV_OK;
 }
 
 int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, const int32_t* sel_count,

@@ -48,11 +48,14 @@ hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
 
 // Recall: cluster scores (several workgroups per unit), then the last of them
 // finds the cut, the partial top-k and writes the positions.  counters[units]
-// must be zero on entry and are zero again on exit.
+// must be zero on entry and are zero again on exit.  With k_new non-null the
+// same launch also writes k_new / v_new into row `row` of k_tok / v_tok.
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
                          const int32_t* offsets, int K, const uint16_t* k_clu, int clu_stride,
                          int budget, int32_t* sel_pos, int32_t* sel_count, float* scores_ws,
-                         uint32_t* cut_ws, uint32_t* counters, int units, hipStream_t s);
+                         uint32_t* cut_ws, uint32_t* counters, const uint16_t* k_new,
+                         const uint16_t* v_new, uint16_t* k_tok, uint16_t* v_tok, int capacity, int row,
+                         int units, hipStream_t s);
 
 // Split-K sparse decode streaming rows through per-wave LDS rings; the last
 // chunk of each unit merges the chunk partials.  counters[units] must be zero

@@ -385,7 +385,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint16_t* __restrict__ q, int G, const float* __restrict__ cmean,
     const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ k_clu, int clu_stride,
     int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count, float* __restrict__ scores_ws,
-    uint32_t* __restrict__ cut_ws, uint32_t* __restrict__ counters) {
+    uint32_t* __restrict__ cut_ws, uint32_t* __restrict__ counters, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_tok, uint16_t* __restrict__ v_tok, int capacity,
+    int row) {
   __shared__ __attribute__((aligned(16))) uint32_t key[kMaxClusters];
   __shared__ __attribute__((aligned(16))) float csc[kMaxClusters];
   __shared__ __attribute__((aligned(16))) int sz[kMaxClusters];
@@ -407,6 +409,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int32_t* off = offsets + (size_t)u * (K + 1);
   const int m = off[K];
   const int beff = budget < m ? budget : m;
+
+  // fused append of the decoded token's K and V rows (row `row` of the
+  // token-order cache, which recall never reads)
+  if (k_new != nullptr && part == 0 && tid < 32) {
+    const int c8 = (tid & 15) * 8;
+    const uint16_t* src = (tid < 16 ? k_new : v_new) + (size_t)u * kHeadDim + c8;
+    uint16_t* dst = (tid < 16 ? k_tok : v_tok) + ((size_t)u * capacity + row) * kHeadDim + c8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
 
   float qb[8];
   qbar8(q, u, G, li, qb);
@@ -630,10 +641,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean, const int32_t* offsets,
                          int K, const uint16_t* k_clu, int clu_stride, int budget, int32_t* sel_pos,
                          int32_t* sel_count, float* scores_ws, uint32_t* cut_ws, uint32_t* counters,
-                         int units, hipStream_t s) {
+                         const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok, uint16_t* v_tok,
+                         int capacity, int row, int units, hipStream_t s) {
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * kSelSplit)), dim3(kSelThreads), 0, s, q, group,
                      cmean, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, scores_ws, cut_ws,
-                     counters);
+                     counters, k_new, v_new, k_tok, v_tok, capacity, row);
   return hipGetLastError();
 }
 

@@ -100,6 +100,16 @@ class Layer:
         ckv.ckv_select(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
                        self.ws.data_ptr(), self.ws_bytes, _stream())
 
+    def append_select(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, budget: int,
+                      sel_pos: torch.Tensor, sel_count: torch.Tensor) -> None:
+        assert k_new.shape == (self.units, HEAD_DIM) and v_new.shape == (self.units, HEAD_DIM)
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * budget and sel_count.numel() >= self.units
+        ckv.ckv_append_select(self.struct, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), budget,
+                              sel_pos.data_ptr(), sel_count.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                              _stream())
+
     def sparse_decode(self, q: torch.Tensor, sel_pos: torch.Tensor, sel_count: torch.Tensor,
                       budget: int, out: torch.Tensor) -> None:
         assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32

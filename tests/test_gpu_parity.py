@@ -356,6 +356,37 @@ def test_incremental_noop():
         assert torch.equal(a, b)
 
 
+def test_append_select_matches_separate_calls():
+    say("case: fused append + select against ckv_append then ckv_select (llama layer, 8 units)")
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    cap = cfg.n_tokens + 4
+    k, v, cen = synth.make_layer_inputs(cfg, capacity=cap)
+    init = synth.make_init_indices(cfg.init_seed, cfg.units, cfg.m, cfg.n_clusters)
+    q = dev_bf16(synth.make_queries(cfg.query_seed, cen, cfg.group))
+    L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.budget)
+    L.prefill(cfg.n_tokens, 2, to_dev(init, torch.int32))
+    kn, vn, _ = synth.make_new_tokens(cfg.data_seed, cen, 1, 0, 0.0)
+    kd, vd = dev_bf16(kn[:, 0]), dev_bf16(vn[:, 0])
+    outs = []
+    for fused in (False, True):
+        L.set_counters(cfg.n_tokens, cfg.n_tokens)
+        L.k_tok[:, cfg.n_tokens].zero_()
+        L.v_tok[:, cfg.n_tokens].zero_()
+        sel_pos = torch.full((cfg.units, cfg.budget), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((cfg.units,), dtype=torch.int32, device="cuda")
+        if fused:
+            L.append_select(kd, vd, q, cfg.budget, sel_pos, cnt)
+        else:
+            L.append(kd, vd)
+            L.select(q, cfg.budget, sel_pos, cnt)
+        torch.cuda.synchronize()
+        assert L.n_total == cfg.n_tokens + 1
+        outs.append((sel_pos.clone(), cnt.clone(), L.k_tok[:, cfg.n_tokens].clone(), L.v_tok[:, cfg.n_tokens].clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert torch.equal(outs[1][2], kd) and torch.equal(outs[1][3], vd)
+
+
 # ------------------------------------------------------------------ edge cases
 
 
