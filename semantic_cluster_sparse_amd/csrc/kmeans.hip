@@ -181,12 +181,14 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Assignment with every direction resident in LDS (K <= 512): one workgroup of
-// 8 waves per CU walks a range of 64-key tiles of one unit; each wave keeps
+// 8 waves per CU walks a range of 48-key tiles of one unit; each wave keeps
 // the MFMA A-operands of its current tile in registers and loads the next
 // tile's while the MFMAs of the current one run.  The directions are loaded
 // into LDS once per workgroup instead of once per 256 keys.
 // ---------------------------------------------------------------------------
 constexpr int kAsResWaves = 8;
+constexpr int kAsResMt = 3;                  // 16-key M-tiles per wave tile (register budget)
+constexpr int kAsResTile = 16 * kAsResMt;     // keys per wave tile
 constexpr int kAsResMaxK = 512;
 
 __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int kg = lane >> 4;
-  const int ntiles = (count + 63) >> 6;
+  const int ntiles = (count + kAsResTile - 1) / kAsResTile;
   const int t0 = part * tiles_per_wg;
   const int t1 = min(ntiles, t0 + tiles_per_wg);
   if (t0 >= t1) return;  // uniform over the workgroup
@@ -218,42 +220,44 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
 
   const uint16_t* kbase = k_tok + ((size_t)u * capacity + row0) * kHeadDim;
   int32_t* out = assign + (size_t)u * clu_stride + first;
-  auto load_tile = [&](bf16x8 (&a)[kAsMt][4], int t) {
+  auto load_tile = [&](bf16x8 (&a)[kAsResMt][4], int t) {
 #pragma unroll
-    for (int mt = 0; mt < kAsMt; ++mt) {
-      int r = t * 64 + mt * 16 + r16;
+    for (int mt = 0; mt < kAsResMt; ++mt) {
+      int r = t * kAsResTile + mt * 16 + r16;
       r = r < count ? r : count - 1;
       const uint16_t* src = kbase + (size_t)r * kHeadDim + kg * 8;
 #pragma unroll
       for (int s = 0; s < 4; ++s) a[mt][s] = *reinterpret_cast<const bf16x8*>(src + s * 32);
     }
   };
-  auto compute_tile = [&](const bf16x8 (&a)[kAsMt][4], int t) {
-    float best[kAsMt][4];
-    int bidx[kAsMt][4];
+  auto compute_tile = [&](const bf16x8 (&a)[kAsResMt][4], int t) {
+    float best[kAsResMt][4];
+    int bidx[kAsResMt][4];
 #pragma unroll
-    for (int mt = 0; mt < kAsMt; ++mt)
+    for (int mt = 0; mt < kAsResMt; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         best[mt][i] = -INFINITY;
         bidx[mt][i] = 0;
       }
-    auto mfma_tile = [&](int ct, f32x4* o) {
-      bf16x8 b[4];
+    // B operands (16 directions x 128 dims) of column block ct
+    auto load_b = [&](bf16x8 (&b)[4], int ct) {
       const uint16_t* bp = csr + (ct * 16 + r16) * kAsLds + kg * 8;
 #pragma unroll
       for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const bf16x8*>(bp + s * 32);
+    };
+    auto mfma_tile = [&](const bf16x8 (&b)[4], f32x4* o) {
 #pragma unroll
-      for (int mt = 0; mt < kAsMt; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < kAsResMt; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int mt = 0; mt < kAsMt; ++mt)
+        for (int mt = 0; mt < kAsResMt; ++mt)
           o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], o[mt], 0, 0, 0);
     };
     auto argmax_tile = [&](const f32x4* in, int j) {
 #pragma unroll
-      for (int mt = 0; mt < kAsMt; ++mt)
+      for (int mt = 0; mt < kAsResMt; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = in[mt][i];
@@ -262,48 +266,65 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
           bidx[mt][i] = gt ? j : bidx[mt][i];
         }
     };
-    const int nfull = K >> 4;
-    f32x4 acc[kAsMt], nxt[kAsMt];
-    if (nfull > 0) {
-      mfma_tile(0, acc);
-      for (int ct = 1; ct < nfull; ++ct) {
-        mfma_tile(ct, nxt);
-        argmax_tile(acc, (ct - 1) * 16 + r16);
-#pragma unroll
-        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = nxt[mt];
-      }
-      argmax_tile(acc, (nfull - 1) * 16 + r16);
+    // Two accumulator sets alternate (no copies, which would wait for the
+    // MFMAs); two B buffers alternate with blocks of the same parity, each
+    // refilled right after its MFMAs issue, so an LDS read has a whole block of
+    // MFMAs and argmax work to land in.
+    const int nblk = (K + 15) >> 4;  // the last block may be partial (padded rows are zero)
+    f32x4 acc0[kAsResMt], acc1[kAsResMt];
+    bf16x8 b0[4], b1[4];
+    load_b(b0, 0);
+    if (nblk > 1) load_b(b1, 1);
+    mfma_tile(b0, acc0);                        // block 0
+    if (nblk > 2) load_b(b0, 2);
+    int ct = 1;
+    for (; ct + 1 < nblk; ct += 2) {
+      mfma_tile(b1, acc1);                      // block ct (odd)
+      if (ct + 2 < nblk) load_b(b1, ct + 2);
+      argmax_tile(acc0, (ct - 1) * 16 + r16);   // block ct-1
+      mfma_tile(b0, acc0);                      // block ct+1 (even)
+      if (ct + 3 < nblk) load_b(b0, ct + 3);
+      argmax_tile(acc1, ct * 16 + r16);         // block ct
     }
-    if (K & 15) {
-      mfma_tile(nfull, acc);
-      if (nfull * 16 + r16 >= K) {
+    // acc0 holds block ct-1; block ct (odd, in b1), if any, is the last
+    const bool tail = ct < nblk;
+    if (tail) mfma_tile(b1, acc1);
+    auto mask_pad = [&](f32x4* acc, int blk) {  // padded directions of a partial block never win
+      if (blk * 16 + r16 >= K) {
 #pragma unroll
-        for (int mt = 0; mt < kAsMt; ++mt) acc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int mt = 0; mt < kAsResMt; ++mt) acc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
-      argmax_tile(acc, nfull * 16 + r16);
+    };
+    mask_pad(acc0, ct - 1);
+    argmax_tile(acc0, (ct - 1) * 16 + r16);
+    if (tail) {
+      mask_pad(acc1, ct);
+      argmax_tile(acc1, ct * 16 + r16);
     }
+    // row results over the 16 lanes of each row group (DPP, no LDS round
+    // trips); ties go to the smaller index
 #pragma unroll
-    for (int mt = 0; mt < kAsMt; ++mt)
+    for (int mt = 0; mt < kAsResMt; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float bv = best[mt][i];
         int bi = bidx[mt][i];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (ov > bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
-        const int r = t * 64 + mt * 16 + kg * 4 + i;
+        auto step = [&](float ov, int oi) {
+          const bool take = ov > bv || (ov == bv && oi < bi);
+          bv = take ? ov : bv;
+          bi = take ? oi : bi;
+        };
+        step(dpp_f32<kDppXor1>(bv), dpp_row_i32<kDppXor1>(bi));
+        step(dpp_f32<kDppXor2>(bv), dpp_row_i32<kDppXor2>(bi));
+        step(dpp_f32<kDppHalfMirror>(bv), dpp_row_i32<kDppHalfMirror>(bi));
+        step(dpp_f32<kDppMirror>(bv), dpp_row_i32<kDppMirror>(bi));
+        const int r = t * kAsResTile + mt * 16 + kg * 4 + i;
         if (r16 == i && r < count) out[r] = bi;
       }
   };
 
   // tiles of this wave: t0 + wave, t0 + wave + 8, ...; two register sets alternate
-  bf16x8 a0[kAsMt][4], a1[kAsMt][4];
+  bf16x8 a0[kAsResMt][4], a1[kAsResMt][4];
   int t = t0 + wave;
   if (t < t1) load_tile(a0, t);
   for (; t < t1; t += 2 * kAsResWaves) {
@@ -608,8 +629,8 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
                          int first, int units, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   if (K <= kAsResMaxK) {
-    // about one 8-wave workgroup per CU, each on one unit's range of 64-key tiles
-    const int ntiles = (count + 63) / 64;
+    // about one 8-wave workgroup per CU, each on one unit's range of key tiles
+    const int ntiles = (count + kAsResTile - 1) / kAsResTile;
     int wpu = (256 + units - 1) / units;
     const int max_wpu = (ntiles + kAsResWaves - 1) / kAsResWaves;
     if (wpu > max_wpu) wpu = max_wpu;
