@@ -1,16 +1,30 @@
 """Benchmark: ClusterKV sparse decode on one MI355X.
 
-Workload (``llama8b-stack-32k-b8``): 32 Llama-3.1-8B-shaped layers, batch 8,
-8 KV heads x 4 query heads, head_dim 128, 32768-token context per sequence
-(16 sinks + 32752 clustered keys, 400 clusters per KV head, 10 Lloyd
+Default workload (``llama8b-stack-32k-b8``): 32 Llama-3.1-8B-shaped layers,
+batch 8, 8 KV heads x 4 query heads, head_dim 128, 32768-token context per
+sequence (16 sinks + 32752 clustered keys, 400 clusters per KV head, 10 Lloyd
 rounds), recall budget 2048.  One *step* is one decode token for the whole
-batch through all 32 layers: per layer ckv_append_select (the new token's
-K/V row written and the recall, one launch) + ckv_sparse_decode.  Prefill clustering is timed separately (K-means keys/s).
+batch through all layers: per layer ckv_append_select (the new token's K/V
+row written and the recall, one launch) + ckv_sparse_decode.  Prefill
+clustering is timed separately (K-means keys/s).
+
+``--workload glm4-stack-32k-b16``: 40 GLM4-9B-shaped layers (2 KV heads x 16
+query heads), batch 16, 32468 clustered + 300 recent tokens, 410 clusters,
+budget 2048, 50 steps; a step that finds 320 recent tokens first calls
+ckv_cluster_incremental on every layer, so the timed steps include one
+re-clustering.  Reports steady-state tokens/s with the re-clustering spread
+over its 320 steps.
+
+``--workload llama8b-incremental-b16``: one Llama layer at batch 16 (128
+units), 32768 clustered tokens, then 320 new keys per KV head (10% from 8
+new mixture components): times ckv_cluster_incremental, then a budget-1024
+ckv_select and ckv_sparse_decode on batch-16 queries.  Reports the
+incremental latency.
 
 Inputs are synthetic (seeded Gaussian-mixture keys on the GPU) and resident
-in HBM before the timed region.  Each step is captured once as a HIP graph
-(the per-step host counters differ, so every step has its own graph) and the
-timed region replays them.  Prints one JSON line on stdout.
+in HBM before the timed region.  Decode steps are captured once each as a HIP
+graph (the per-step host counters differ, so every step has its own graph)
+and the timed region replays them.  Prints one JSON line on stdout.
 """
 
 from __future__ import annotations
@@ -122,65 +136,67 @@ def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
     }
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by unit with no exchange, see DESIGN.md)", file=sys.stderr)
-        return 2
+def incremental_bytes(units: int, K: int, m_old: int, m_new: int) -> int:
+    """Algorithmic HBM bytes of one ckv_cluster_incremental call.
 
+    Per unit: the new keys read twice (assignment, norms: 2 x 256 B each) and
+    their labels written; every clustered token's label read twice (histogram,
+    scatter) and its index written (4 + 4 + 4 B); every clustered token's K and
+    V rows gathered and written in cluster order (4 x 256 B); per cluster the
+    bf16 direction read and written, both f64 sums read and written, the f32
+    mean written, the size read and written and the offset written.
+    """
+    d = 128
+    m = m_old + m_new
+    per_cluster = 2 * 2 * d + 2 * 2 * 8 * d + 4 * d + 4 * 2 + 4
+    return units * (m_new * (2 * 2 * d + 4) + m * (4 + 4 + 4 + 4 * 2 * d) + K * per_cluster)
+
+
+def setup(args):
     import torch
 
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
-                          "copies": 5}), flush=True)
-        return 0
-
-    import synth
-    from synth import device as dgen
     from semantic_cluster_sparse_amd import ckv
-    from semantic_cluster_sparse_amd.layer import Layer
 
     ckv.load_library()
-    cfg = synth.CONFIGS["llama8b-stack-32k-b8"]
-    n_layers = args.layers or cfg.layers
-    W, K = args.warmup, args.steps
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cap = cfg.n_tokens + W + K + 1
+    return dev
+
+
+def run_stack(cfg, args) -> dict:
+    """Decode steps through a layer stack (append_select + sparse_decode per layer),
+    with ckv_cluster_incremental on every layer whenever 320 recent tokens have built up."""
+    import torch
+
+    from synth import device as dgen
+    from semantic_cluster_sparse_amd.layer import Layer
+
+    dev = setup(args)
+    n_layers = args.layers or cfg.layers
+    W = args.warmup
+    K = args.steps if args.steps is not None else cfg.steps
+    n_fill = cfg.n_tokens + cfg.n_recent
+    cap = n_fill + W + K + 1
     units, G, budget = cfg.units, cfg.group, cfg.budget
+    recluster = cfg.new_tokens if cfg.new_tokens > 0 else 0
+    so = seed_offset(cfg)
     stream = torch.cuda.current_stream()
 
-    log(f"[bench] allocating {n_layers} layers of {units} units, capacity {cap}")
+    log(f"[bench] {cfg.name}: allocating {n_layers} layers of {units} units, capacity {cap}")
     layers = []
     qs = []
     for li in range(n_layers):
         L = Layer(batch=cfg.batch, n_kv_heads=cfg.n_kv_heads, group=G, n_clusters=cfg.n_clusters,
-                  capacity=cap, max_budget=budget, incremental=False, device=dev)
-        cen = dgen.fill_mixture(L.k_tok, L.v_tok, cfg.n_tokens, cfg.components, seed=10_000 + li)
-        qs.append([dgen.queries(cen, G, seed=20_000 + 100 * li + s) for s in range(W + K)])
+                  capacity=cap, max_budget=budget, incremental=recluster > 0, device=dev)
+        cen = dgen.fill_mixture(L.k_tok, L.v_tok, n_fill, cfg.components, seed=10_000 + so + li)
+        qs.append([dgen.queries(cen, G, seed=20_000 + so + 100 * li + s) for s in range(W + K)])
         del cen
         layers.append(L)
     torch.cuda.synchronize()
     log(f"[bench] generated inputs; {torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
     # ---------------------------------------------------------------- prefill (timed separately)
-    inits = [dgen.init_indices(units, cfg.m, cfg.n_clusters, seed=30_000 + li, device=dev)
+    inits = [dgen.init_indices(units, cfg.m, cfg.n_clusters, seed=30_000 + so + li, device=dev)
              for li in range(n_layers)]
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -196,6 +212,9 @@ def main() -> int:
     log(f"[bench] prefill {prefill_s * 1e3:.1f} ms wall, {prefill_ev_s * 1e3:.1f} ms events; "
         f"{keys / prefill_ev_s / 1e6:.1f} M keys/s")
     del inits
+    # the recent tokens past the clustered prefix are already in the token-order rows
+    for L in layers:
+        L.set_counters(n_fill, cfg.n_tokens)
 
     # ---------------------------------------------------------------- decode step buffers
     sel_pos = [torch.zeros((units, budget), dtype=torch.int32, device=dev) for _ in range(n_layers)]
@@ -203,13 +222,19 @@ def main() -> int:
     outs = [torch.zeros((units, G, 128), dtype=torch.float32, device=dev) for _ in range(n_layers)]
     k_new = [dgen.rows(units, 128, 40_000 + s, dev) for s in range(W + K)]
     v_new = [dgen.rows(units, 128, 50_000 + s, dev) for s in range(W + K)]
+    incr_steps = []
 
     def step(s: int) -> None:
+        if recluster and layers[0].n_total - layers[0].n_clustered >= recluster:
+            incr_steps.append(s)
+            for L in layers:
+                L.incremental()
         for li, L in enumerate(layers):
             L.append_select(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li])
             L.sparse_decode(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
 
     graphs = []
+    cs = None
     if not args.no_graph:
         log("[bench] capturing one HIP graph per step")
         cs = torch.cuda.Stream()
@@ -230,9 +255,15 @@ def main() -> int:
         run(s)
     torch.cuda.synchronize()
     log("[bench] warmup done; timing")
+    per_step = bool(recluster)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)] if per_step else []
     t0 = time.perf_counter()
-    for s in range(W, W + K):
+    if per_step:
+        evs[0].record(stream)
+    for i, s in enumerate(range(W, W + K)):
         run(s)
+        if per_step:
+            evs[i + 1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / K * 1e3
@@ -269,10 +300,13 @@ def main() -> int:
     r_now = layers[0].n_total - layers[0].n_clustered
     dbytes = decode_bytes(units, 16, budget, r_now, G)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
-    step_bytes = n_layers * (decode_bytes(units, 16, budget, (W + K) // 2, G)
+    r_mean = cfg.n_recent + (W + K) // 2
+    if recluster:
+        r_mean = recluster // 2
+    step_bytes = n_layers * (decode_bytes(units, 16, budget, r_mean, G)
                              + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
     log(f"[bench] ckv_sparse_decode {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
-    traffic = measured_traffic()
+    traffic = measured_traffic() if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers else None
 
     result = {
         "metric": METRIC,
@@ -288,9 +322,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": n_layers, "batch": cfg.batch, "kv_heads": cfg.n_kv_heads,
-                   "group": G, "context": cfg.n_tokens, "clusters": cfg.n_clusters, "budget": budget,
+                   "group": G, "context": n_fill, "clusters": cfg.n_clusters, "budget": budget,
                    "graphs": not args.no_graph},
-        "roofline": {"bound": "hbm", "kernel": "ckv::sparse_decode_kernel<4>",
+        "roofline": {"bound": "hbm", "kernel": f"ckv::sparse_decode_kernel<{_group_tier(G)}>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},
@@ -298,7 +332,171 @@ def main() -> int:
         "kmeans_keys_per_s": keys / prefill_ev_s,
         "prefill_ms": prefill_ev_s * 1e3,
     }
-    if not args.no_cpu_baseline:
+    if per_step:
+        times = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+        timed_incr = [s - W for s in incr_steps if W <= s < W + K]
+        plain = sorted(t for i, t in enumerate(times) if i not in timed_incr)
+        t_plain = plain[len(plain) // 2] if plain else float("nan")
+        t_incr = [times[i] - t_plain for i in timed_incr]
+        result["recluster"] = {
+            "every_tokens": recluster,
+            "steps_with_recluster": timed_incr,
+            "step_ms_median": t_plain,
+            "recluster_ms": t_incr,
+            "steady_tokens_per_s": (cfg.batch / ((t_plain + (sum(t_incr) / len(t_incr)) / recluster) * 1e-3)
+                                    if t_incr else None),
+        }
+        log(f"[bench] median step {t_plain:.3f} ms; re-clustering steps {timed_incr} cost "
+            f"{', '.join(f'{t:.3f}' for t in t_incr)} ms extra")
+    return result
+
+
+def run_incremental(cfg, args) -> dict:
+    """One layer: prefill, append cfg.new_tokens keys per unit, then time
+    ckv_cluster_incremental, ckv_select and ckv_sparse_decode (median over repetitions)."""
+    import torch
+
+    from synth import device as dgen
+    from semantic_cluster_sparse_amd.layer import Layer
+
+    dev = setup(args)
+    W = args.warmup
+    reps = args.steps if args.steps is not None else 10
+    n0, n_new = cfg.n_tokens, cfg.new_tokens
+    units, G, budget = cfg.units, cfg.group, cfg.budget
+    cap = n0 + n_new
+    so = seed_offset(cfg)
+    stream = torch.cuda.current_stream()
+    L = Layer(batch=cfg.batch, n_kv_heads=cfg.n_kv_heads, group=G, n_clusters=cfg.n_clusters,
+              capacity=cap, max_budget=budget, incremental=True, device=dev)
+    cen = dgen.fill_mixture(L.k_tok, L.v_tok, n0, cfg.components, seed=10_000 + so)
+    k_add, v_add = dgen.new_rows(cen, n_new, cfg.new_components, cfg.new_fraction,
+                                 seed=60_000 + so)
+    q = dgen.queries(cen, G, seed=20_000 + so)
+    init = dgen.init_indices(units, cfg.m, cfg.n_clusters, seed=30_000 + so, device=dev)
+    del cen
+    sel_pos = torch.zeros((units, budget), dtype=torch.int32, device=dev)
+    cnt = torch.zeros((units,), dtype=torch.int32, device=dev)
+    out = torch.zeros((units, G, 128), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: {units} units, {n0} clustered + {n_new} new tokens; "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    t_inc, t_sel, t_dec, t_sel0 = [], [], [], []
+    for r in range(W + reps):
+        L.prefill(n0, cfg.iters, init)
+        L.k_tok[:, n0:cap].copy_(k_add)
+        L.v_tok[:, n0:cap].copy_(v_add)
+        L.set_counters(cap, n0)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        L.select(q, budget, sel_pos, cnt)        # recall with the 320 tokens still recent
+        e[1].record(stream)
+        L.incremental()
+        e[2].record(stream)
+        L.select(q, budget, sel_pos, cnt)
+        e[3].record(stream)
+        L.sparse_decode(q, sel_pos, cnt, budget, out)
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        if r >= W:
+            t_sel0.append(e[0].elapsed_time(e[1]))
+            t_inc.append(e[1].elapsed_time(e[2]))
+            t_sel.append(e[2].elapsed_time(e[3]))
+            t_dec.append(e[3].elapsed_time(e[4]))
+
+    def med(x):
+        return sorted(x)[len(x) // 2]
+
+    inc_ms = med(t_inc)
+    ibytes = incremental_bytes(units, cfg.n_clusters, cfg.m, n_new)
+    achieved = ibytes / (inc_ms * 1e-3) / 1e9
+    log(f"[bench] ckv_cluster_incremental {inc_ms * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic; "
+        f"select {med(t_sel) * 1e3:.1f} us; decode {med(t_dec) * 1e3:.1f} us")
+    return {
+        "metric": "incremental clustering latency (320 new keys per KV head), then budget-1024 recall",
+        "value": inc_ms * 1e3,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": W,
+        "ms_per_step": inc_ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": 1, "batch": cfg.batch, "kv_heads": cfg.n_kv_heads,
+                   "group": G, "context": n0, "new_tokens": n_new, "new_components": cfg.new_components,
+                   "new_fraction": cfg.new_fraction, "clusters": cfg.n_clusters, "budget": budget},
+        "roofline": {"bound": "hbm", "kernel": "ckv_cluster_incremental (whole call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launch_us": inc_ms * 1e3, "bytes_per_launch": ibytes},
+        "select_us": med(t_sel) * 1e3,
+        "select_before_incremental_us": med(t_sel0) * 1e3,
+        "sparse_decode_us": med(t_dec) * 1e3,
+    }
+
+
+def seed_offset(cfg) -> int:
+    """Generator seeds of a workload: the default one keeps offset 0, the others get their own range."""
+    return 0 if cfg.name == DEFAULT_WORKLOAD else 100_000 * cfg.seed_base
+
+
+def _group_tier(G: int) -> int:
+    t = 1
+    while t < G:
+        t <<= 1
+    return t
+
+
+DEFAULT_WORKLOAD = "llama8b-stack-32k-b8"
+WORKLOADS = (DEFAULT_WORKLOAD, "glm4-stack-32k-b16", "llama8b-incremental-b16")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for the default workload, the workload's own count otherwise)")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=WORKLOADS, default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by unit with no exchange between GPUs)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "copies": 5}), flush=True)
+        return 0
+
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    if args.workload == DEFAULT_WORKLOAD and args.steps is None:
+        args.steps = 20
+    if cfg.new_tokens and cfg.layers == 1:
+        result = run_incremental(cfg, args)
+    else:
+        result = run_stack(cfg, args)
+    if args.workload == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         result["cpu_baseline"] = run_cpu_baseline(cfg, steps=3, seconds=args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -54,3 +54,27 @@ def init_indices(units: int, m: int, k: int, seed: int, device) -> torch.Tensor:
     g.manual_seed(seed)
     r = torch.rand((units, m), generator=g, device=device)
     return torch.argsort(r, dim=1)[:, :k].to(torch.int32).contiguous()
+
+
+def new_rows(centres: torch.Tensor, count: int, new_components: int, fraction: float, seed: int,
+             radius: float = 8.0, sigma: float = 1.0):
+    """Keys and values of `count` decoded tokens per unit: round(count * fraction)
+    of them near `new_components` fresh centres, the rest near the unit's own
+    centres, positions shuffled.  Returns (k, v), each [U, count, d] bf16."""
+    U, C, d = centres.shape
+    dev = centres.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    n_new = int(round(count * fraction))
+    z_old = torch.randint(0, C, (U, count - n_new), generator=g, device=dev)
+    mu = torch.gather(centres, 1, z_old[..., None].expand(-1, -1, d))
+    if n_new > 0 and new_components > 0:
+        newc = torch.randn((U, new_components, d), generator=g, device=dev)
+        newc = radius * newc / newc.norm(dim=2, keepdim=True)
+        z_new = torch.randint(0, new_components, (U, n_new), generator=g, device=dev)
+        mu = torch.cat([mu, torch.gather(newc, 1, z_new[..., None].expand(-1, -1, d))], dim=1)
+    order = torch.argsort(torch.rand((U, count), generator=g, device=dev), dim=1)
+    mu = torch.gather(mu, 1, order[..., None].expand(-1, -1, d))
+    k = (mu + sigma * torch.randn(mu.shape, generator=g, device=dev)).to(torch.bfloat16).contiguous()
+    v = torch.randn(mu.shape, generator=g, device=dev).to(torch.bfloat16).contiguous()
+    return k, v
