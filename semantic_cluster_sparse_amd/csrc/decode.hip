@@ -346,22 +346,38 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     }
   }
   __syncthreads();
+  // Each thread owns kPer head-dim entries of one head, kTph apart (kTph
+  // threads per head), so a head's (max, sum) is read once per thread, every
+  // load instruction covers contiguous floats, and all of a thread's loads of
+  // a merge step are in flight together.
+  constexpr int kPer = GT * kHeadDim >= kDecThreads ? GT * kHeadDim / kDecThreads : 1;
+  constexpr int kTph = kHeadDim / kPer;
+  static_assert(kHeadDim % kPer == 0, "a thread's entries stay inside one head");
+  const int th = tid / kTph;  // head of this thread
+  const int td = tid % kTph;  // its entries are td + kTph * i
+  const bool tact = th < G;
+  // this workgroup's (max, sum, unnormalised output) of head th over its 8 waves
+  float wM = -INFINITY, wL = 0.f, wO[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) wO[i] = 0.f;
+  if (tact) {
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) wM = fmaxf(wM, red[(w * GT + th) * kPartialStride + kHeadDim]);
+    const float Ms = (wM == -INFINITY) ? 0.f : wM;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float* rw = red + (w * GT + th) * kPartialStride;
+      const float a = exp2f(rw[kHeadDim] - Ms);
+      wL += rw[kHeadDim + 1] * a;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) wO[i] += rw[td + kTph * i] * a;
+    }
+  }
   if (n_chunks == 1) {  // the whole unit in one workgroup: normalise directly
-    for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
-      const int h = t / kHeadDim, d = t % kHeadDim;
-      float M = -INFINITY;
+    if (tact) {
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GT + h) * kPartialStride + kHeadDim]);
-      const float Ms = (M == -INFINITY) ? 0.f : M;
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float* rw = red + (w * GT + h) * kPartialStride;
-        const float a = exp2f(rw[kHeadDim] - Ms);
-        L += rw[kHeadDim + 1] * a;
-        O += rw[d] * a;
-      }
-      out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+      for (int i = 0; i < kPer; ++i)
+        out[((size_t)u * G + th) * kHeadDim + td + kTph * i] = wL > 0.f ? wO[i] / wL : 0.f;
     }
     return;
   }
@@ -370,26 +386,14 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   // per-XCD L2), so the workgroup that merges may run on any XCD; the wait
   // before the counter increment makes this chunk's stores complete first.
   const size_t cs = (size_t)GT * kPartialStride;
-  float* outp = partials + ((size_t)u * n_chunks + c) * cs;
-  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
-    const int h = t / kHeadDim, d = t % kHeadDim;
-    float M = -INFINITY;
+  if (tact) {
+    float* outp = partials + ((size_t)u * n_chunks + c) * cs + th * kPartialStride;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GT + h) * kPartialStride + kHeadDim]);
-    const float Ms = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float* rw = red + (w * GT + h) * kPartialStride;
-      const float a = exp2f(rw[kHeadDim] - Ms);
-      L += rw[kHeadDim + 1] * a;
-      O += rw[d] * a;
-    }
-    __hip_atomic_store(&outp[h * kPartialStride + d], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == 0) {
-      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&outp[h * kPartialStride + kHeadDim + 1], L, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kPer; ++i)
+      __hip_atomic_store(&outp[td + kTph * i], wO[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (td == 0) {
+      __hip_atomic_store(&outp[kHeadDim], wM, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&outp[kHeadDim + 1], wL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -401,21 +405,23 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   }
   __syncthreads();
   if (!sh_last) return;
-  // last chunk of the unit to arrive: log-sum-exp merge over all chunks, every load independent
-  const float* p = partials + (size_t)u * n_chunks * cs;
-  for (int t = tid; t < G * kHeadDim; t += kDecThreads) {
-    const int h = t / kHeadDim, d = t % kHeadDim;
-    const float* ph = p + h * kPartialStride;
-    float M = -INFINITY, L = 0.f, O = 0.f;
+  // last chunk of the unit to arrive: log-sum-exp merge over all chunks
+  if (tact) {
+    const float* ph = partials + (size_t)u * n_chunks * cs + th * kPartialStride;
+    float M = -INFINITY, L = 0.f, O[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) O[i] = 0.f;
     for (int c0 = 0; c0 < n_chunks; c0 += 8) {
       // all loads of 8 chunks in flight together (indices clamped, extras ignored)
-      float mc[8], lc[8], oc[8];
+      float mc[8], lc[8], oc[8][kPer];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float* pc = ph + min(c0 + k, n_chunks - 1) * cs;
         mc[k] = __hip_atomic_load(pc + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lc[k] = __hip_atomic_load(pc + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        oc[k] = __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          oc[k][i] = __hip_atomic_load(pc + td + kTph * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -424,12 +430,15 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
           const float Ms = (Mn == -INFINITY) ? 0.f : Mn;
           const float a0 = exp2f(M - Ms), a1 = exp2f(mc[k] - Ms);
           L = L * a0 + lc[k] * a1;
-          O = O * a0 + oc[k] * a1;
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) O[i] = O[i] * a0 + oc[k][i] * a1;
           M = Mn;
         }
       }
     }
-    out[((size_t)u * G + h) * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      out[((size_t)u * G + th) * kHeadDim + td + kTph * i] = L > 0.f ? O[i] / L : 0.f;
   }
   if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -146,14 +146,22 @@ __device__ __forceinline__ void wave_radix_select(const uint32_t* keys, const in
 }
 
 __device__ __forceinline__ void qbar8(const uint16_t* q, int u, int G, int li, float* qb) {
+  // every head's load in flight at once, then the sum in head order
+  uint4 w[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    w[h] = h < G ? *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8)
+                 : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int e = 0; e < 8; ++e) qb[e] = 0.f;
-  for (int h = 0; h < G; ++h) {
-    const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)u * G + h) * kHeadDim + li * 8);
-    qb[0] += bf16_lo(w.x); qb[1] += bf16_hi(w.x);
-    qb[2] += bf16_lo(w.y); qb[3] += bf16_hi(w.y);
-    qb[4] += bf16_lo(w.z); qb[5] += bf16_hi(w.z);
-    qb[6] += bf16_lo(w.w); qb[7] += bf16_hi(w.w);
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      qb[0] += bf16_lo(w[h].x); qb[1] += bf16_hi(w[h].x);
+      qb[2] += bf16_lo(w[h].y); qb[3] += bf16_hi(w[h].y);
+      qb[4] += bf16_lo(w[h].z); qb[5] += bf16_hi(w[h].z);
+      qb[6] += bf16_lo(w[h].w); qb[7] += bf16_hi(w[h].w);
+    }
   }
 }
 
@@ -419,9 +427,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
 
-  float qb[8];
-  qbar8(q, u, G, li, qb);
-
   // ---- phase 1: this workgroup's share of the cluster scores (16 lanes per
   // centroid row, every row of the share in flight at once), stored
   // device-scope; the last workgroup of the unit to finish goes on
@@ -430,6 +435,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int j_lo = part * K / kSelSplit, j_hi = (part + 1) * K / kSelSplit;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
   float* sc_u = scores_ws + (size_t)u * K;
+  float qb[8];
   {
     float4 a[kRowsInFlight][2];
 #pragma unroll
@@ -442,6 +448,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         a[t][0] = a[t][1] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+    // the query sum while the centroid rows are in flight
+    qbar8(q, u, G, li, qb);
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j_lo + grp + t * kSelGroups;

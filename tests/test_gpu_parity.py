@@ -236,6 +236,8 @@ def test_select_teacher_forced():
     (4, 16, 37, 2048, 48),
     (1, 16, 5, 256, 24),
     (16, 16, 300, 2048, 41),
+    (8, 16, 20, 1024, 40),
+    (13, 16, 1, 16, 40),      # G not a power of two, the 16-head tier; one chunk per unit
     (2, 0, 3, 64, 30),
     (4, 16, 11, 0, 20),
     (3, 16, 0, 500, 33),
