@@ -21,6 +21,10 @@ new mixture components): times ckv_cluster_incremental, then a budget-1024
 ckv_select and ckv_sparse_decode on batch-16 queries.  Reports the
 incremental latency.
 
+The stack workloads also time a dense-decode baseline on the same harness
+(``full_attention``): budget >= m, so recall takes every cluster and the
+decode kernel attends to all cached tokens.
+
 Inputs are synthetic (seeded Gaussian-mixture keys on the GPU) and resident
 in HBM before the timed region.  Decode steps are captured once each as a HIP
 graph (the per-step host counters differ, so every step has its own graph)
@@ -69,8 +73,8 @@ def select_bytes(units: int, K: int, c: int, group: int, cut_rows: int) -> int:
 # WRITE_SIZE x 1.0).  Valid only for the kernel sources they were taken on:
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC_SOURCES = ("decode.hip", "common.hpp")
-TRAFFIC = {"sha256": "a727886e46567c8861703cf6bdc99d72e76965532d8f6a1b6363abe82ffb8081",
-           "fetch_kib": 34308.39, "write_kib": 762.0}
+TRAFFIC = {"sha256": "c66a9a98abb0b8b9bb65c53e57049c431aa4733bd39aed3df5ab108438d9b830",
+           "fetch_kib": 34292.92, "write_kib": 762.0}
 
 
 def kernel_source_hash() -> str:
@@ -161,6 +165,48 @@ def setup(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     return dev
+
+
+def full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs, stream, dev) -> dict:
+    """Dense decode on the same harness: with budget >= m, ckv_select takes every
+    cluster whole, so ckv_sparse_decode attends to every cached token.  Timed like
+    the sparse decode (one graph over all layers, events around its replays)."""
+    import torch
+
+    n_layers = len(layers)
+    m_now = layers[0].n_clustered - 16
+    sp_full = [torch.empty((units, m_now), dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    cnt_full = [torch.empty((units,), dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    for li, L in enumerate(layers):
+        L.select(qs[li][qlast], m_now, sp_full[li], cnt_full[li])
+
+    def decode_full() -> None:
+        for li, L in enumerate(layers):
+            L.sparse_decode(qs[li][qlast], sp_full[li], cnt_full[li], m_now, outs[li])
+
+    if cs is not None:
+        fg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fg, stream=cs):
+            decode_full()
+        launch_full = fg.replay
+    else:
+        launch_full = decode_full
+    launch_full()
+    torch.cuda.synchronize()
+    reps = 3
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        launch_full()
+    b.record(stream)
+    torch.cuda.synchronize()
+    full_ms = a.elapsed_time(b) / (reps * n_layers)
+    fbytes = decode_bytes(units, 16, m_now, r_now, G)
+    gbs = fbytes / (full_ms * 1e-3) / 1e9
+    log(f"[bench] full-attention decode {full_ms * 1e3:.1f} us/launch ({gbs:.0f} GB/s); "
+        f"sparse decode is {full_ms / dec_ms:.1f}x faster per launch")
+    return {"decode_us": full_ms * 1e3, "bytes_per_launch": fbytes, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "decode_speedup": full_ms / dec_ms}
 
 
 def run_stack(cfg, args) -> dict:
@@ -306,6 +352,13 @@ def run_stack(cfg, args) -> dict:
     step_bytes = n_layers * (decode_bytes(units, 16, budget, r_mean, G)
                              + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
     log(f"[bench] ckv_sparse_decode {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+
+    # ---------------------------------------------------------------- full-attention baseline
+    full = None
+    if not args.no_full_attention:
+        full = full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs if graphs else None,
+                                       stream, dev)
+        full["step_speedup"] = n_layers * full["decode_us"] * 1e-3 / ms_per_step
     traffic = measured_traffic() if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers else None
 
     result = {
@@ -331,6 +384,7 @@ def run_stack(cfg, args) -> dict:
         "step_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kmeans_keys_per_s": keys / prefill_ev_s,
         "prefill_ms": prefill_ev_s * 1e3,
+        "full_attention": full,
     }
     if per_step:
         times = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
@@ -466,6 +520,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-attention", action="store_true", help="skip the dense-decode baseline")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")
