@@ -181,13 +181,17 @@ __global__ __launch_bounds__(256) void assign_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Assignment with every direction resident in LDS (K <= 512): one workgroup of
-// 8 waves per CU walks a range of 48-key tiles of one unit; each wave keeps
-// the MFMA A-operands of its current tile in registers and loads the next
-// tile's while the MFMAs of the current one run.  The directions are loaded
-// into LDS once per workgroup instead of once per 256 keys.
+// 12 waves per CU (three per SIMD) walks a range of 32-key tiles of one unit;
+// each wave keeps the MFMA A-operands of its current tile in registers and
+// loads the next tile's while the MFMAs of the current one run.  The
+// directions are loaded into LDS once per workgroup instead of once per 256
+// keys.  Two 16-key M-tiles per wave keep the kernel under 170 VGPRs, so a
+// third wave per SIMD fits: the argmax VALU work of one wave then overlaps
+// the MFMAs of two others (measured faster than three M-tiles at two waves
+// per SIMD, whose B operands are reused more but hide less latency).
 // ---------------------------------------------------------------------------
-constexpr int kAsResWaves = 8;
-constexpr int kAsResMt = 3;                  // 16-key M-tiles per wave tile (register budget)
+constexpr int kAsResWaves = 12;
+constexpr int kAsResMt = 2;                  // 16-key M-tiles per wave tile (register budget)
 constexpr int kAsResTile = 16 * kAsResMt;     // keys per wave tile
 constexpr int kAsResMaxK = 512;
 
