@@ -13,7 +13,10 @@ query heads), batch 16, 32468 clustered + 300 recent tokens, 410 clusters,
 budget 2048, 50 steps; a step that finds 320 recent tokens first calls
 ckv_cluster_incremental on every layer, so the timed steps include one
 re-clustering.  Reports steady-state tokens/s with the re-clustering spread
-over its 320 steps.
+over its 320 steps.  With ``--async-recluster`` the re-clustering runs as
+ckv_cluster_incremental_async on a second stream beside the decode steps and
+is committed ``--async-lag`` steps later (the steps in between still see the
+old clusters plus a growing recent window).
 
 ``--workload llama8b-incremental-b16``: one Llama layer at batch 16 (128
 units), 32768 clustered tokens, then 320 new keys per KV head (10% from 8
@@ -268,10 +271,45 @@ def run_stack(cfg, args) -> dict:
     outs = [torch.zeros((units, G, 128), dtype=torch.float32, device=dev) for _ in range(n_layers)]
     k_new = [dgen.rows(units, 128, 40_000 + s, dev) for s in range(W + K)]
     v_new = [dgen.rows(units, 128, 50_000 + s, dev) for s in range(W + K)]
-    incr_steps = []
+    incr_steps = []      # steps that start a re-clustering
+    commit_steps = []    # asynchronous mode: steps before which the last layers are committed
+    lag = args.async_lag if (recluster and args.async_recluster) else 0
+    main = torch.cuda.current_stream()
+    bs = torch.cuda.Stream() if lag else None          # background clustering stream
+    starts = {}          # step -> layers whose clustering starts before it
+    commits = {}         # step -> (layer, start step) committed before it
+    bg_work = {}         # step -> graph of that step's background clustering
+    bg_done = {}         # start step -> event on the background stream
+    busy = [False]
+
+    def recluster_due() -> bool:
+        return bool(recluster) and layers[0].n_total - layers[0].n_clustered >= recluster
+
+    def host_schedule(s: int) -> None:
+        """Asynchronous mode.  When 320 recent tokens have built up, the layers'
+        clusterings start spread over the first half of the next `lag` steps, and
+        each is committed half a window after its start, so the background work
+        is shared out over the steps instead of landing on one."""
+        for li, _ in commits.get(s, []):
+            layers[li].commit()
+        if commits.get(s) and not any(t > s for t in commits):
+            commit_steps.append(s)
+            busy[0] = False
+        if not busy[0] and recluster_due():
+            busy[0] = True
+            incr_steps.append(s)
+            spread = max(1, lag // 2)
+            for li in range(n_layers):
+                st = s + (li * spread) // n_layers
+                starts.setdefault(st, []).append(li)
+                commits.setdefault(st + lag - spread, []).append((li, st))
+
+    def background(s: int) -> None:
+        for li in starts.get(s, []):
+            layers[li].incremental_async()
 
     def step(s: int) -> None:
-        if recluster and layers[0].n_total - layers[0].n_clustered >= recluster:
+        if not lag and recluster_due():
             incr_steps.append(s)
             for L in layers:
                 L.incremental()
@@ -284,7 +322,15 @@ def run_stack(cfg, args) -> dict:
     if not args.no_graph:
         log("[bench] capturing one HIP graph per step")
         cs = torch.cuda.Stream()
+        bcs = torch.cuda.Stream() if lag else None
         for s in range(W + K):
+            if lag:
+                host_schedule(s)
+                if starts.get(s):
+                    bg = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(bg, stream=bcs):
+                        background(s)
+                    bg_work[s] = bg
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cs):
                 step(s)
@@ -292,6 +338,23 @@ def run_stack(cfg, args) -> dict:
         torch.cuda.synchronize()
 
     def run(s: int) -> None:
+        if lag:
+            if not graphs:
+                host_schedule(s)
+            for st in sorted({st for _, st in commits.get(s, [])}):
+                main.wait_event(bg_done[st])
+            if starts.get(s):
+                # the clustering reads the rows appended so far: start after the main stream's work
+                ready = torch.cuda.Event()
+                ready.record(main)
+                bs.wait_event(ready)
+                with torch.cuda.stream(bs):
+                    if graphs:
+                        bg_work[s].replay()
+                    else:
+                        background(s)
+                    bg_done[s] = torch.cuda.Event()
+                    bg_done[s].record(bs)
         if graphs:
             graphs[s].replay()
         else:
@@ -389,19 +452,34 @@ def run_stack(cfg, args) -> dict:
     if per_step:
         times = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
         timed_incr = [s - W for s in incr_steps if W <= s < W + K]
-        plain = sorted(t for i, t in enumerate(times) if i not in timed_incr)
+        timed_commit = [s - W for s in commit_steps if W <= s < W + K]
+        # steps that carry re-clustering work: the step itself (synchronous), or every
+        # step from the start to the commit (asynchronous, the work overlaps them)
+        carry = set(timed_incr)
+        for a0 in timed_incr:
+            ends = [c for c in timed_commit if c > a0]
+            if lag and ends:
+                carry.update(range(a0, ends[0] + 1))
+        window = sorted(carry)
+        plain = sorted(t for i, t in enumerate(times) if i not in carry)
         t_plain = plain[len(plain) // 2] if plain else float("nan")
-        t_incr = [times[i] - t_plain for i in timed_incr]
+        extra = sum(times[i] - t_plain for i in carry)
+        n_done = len(timed_commit) if lag else len(timed_incr)
         result["recluster"] = {
             "every_tokens": recluster,
+            "mode": (f"async: layers start over {max(1, lag // 2)} steps, each committed "
+                     f"{lag - max(1, lag // 2)} steps after its start") if lag else "sync",
             "steps_with_recluster": timed_incr,
+            "commit_steps": timed_commit,
             "step_ms_median": t_plain,
-            "recluster_ms": t_incr,
-            "steady_tokens_per_s": (cfg.batch / ((t_plain + (sum(t_incr) / len(t_incr)) / recluster) * 1e-3)
-                                    if t_incr else None),
+            "step_ms_max": max(times),
+            "window_step_ms": [round(times[i], 3) for i in window],
+            "recluster_ms": extra,
+            "steady_tokens_per_s": (cfg.batch / ((t_plain + extra / n_done / recluster) * 1e-3)
+                                    if n_done else None),
         }
-        log(f"[bench] median step {t_plain:.3f} ms; re-clustering steps {timed_incr} cost "
-            f"{', '.join(f'{t:.3f}' for t in t_incr)} ms extra")
+        log(f"[bench] median step {t_plain:.3f} ms, slowest {max(times):.3f} ms; re-clustering started at "
+            f"{timed_incr}, committed at {timed_commit}: {extra:.3f} ms extra over those steps")
     return result
 
 
@@ -521,6 +599,9 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-attention", action="store_true", help="skip the dense-decode baseline")
+    ap.add_argument("--async-recluster", action="store_true",
+                    help="re-cluster on a second stream beside the decode steps and commit later")
+    ap.add_argument("--async-lag", type=int, default=16, help="steps between starting and committing")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")

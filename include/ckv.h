@@ -68,7 +68,9 @@ typedef struct ckv_layer {
   int32_t capacity;     /* token rows per unit in k_tok / v_tok              */
   int32_t n_total;      /* tokens in the cache; the library advances it     */
   int32_t n_clustered;  /* sinks + clustered tokens; the library advances it */
-  int32_t reserved;     /* set to 0                                          */
+  int32_t n_pending;    /* token count clustered by an uncommitted
+                           ckv_cluster_incremental_async call, else 0; set to 0
+                           initially, the library maintains it              */
   /* token-order cache, bf16 [units, capacity, 128] */
   uint16_t* k_tok;
   uint16_t* v_tok;
@@ -88,6 +90,10 @@ typedef struct ckv_layer {
   int32_t* offsets;     /* [units, K + 1]: cluster j = positions offsets[j] .. offsets[j+1]-1 */
   int32_t* assign;      /* [units, capacity - n_sink]: cluster of token n_sink + i            */
   int32_t* perm;        /* [units, capacity - n_sink]: token id at cluster-order position p   */
+  /* second copies of offsets and cmean, written by ckv_cluster_incremental_async and
+     swapped in by ckv_cluster_commit (may be NULL if the asynchronous form is never used) */
+  int32_t* offsets_alt; /* [units, K + 1] */
+  float* cmean_alt;     /* f32 [units, K, 128] */
 } ckv_layer;
 
 /* Text of the last error on this thread ("" if none).  Never NULL. */
@@ -118,7 +124,8 @@ int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * ascending token id inside a cluster), csum, msum, cmean = msum / csize,
  * and the cluster-ordered rows k_clu / v_clu.
  * Reads k_tok / v_tok rows [0, n).  Requires n_sink >= 0, 1 <= K <= m,
- * n <= capacity, iters >= 1.  Sets n_total = n_clustered = n on success.
+ * n <= capacity, iters >= 1, and no pending ckv_cluster_incremental_async
+ * result.  Sets n_total = n_clustered = n on success.
  */
 int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
                         void* ws, size_t ws_bytes, void* stream);
@@ -141,10 +148,41 @@ int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void*
  * swapped with k_clu / v_clu in *L.  The caller decides when to call it (the
  * method does so every 320 decoded tokens).  Requires the state written by a
  * previous prefill or incremental call (assign / csize / csum / msum of the
- * already clustered tokens) and non-NULL k_clu_alt / v_clu_alt.  A call with
- * no recent tokens does nothing.  Sets n_clustered = n_total.
+ * already clustered tokens), non-NULL k_clu_alt / v_clu_alt and no pending
+ * ckv_cluster_incremental_async result.  A call with no recent tokens does
+ * nothing.  Sets n_clustered = n_total.
  */
 int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Asynchronous incremental clustering (ClusterKV article §4.1: clustering runs
+ * beside decoding and its result is swapped in).  Computes exactly what
+ * ckv_cluster_incremental computes for the recent tokens [n_clustered, n_total),
+ * but leaves untouched every buffer that ckv_select, ckv_append_select and
+ * ckv_sparse_decode read: the new index and scoring means go to offsets_alt and
+ * cmean_alt, the new cluster-ordered copy to k_clu_alt / v_clu_alt.  The state
+ * only clustering reads (csum, msum, csize, cdir, assign, perm) is updated in
+ * place.  Records n_pending = n_total; nothing becomes current until
+ * ckv_cluster_commit.
+ * While the call's work runs on `stream`, recall, decode and appends may run on
+ * another stream against the old state, with a different workspace: tokens
+ * appended meanwhile are rows >= n_pending and stay recent.  No other
+ * clustering call on the layer until the commit.
+ * Requires non-NULL offsets_alt, cmean_alt, k_clu_alt, v_clu_alt and
+ * n_pending == 0 (CKV_EINVAL otherwise).  With no recent tokens it enqueues
+ * nothing and leaves n_pending at 0.
+ */
+int ckv_cluster_incremental_async(ckv_layer* L, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Make the last ckv_cluster_incremental_async result current (host only,
+ * enqueues nothing): swaps offsets / offsets_alt, cmean / cmean_alt,
+ * k_clu / k_clu_alt and v_clu / v_clu_alt in *L, sets n_clustered = n_pending
+ * and n_pending = 0.  The caller orders every later call that reads the layer
+ * after the async call's work (an event recorded on its stream, waited on by
+ * the other stream).  CKV_EINVAL if nothing is pending.
+ */
+int ckv_cluster_commit(ckv_layer* L);
 
 /*
  * Cluster-granularity recall (ClusterKV article §3.3; GQA reading: one recall

@@ -14,7 +14,9 @@ from .ckv import (  # noqa: F401
     ckv_abi_layer_bytes,
     ckv_append,
     ckv_append_select,
+    ckv_cluster_commit,
     ckv_cluster_incremental,
+    ckv_cluster_incremental_async,
     ckv_cluster_prefill,
     ckv_last_error,
     ckv_select,

@@ -30,13 +30,14 @@ class CkvLayerStruct(Structure):
         ("batch", c_int32), ("n_kv_heads", c_int32), ("group", c_int32),
         ("head_dim", c_int32), ("n_sink", c_int32), ("n_clusters", c_int32),
         ("capacity", c_int32), ("n_total", c_int32), ("n_clustered", c_int32),
-        ("reserved", c_int32),
+        ("n_pending", c_int32),
         ("k_tok", c_void_p), ("v_tok", c_void_p),
         ("k_clu", c_void_p), ("v_clu", c_void_p),
         ("k_clu_alt", c_void_p), ("v_clu_alt", c_void_p),
         ("cdir", c_void_p), ("csum", c_void_p), ("msum", c_void_p),
         ("cmean", c_void_p), ("csize", c_void_p), ("offsets", c_void_p),
         ("assign", c_void_p), ("perm", c_void_p),
+        ("offsets_alt", c_void_p), ("cmean_alt", c_void_p),
     ]
 
 
@@ -79,6 +80,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_append.argtypes = [LP, c_void_p, c_void_p, c_void_p]
     lib.ckv_cluster_incremental.restype = c_int
     lib.ckv_cluster_incremental.argtypes = [LP, c_void_p, c_size_t, c_void_p]
+    lib.ckv_cluster_incremental_async.restype = c_int
+    lib.ckv_cluster_incremental_async.argtypes = [LP, c_void_p, c_size_t, c_void_p]
+    lib.ckv_cluster_commit.restype = c_int
+    lib.ckv_cluster_commit.argtypes = [LP]
     lib.ckv_select.restype = c_int
     lib.ckv_select.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.ckv_append_select.restype = c_int
@@ -135,6 +140,15 @@ def ckv_append(layer: CkvLayerStruct, k_new: int, v_new: int, stream: int = 0) -
 def ckv_cluster_incremental(layer: CkvLayerStruct, ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check("ckv_cluster_incremental",
            load_library().ckv_cluster_incremental(_ref(layer), ws, ws_bytes, stream))
+
+
+def ckv_cluster_incremental_async(layer: CkvLayerStruct, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_cluster_incremental_async",
+           load_library().ckv_cluster_incremental_async(_ref(layer), ws, ws_bytes, stream))
+
+
+def ckv_cluster_commit(layer: CkvLayerStruct) -> None:
+    _check("ckv_cluster_commit", load_library().ckv_cluster_commit(_ref(layer)))
 
 
 def ckv_select(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, ws: int,

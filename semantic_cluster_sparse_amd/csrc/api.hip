@@ -89,6 +89,8 @@ int check_layer(const ckv_layer* L) {
     return fail(CKV_EINVAL, "n_total %d outside [0, capacity]", L->n_total);
   if (L->n_clustered < 0 || L->n_clustered > L->n_total)
     return fail(CKV_EINVAL, "n_clustered %d outside [0, n_total]", L->n_clustered);
+  if (L->n_pending != 0 && (L->n_pending < L->n_clustered || L->n_pending > L->n_total))
+    return fail(CKV_EINVAL, "n_pending %d outside [n_clustered, n_total]", L->n_pending);
   return CKV_OK;
 }
 
@@ -115,6 +117,45 @@ int check_ws(const ckv_layer* L, const void* ws, size_t ws_bytes) {
 }
 
 int clustered_tokens(const ckv_layer* L) { return L->n_clustered - L->n_sink; }
+
+// The kernels of one incremental clustering pass over the recent tokens
+// [n_clustered, n_total): labels and running sums in place; the rebuilt index
+// and scoring means go to offsets_out / cmean_out, the cluster-ordered copy to
+// k_clu_alt / v_clu_alt.  Leaves *L unchanged.
+int incremental_impl(const ckv_layer* L, void* ws, size_t ws_bytes, hipStream_t s, int32_t* offsets_out,
+                     float* cmean_out) {
+  int rc = check_ptrs("k_tok,v_tok,k_clu_alt,v_clu_alt,cdir,csum,msum,cmean,csize,offsets,assign,perm", 12,
+                      L->k_tok, L->v_tok, L->k_clu_alt, L->v_clu_alt, L->cdir, L->csum, L->msum, cmean_out,
+                      L->csize, offsets_out, L->assign, L->perm);
+  if (rc) return rc;
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+  const int units = L->batch * L->n_kv_heads;
+  const int K = L->n_clusters;
+  const int clu_stride = L->capacity - L->n_sink;
+  const int m_old = L->n_clustered - L->n_sink;
+  const int m_new = L->n_total - L->n_clustered;
+  const int m = m_old + m_new;
+  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
+  const Layout w = layout_of(L);
+  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
+  double* invn = (double*)((char*)ws + w.off_invn);
+
+  hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
+                                    clu_stride, m_old, units, s);
+  if (e != hipSuccess) return hip_status(e, "assign");
+  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, m_old, m_new, invn, clu_stride, units, s);
+  if (e != hipSuccess) return hip_status(e, "norms");
+  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
+  if (e != hipSuccess) return hip_status(e, "hist");
+  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, offsets_out, units, s);
+  if (e != hipSuccess) return hip_status(e, "scatter");
+  e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride,
+                         offsets_out, K, invn, L->csum, L->msum, cmean_out, L->csize, L->cdir, L->k_clu_alt,
+                         L->v_clu_alt, units, s);
+  if (e != hipSuccess) return hip_status(e, "update");
+  return CKV_OK;
+}
 
 }  // namespace
 
@@ -145,6 +186,9 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
   if (rc) return rc;
   if (iters < 1) return fail(CKV_EINVAL, "iters %d < 1", iters);
   if (n > L->capacity) return fail(CKV_EINVAL, "n %d > capacity %d", n, L->capacity);
+  if (L->n_pending != 0)
+    return fail(CKV_EINVAL, "an asynchronous incremental call is pending (n_pending %d): commit it first",
+                L->n_pending);
   const int m = n - L->n_sink;
   if (m < L->n_clusters) return fail(CKV_EINVAL, "need n_clusters %d <= m = n - n_sink = %d", L->n_clusters, m);
   rc = check_ptrs("k_tok,v_tok,k_clu,v_clu,cdir,csum,msum,cmean,csize,offsets,assign,perm,init_idx", 13,
@@ -202,41 +246,13 @@ int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void*
 int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
+  if (L->n_pending != 0)
+    return fail(CKV_EINVAL, "an asynchronous incremental call is pending (n_pending %d): commit it first",
+                L->n_pending);
   if (L->n_clustered < L->n_sink) return fail(CKV_EINVAL, "no cluster state (n_clustered < n_sink)");
   if (L->n_total == L->n_clustered) return CKV_OK;
-  rc = check_ptrs("k_tok,v_tok,k_clu_alt,v_clu_alt,cdir,csum,msum,cmean,csize,offsets,assign,perm", 12,
-                  L->k_tok, L->v_tok, L->k_clu_alt, L->v_clu_alt, L->cdir, L->csum, L->msum, L->cmean,
-                  L->csize, L->offsets, L->assign, L->perm);
+  rc = incremental_impl(L, ws, ws_bytes, (hipStream_t)stream, L->offsets, L->cmean);
   if (rc) return rc;
-  rc = check_ws(L, ws, ws_bytes);
-  if (rc) return rc;
-
-  const hipStream_t s = (hipStream_t)stream;
-  const int units = L->batch * L->n_kv_heads;
-  const int K = L->n_clusters;
-  const int clu_stride = L->capacity - L->n_sink;
-  const int m_old = L->n_clustered - L->n_sink;
-  const int m_new = L->n_total - L->n_clustered;
-  const int m = m_old + m_new;
-  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
-  const Layout w = layout_of(L);
-  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
-
-  double* invn = (double*)((char*)ws + w.off_invn);
-
-  hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
-                                    clu_stride, m_old, units, s);
-  if (e != hipSuccess) return hip_status(e, "assign");
-  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, m_old, m_new, invn, clu_stride, units, s);
-  if (e != hipSuccess) return hip_status(e, "norms");
-  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
-  if (e != hipSuccess) return hip_status(e, "hist");
-  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
-  if (e != hipSuccess) return hip_status(e, "scatter");
-  e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets,
-                         K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu_alt, L->v_clu_alt, units,
-                         s);
-  if (e != hipSuccess) return hip_status(e, "update");
   uint16_t* tk = L->k_clu;
   uint16_t* tv = L->v_clu;
   L->k_clu = L->k_clu_alt;
@@ -244,6 +260,44 @@ int ckv_cluster_incremental(ckv_layer* L, void* ws, size_t ws_bytes, void* strea
   L->k_clu_alt = tk;
   L->v_clu_alt = tv;
   L->n_clustered = L->n_total;
+  return CKV_OK;
+}
+
+int ckv_cluster_incremental_async(ckv_layer* L, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->n_pending != 0)
+    return fail(CKV_EINVAL, "an asynchronous incremental call is already pending (n_pending %d)", L->n_pending);
+  if (L->n_clustered < L->n_sink) return fail(CKV_EINVAL, "no cluster state (n_clustered < n_sink)");
+  rc = check_ptrs("offsets_alt,cmean_alt", 2, L->offsets_alt, L->cmean_alt);
+  if (rc) return rc;
+  if (L->n_total == L->n_clustered) return CKV_OK;
+  rc = incremental_impl(L, ws, ws_bytes, (hipStream_t)stream, L->offsets_alt, L->cmean_alt);
+  if (rc) return rc;
+  L->n_pending = L->n_total;
+  return CKV_OK;
+}
+
+int ckv_cluster_commit(ckv_layer* L) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->n_pending == 0) return fail(CKV_EINVAL, "no asynchronous incremental call is pending");
+  if (L->n_pending < L->n_clustered || L->n_pending > L->n_total)
+    return fail(CKV_EINVAL, "n_pending %d outside [n_clustered, n_total]", L->n_pending);
+  int32_t* to = L->offsets;
+  L->offsets = L->offsets_alt;
+  L->offsets_alt = to;
+  float* tm = L->cmean;
+  L->cmean = L->cmean_alt;
+  L->cmean_alt = tm;
+  uint16_t* tk = L->k_clu;
+  uint16_t* tv = L->v_clu;
+  L->k_clu = L->k_clu_alt;
+  L->v_clu = L->v_clu_alt;
+  L->k_clu_alt = tk;
+  L->v_clu_alt = tv;
+  L->n_clustered = L->n_pending;
+  L->n_pending = 0;
   return CKV_OK;
 }
 

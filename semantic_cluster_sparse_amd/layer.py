@@ -47,18 +47,25 @@ class Layer:
         self.offsets = torch.zeros((u, K + 1), **i32)
         self.assign = torch.zeros((u, clu), **i32)
         self.perm = torch.zeros((u, clu), **i32)
+        # second index / means and a second workspace for clustering beside decoding
+        self.offsets_alt = torch.zeros((u, K + 1), **i32) if incremental else None
+        self.cmean_alt = torch.zeros((u, K, d), dtype=torch.float32, device=self.device) if incremental else None
         self.struct = ckv.CkvLayerStruct(
             batch=batch, n_kv_heads=n_kv_heads, group=group, head_dim=HEAD_DIM, n_sink=n_sink,
-            n_clusters=n_clusters, capacity=capacity, n_total=0, n_clustered=0, reserved=0)
+            n_clusters=n_clusters, capacity=capacity, n_total=0, n_clustered=0, n_pending=0)
         self._bind()
         self.ws_bytes = ckv.ckv_workspace_bytes(self.struct, max_budget)
         self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=self.device)
         ckv.ckv_workspace_init(self.ws.data_ptr(), self.ws_bytes, _stream())
+        self.ws_bg = None
+        if incremental:
+            self.ws_bg = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=self.device)
+            ckv.ckv_workspace_init(self.ws_bg.data_ptr(), self.ws_bytes, _stream())
 
     def _bind(self) -> None:
         s = self.struct
         for name in ("k_tok", "v_tok", "k_clu", "v_clu", "k_clu_alt", "v_clu_alt", "cdir", "csum",
-                     "msum", "cmean", "csize", "offsets", "assign", "perm"):
+                     "msum", "cmean", "csize", "offsets", "assign", "perm", "offsets_alt", "cmean_alt"):
             t = getattr(self, name)
             setattr(s, name, t.data_ptr() if t is not None else None)
 
@@ -88,10 +95,30 @@ class Layer:
 
     def incremental(self) -> None:
         ckv.ckv_cluster_incremental(self.struct, self.ws.data_ptr(), self.ws_bytes, _stream())
-        # the library swapped the cluster-ordered buffers inside the struct
-        if self.struct.k_clu != self.k_clu.data_ptr():
-            self.k_clu, self.k_clu_alt = self.k_clu_alt, self.k_clu
-            self.v_clu, self.v_clu_alt = self.v_clu_alt, self.v_clu
+        self._sync_swapped()
+
+    def incremental_async(self) -> None:
+        """Cluster the recent tokens into the second buffers, on the current stream,
+        with the second workspace; recall and decode may go on meanwhile on another
+        stream.  commit() makes the result current."""
+        ckv.ckv_cluster_incremental_async(self.struct, self.ws_bg.data_ptr(), self.ws_bytes, _stream())
+
+    def commit(self) -> None:
+        ckv.ckv_cluster_commit(self.struct)
+        self._sync_swapped()
+
+    def _sync_swapped(self) -> None:
+        # the library exchanged buffers inside the struct: follow it
+        pairs = (("k_clu", "k_clu_alt"), ("v_clu", "v_clu_alt"), ("offsets", "offsets_alt"), ("cmean", "cmean_alt"))
+        for cur, alt in pairs:
+            t_cur, t_alt = getattr(self, cur), getattr(self, alt)
+            if t_alt is not None and getattr(self.struct, cur) == t_alt.data_ptr():
+                setattr(self, cur, t_alt)
+                setattr(self, alt, t_cur)
+
+    @property
+    def n_pending(self) -> int:
+        return self.struct.n_pending
 
     def select(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor,
                sel_count: torch.Tensor) -> None:

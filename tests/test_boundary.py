@@ -40,7 +40,7 @@ def test_layer_struct_size_matches():
 
 def _layer(**kw):
     base = dict(batch=1, n_kv_heads=8, group=4, head_dim=128, n_sink=16, n_clusters=400,
-                capacity=32768 + 64, n_total=0, n_clustered=0, reserved=0)
+                capacity=32768 + 64, n_total=0, n_clustered=0, n_pending=0)
     base.update(kw)
     return ckv.CkvLayerStruct(**base)
 
@@ -142,3 +142,46 @@ def test_state_inconsistency_is_rejected():
     with pytest.raises(ckv.CkvError) as e:
         ckv.ckv_sparse_decode(L, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 1 << 40)
     assert e.value.code == ckv.CKV_EINVAL
+
+
+def test_async_incremental_and_commit_host_rules():
+    # commit with nothing pending
+    L = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_commit(L)
+    assert e.value.code == ckv.CKV_EINVAL
+    # the asynchronous form needs the second index and means
+    L.offsets_alt = None
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_incremental_async(L, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and L.n_pending == 0
+    # no recent tokens: nothing to do, nothing pending
+    L0 = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=100, n_clustered=100))
+    ckv.ckv_cluster_incremental_async(L0, FAKE, 1 << 40)
+    assert L0.n_pending == 0
+    # while a result is pending, every other clustering call is refused
+    P = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=120))
+    for call in (lambda: ckv.ckv_cluster_incremental_async(P, FAKE, 1 << 40),
+                 lambda: ckv.ckv_cluster_incremental(P, FAKE, 1 << 40),
+                 lambda: ckv.ckv_cluster_prefill(P, 130, 2, FAKE, FAKE, 1 << 40)):
+        with pytest.raises(ckv.CkvError) as e:
+            call()
+        assert e.value.code == ckv.CKV_EINVAL and "pending" in e.value.message
+    # a pending count outside [n_clustered, n_total] is an inconsistent layer
+    bad = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=140))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_commit(bad)
+    assert e.value.code == ckv.CKV_EINVAL
+
+
+def test_commit_swaps_the_second_buffers():
+    L = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=120))
+    names = ("k_clu", "v_clu", "offsets", "cmean")
+    for i, n in enumerate(names):
+        setattr(L, n, FAKE + 0x1000 * (2 * i + 1))
+        setattr(L, n + "_alt", FAKE + 0x1000 * (2 * i + 2))
+    before = {n: (getattr(L, n), getattr(L, n + "_alt")) for n in names}
+    ckv.ckv_cluster_commit(L)
+    for n in names:
+        assert (getattr(L, n), getattr(L, n + "_alt")) == before[n][::-1], n
+    assert L.n_clustered == 120 and L.n_pending == 0 and L.n_total == 130

@@ -358,6 +358,66 @@ def test_incremental_noop():
         assert torch.equal(a, b)
 
 
+def test_incremental_async_matches_sync():
+    cfg = synth.CONFIGS["llama8b-incremental-b16"]
+    units = [0, 1, 2, 3]
+    say(f"case: async incremental + commit against the synchronous call ({cfg.name}, units 0-3, "
+        f"+{cfg.new_tokens} keys)")
+    cap = cfg.n_tokens + cfg.new_tokens + 4
+    k, v, cen = synth.make_layer_inputs(cfg, units=units, capacity=cap)
+    init = to_dev(synth.make_init_indices(cfg.init_seed, len(units), cfg.m, cfg.n_clusters), torch.int32)
+    kn, vn, newc = synth.make_new_tokens(cfg.data_seed, cen, cfg.new_tokens, cfg.new_components,
+                                         cfg.new_fraction)
+    q = dev_bf16(synth.make_queries(cfg.query_seed, np.concatenate([cen, newc], axis=1), cfg.group))
+    n_new = cfg.n_tokens + cfg.new_tokens
+    layers = []
+    for _ in range(2):
+        L = gpu_layer(k, v, cfg.group, cfg.n_clusters, max_budget=cfg.budget)
+        L.prefill(cfg.n_tokens, 2, init)
+        L.k_tok[:, cfg.n_tokens:n_new].copy_(dev_bf16(kn))
+        L.v_tok[:, cfg.n_tokens:n_new].copy_(dev_bf16(vn))
+        L.set_counters(n_new, cfg.n_tokens)
+        layers.append(L)
+    A, B = layers
+    A.incremental()
+    U = len(units)
+
+    def recall_decode(L):
+        sp = torch.full((U, cfg.budget), -1, dtype=torch.int32, device="cuda")
+        cn = torch.zeros((U,), dtype=torch.int32, device="cuda")
+        out = torch.zeros((U, cfg.group, D), dtype=torch.float32, device="cuda")
+        L.select(q, cfg.budget, sp, cn)
+        L.sparse_decode(q, sp, cn, cfg.budget, out)
+        return sp, cn, out
+
+    before = recall_decode(B)
+    cur_before = [t.clone() for t in (B.offsets, B.cmean, B.k_clu, B.v_clu)]
+    main = torch.cuda.current_stream()
+    bg = torch.cuda.Stream()
+    bg.wait_stream(main)
+    with torch.cuda.stream(bg):
+        B.incremental_async()
+        done = torch.cuda.Event()
+        done.record(bg)
+    during = recall_decode(B)             # main stream, old state, beside the clustering
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    assert B.n_pending == n_new and B.n_clustered == cfg.n_tokens
+    for a, b in zip(before, during):
+        assert torch.equal(a, b), "recall / decode changed while the clustering ran"
+    for a, b in zip(cur_before, (B.offsets, B.cmean, B.k_clu, B.v_clu)):
+        assert torch.equal(a, b), "the current state changed before the commit"
+    B.commit()
+    assert B.n_pending == 0 and B.n_clustered == A.n_clustered == n_new
+    m = n_new - 16
+    for name in ("offsets", "cmean", "csum", "msum", "csize", "cdir"):
+        assert torch.equal(getattr(A, name), getattr(B, name)), name
+    for name in ("k_clu", "v_clu", "assign", "perm"):
+        assert torch.equal(getattr(A, name)[:, :m], getattr(B, name)[:, :m]), name
+    for a, b in zip(recall_decode(A), recall_decode(B)):
+        assert torch.equal(a, b)
+
+
 def test_append_select_matches_separate_calls():
     say("case: fused append + select against ckv_append then ckv_select (llama layer, 8 units)")
     cfg = synth.CONFIGS["llama8b-layer-32k"]
