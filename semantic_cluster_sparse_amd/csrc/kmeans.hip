@@ -355,9 +355,17 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ a
   __syncthreads();
   const int lo = t * kSortTile, hi = min(count, lo + kSortTile);
   const int32_t* a = assign + (size_t)u * clu_stride;
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    int c = a[i];
-    c = c < 0 ? 0 : (c >= K ? K - 1 : c);
+  constexpr int kPer = kSortTile / 256;  // labels per thread, all loads in flight at once
+  int lab[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = lo + threadIdx.x + k * 256;
+    lab[k] = i < hi ? a[i] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    if (lo + (int)threadIdx.x + k * 256 >= hi) continue;
+    const int c = lab[k] < 0 ? 0 : (lab[k] >= K ? K - 1 : lab[k]);
     atomicAdd(&h[c], 1);
   }
   __syncthreads();
@@ -399,10 +407,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     const int c = c0 + threadIdx.x;
     int total = 0, before = 0;
     if (c < K) {
-      for (int tt = 0; tt < tiles; ++tt) {
-        const int v = hu[(size_t)tt * K + c];
-        total += v;
-        if (tt < t) before += v;
+      for (int tt0 = 0; tt0 < tiles; tt0 += 8) {  // 8 tiles' counts in flight at once
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = tt0 + k < tiles ? hu[(size_t)(tt0 + k) * K + c] : 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          total += v[k];
+          if (tt0 + k < t) before += v[k];
+        }
       }
     }
     int chunk_total;
@@ -415,18 +428,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   }
   if (t == 0 && threadIdx.x == 0) offsets[(size_t)u * (K + 1) + K] = running;
 
-  for (int e = threadIdx.x; e < 4 * kMaxClusters; e += blockDim.x) (&hw[0][0])[e] = 0;
-  __syncthreads();
+  // this wave's labels, all loads in flight at once (reused for the placement)
+  constexpr int kBatches = kSortTile / 4 / kWave;
   const int32_t* a = assign + (size_t)u * clu_stride;
   const int wlo = t * kSortTile + wave * (kSortTile / 4);
-  for (int b = 0; b < kSortTile / 4; b += kWave) {
-    const int i = wlo + b + lane;
-    if (i < count) {
-      int c = a[i];
-      c = c < 0 ? 0 : (c >= K ? K - 1 : c);
-      atomicAdd(&hw[wave][c], 1);
-    }
+  int lab[kBatches];
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) {
+    const int i = wlo + b * kWave + lane;
+    int c = i < count ? a[i] : 0;
+    lab[b] = c < 0 ? 0 : (c >= K ? K - 1 : c);
   }
+  for (int e = threadIdx.x; e < 4 * kMaxClusters; e += blockDim.x) (&hw[0][0])[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b)
+    if (wlo + b * kWave + lane < count) atomicAdd(&hw[wave][lab[b]], 1);
   __syncthreads();
   for (int c = threadIdx.x; c < K; c += blockDim.x) {
     int run = base[c];
@@ -443,11 +460,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   while ((1 << nbits) < K) ++nbits;
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* pu = perm + (size_t)u * clu_stride;
-  for (int b = 0; b < kSortTile / 4; b += kWave) {
-    const int i = wlo + b + lane;
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) {
+    const int i = wlo + b * kWave + lane;
     const bool valid = i < count;
-    int c = valid ? a[i] : 0;
-    c = c < 0 ? 0 : (c >= K ? K - 1 : c);
+    const int c = lab[b];
     const unsigned long long peers = match_label(c, valid, nbits);
     int bs = 0;
     if (valid) bs = hw[wave][c];
