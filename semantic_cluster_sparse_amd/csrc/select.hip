@@ -557,22 +557,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int n_cut = fill ? sz[cut] : 0;
   const int lo_cut = fill ? off[cut] : 0;
 
-  // ---- phase 3: scores q_bar . k of the cut cluster's tokens (and their range)
-  constexpr int kCutRows = 4;
+  // ---- phase 3 (waves 0-7): scores q_bar . k of the cut cluster's tokens (and
+  // their range).  Meanwhile phase 5 (waves 8-15) writes the whole clusters, so
+  // those stores overlap the wait for the cut cluster's rows.
+  constexpr int kCutWaves = kSelWaves / 2;
+  constexpr int kCutGroups = kCutWaves * (kWave / 16);
+  constexpr int kCutRows = 8;
   const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo_cut) * kHeadDim + li * 8;
   uint32_t* cut_keys_g = cut_ws + (size_t)u * clu_stride;
-  {
+  int32_t* out = sel_pos + (size_t)u * budget;
+  if (wave < kCutWaves) {
     float mn = INFINITY, mx = -INFINITY;
-    for (int r0 = 0; r0 < n_cut; r0 += kCutRows * kSelGroups) {
+    for (int r0 = 0; r0 < n_cut; r0 += kCutRows * kCutGroups) {
       uint4 cw[kCutRows];
 #pragma unroll
       for (int t = 0; t < kCutRows; ++t) {
-        const int i = r0 + grp + t * kSelGroups;
+        const int i = r0 + grp + t * kCutGroups;
         cw[t] = i < n_cut ? *reinterpret_cast<const uint4*>(kc + (size_t)i * kHeadDim) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < kCutRows; ++t) {
-        const int i = r0 + grp + t * kSelGroups;
+        const int i = r0 + grp + t * kCutGroups;
         float d = qb[0] * bf16_lo(cw[t].x);
         d = fmaf(qb[1], bf16_hi(cw[t].x), d); d = fmaf(qb[2], bf16_lo(cw[t].y), d);
         d = fmaf(qb[3], bf16_hi(cw[t].y), d); d = fmaf(qb[4], bf16_lo(cw[t].z), d);
@@ -597,13 +602,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       ws.rmin[wave] = mn;
       ws.rmax[wave] = mx;
     }
+  } else {
+    if (lane == 0) {
+      ws.rmin[wave] = INFINITY;
+      ws.rmax[wave] = -INFINITY;
+    }
+    // ---- phase 5: whole clusters (positions off_j .. off_j + n_j - 1 at ost_j,
+    // 64 consecutive slots per store instruction)
+    for (int jb = (wave - kCutWaves) * kWave; jb < K; jb += (kSelWaves - kCutWaves) * kWave) {
+      const int j = jb + lane;
+      const int t = j < K ? take[j] : 0;
+      const int o = j < K ? ost[j] : 0;
+      const int lo2 = j < K ? off[j] : 0;
+      unsigned long long live = __ballot(t > 0);
+      while (live) {
+        const int l = (int)__ffsll((long long)live) - 1;
+        live &= live - 1;
+        const int tl = __builtin_amdgcn_readlane(t, l), ol = __builtin_amdgcn_readlane(o, l);
+        const int ll = __builtin_amdgcn_readlane(lo2, l);
+        for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
+      }
+    }
   }
   if (n_cut > kCutLds) __threadfence_block();  // the wave-0 fallback below re-reads cut_keys_g
   lds_barrier();
 
   // ---- phase 4: the need highest-scoring tokens of the cut cluster, written
   // in position order (4 consecutive tokens per thread)
-  int32_t* out = sel_pos + (size_t)u * budget;
   if (fill) {
     constexpr int E = kCutLds / kSelThreads;
     int st[E];
@@ -627,22 +652,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
 
-  // ---- phase 5: whole clusters (positions off_j .. off_j + n_j - 1 at ost_j,
-  // 64 consecutive slots per store instruction)
-  for (int jb = wave * kWave; jb < K; jb += kSelThreads) {
-    const int j = jb + lane;
-    const int t = j < K ? take[j] : 0;
-    const int o = j < K ? ost[j] : 0;
-    const int lo2 = j < K ? off[j] : 0;
-    unsigned long long live = __ballot(t > 0);
-    while (live) {
-      const int l = (int)__ffsll((long long)live) - 1;
-      live &= live - 1;
-      const int tl = __builtin_amdgcn_readlane(t, l), ol = __builtin_amdgcn_readlane(o, l);
-      const int ll = __builtin_amdgcn_readlane(lo2, l);
-      for (int i = lane; i < tl; i += kWave) out[ol + i] = ll + i;
-    }
-  }
   if (tid == 0) sel_count[u] = beff;
 }
 
