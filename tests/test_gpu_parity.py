@@ -191,6 +191,47 @@ def test_llama_layer_end_to_end():
     assert total_diff <= MISMATCH_FRACTION * 2 * 3 * cfg.budget
 
 
+@pytest.mark.parametrize("K", [700, 1024])
+def test_large_k_end_to_end(K):
+    # K > 512 takes the LDS-chunked assignment kernel; 1024 is the largest K the library accepts
+    n, units, iters, budget, G = 16 + 24000, 2, 3, 2048, 4
+    say(f"case: K={K} end to end, {units} units, n={n}, {iters} rounds, budget {budget}")
+    ks, vs, cs = [], [], []
+    for u in range(units):
+        kb, vb, c = synth.make_unit_inputs(95, u, n, 1024)
+        ks.append(kb), vs.append(vb), cs.append(c)
+    k, v, cen = np.stack(ks), np.stack(vs), np.stack(cs)
+    init = synth.make_init_indices(96, units, n - 16, K)
+    q = synth.make_queries(97, cen, G)
+    L = gpu_layer(k, v, G, K, max_budget=budget)
+    L.prefill(n, iters, to_dev(init, torch.int32))
+    sel_pos = torch.zeros((units, budget), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((units,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((units, G, D), dtype=torch.float32, device="cuda")
+    qd = dev_bf16(q)
+    L.select(qd, budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    compared = 0
+    for u in range(units):
+        ora = pipeline.prefill_unit(k[u], n, init[u], K, iters, v_bits=v[u], history=True)
+        x = bf16.widen(k[u][16:n])
+        mism = check_state(L, u, ora, x, ora["history"][-2][1], tag=f"K={K}")
+        assert mism <= MISMATCH_FRACTION * (n - 16)
+        if mism:
+            continue
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+        if compare_selection(L, u, sp, cn, ora, sel, budget) == 0:
+            ref = pipeline.decode_unit(q[u], k[u], v[u], ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
+                                       16, n, n)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+            compared += 1
+    assert compared >= 1
+
+
 # ------------------------------------------------------------------ select
 
 
