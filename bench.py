@@ -24,6 +24,10 @@ new mixture components): times ckv_cluster_incremental, then a budget-1024
 ckv_select and ckv_sparse_decode on batch-16 queries.  Reports the
 incremental latency.
 
+``--per-head-recall`` switches the stack workloads to the other grouped-query
+reading: ckv_append + ckv_select_per_head + ckv_sparse_decode_per_head, one
+recalled set per query head.
+
 The stack workloads also time a dense-decode baseline on the same harness
 (``full_attention``): budget >= m, so recall takes every cluster and the
 decode kernel attends to all cached tokens.
@@ -229,6 +233,7 @@ def run_stack(cfg, args) -> dict:
     units, G, budget = cfg.units, cfg.group, cfg.budget
     recluster = cfg.new_tokens if cfg.new_tokens > 0 else 0
     so = seed_offset(cfg)
+    ph = bool(args.per_head_recall)
     stream = torch.cuda.current_stream()
 
     log(f"[bench] {cfg.name}: allocating {n_layers} layers of {units} units, capacity {cap}")
@@ -236,7 +241,7 @@ def run_stack(cfg, args) -> dict:
     qs = []
     for li in range(n_layers):
         L = Layer(batch=cfg.batch, n_kv_heads=cfg.n_kv_heads, group=G, n_clusters=cfg.n_clusters,
-                  capacity=cap, max_budget=budget, incremental=recluster > 0, device=dev)
+                  capacity=cap, max_budget=budget, incremental=recluster > 0, per_head=ph, device=dev)
         cen = dgen.fill_mixture(L.k_tok, L.v_tok, n_fill, cfg.components, seed=10_000 + so + li)
         qs.append([dgen.queries(cen, G, seed=20_000 + so + 100 * li + s) for s in range(W + K)])
         del cen
@@ -266,8 +271,9 @@ def run_stack(cfg, args) -> dict:
         L.set_counters(n_fill, cfg.n_tokens)
 
     # ---------------------------------------------------------------- decode step buffers
-    sel_pos = [torch.zeros((units, budget), dtype=torch.int32, device=dev) for _ in range(n_layers)]
-    cnt = [torch.zeros((units,), dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    sets = units * G if ph else units     # recalled sets per layer
+    sel_pos = [torch.zeros((sets, budget), dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    cnt = [torch.zeros((sets,), dtype=torch.int32, device=dev) for _ in range(n_layers)]
     outs = [torch.zeros((units, G, 128), dtype=torch.float32, device=dev) for _ in range(n_layers)]
     k_new = [dgen.rows(units, 128, 40_000 + s, dev) for s in range(W + K)]
     v_new = [dgen.rows(units, 128, 50_000 + s, dev) for s in range(W + K)]
@@ -314,8 +320,13 @@ def run_stack(cfg, args) -> dict:
             for L in layers:
                 L.incremental()
         for li, L in enumerate(layers):
-            L.append_select(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li])
-            L.sparse_decode(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
+            if ph:
+                L.append(k_new[s], v_new[s])
+                L.select_per_head(qs[li][s], budget, sel_pos[li], cnt[li])
+                L.sparse_decode_per_head(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
+            else:
+                L.append_select(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li])
+                L.sparse_decode(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
 
     graphs = []
     cs = None
@@ -387,7 +398,8 @@ def run_stack(cfg, args) -> dict:
 
     def decode_all() -> None:
         for li, L in enumerate(layers):
-            L.sparse_decode(qs[li][qlast], sel_pos[li], cnt[li], budget, outs[li])
+            (L.sparse_decode_per_head if ph else L.sparse_decode)(qs[li][qlast], sel_pos[li], cnt[li], budget,
+                                                                  outs[li])
 
     if graphs:
         dg = torch.cuda.CUDAGraph()
@@ -407,13 +419,28 @@ def run_stack(cfg, args) -> dict:
     torch.cuda.synchronize()
     dec_ms = a.elapsed_time(b) / (reps * n_layers)
     r_now = layers[0].n_total - layers[0].n_clustered
-    dbytes = decode_bytes(units, 16, budget, r_now, G)
+    if ph:
+        # The heads of one KV head recall overlapping sets, and their shared rows
+        # are fetched from HBM once (the rest hit the caches), so the bytes that
+        # must move are those of each unit's union of recalled rows, plus every
+        # set's indices and every head's query and output.
+        srt = sel_pos[n_layers - 1].view(units, G * budget).sort(dim=1).values
+        distinct = int((1 + (srt[:, 1:] != srt[:, :-1]).sum(dim=1)).sum())
+        dbytes = (units * (16 + r_now) + distinct) * 2 * 128 * 2 + sets * (4 * budget + 2 * 128 + 4 * 128)
+        log(f"[bench] per-head recall: {distinct / units:.0f} distinct recalled rows per unit "
+            f"(of {G * budget} recalled)")
+    else:
+        dbytes = decode_bytes(units, 16, budget, r_now, G)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
     r_mean = cfg.n_recent + (W + K) // 2
     if recluster:
         r_mean = recluster // 2
-    step_bytes = n_layers * (decode_bytes(units, 16, budget, r_mean, G)
-                             + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
+    if ph:
+        step_bytes = n_layers * (decode_bytes(sets, 16, budget, r_mean, 1)
+                                 + select_bytes(sets, cfg.n_clusters, budget, 1, 82) + units * 2 * 256)
+    else:
+        step_bytes = n_layers * (decode_bytes(units, 16, budget, r_mean, G)
+                                 + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
     log(f"[bench] ckv_sparse_decode {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
 
     # ---------------------------------------------------------------- full-attention baseline
@@ -422,7 +449,7 @@ def run_stack(cfg, args) -> dict:
         full = full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs if graphs else None,
                                        stream, dev)
         full["step_speedup"] = n_layers * full["decode_us"] * 1e-3 / ms_per_step
-    traffic = measured_traffic() if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers else None
+    traffic = measured_traffic() if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph else None
 
     result = {
         "metric": METRIC,
@@ -439,8 +466,8 @@ def run_stack(cfg, args) -> dict:
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": n_layers, "batch": cfg.batch, "kv_heads": cfg.n_kv_heads,
                    "group": G, "context": n_fill, "clusters": cfg.n_clusters, "budget": budget,
-                   "graphs": not args.no_graph},
-        "roofline": {"bound": "hbm", "kernel": f"ckv::sparse_decode_kernel<{_group_tier(G)}>",
+                   "graphs": not args.no_graph, "recall": "per query head" if ph else "per KV head (summed query)"},
+        "roofline": {"bound": "hbm", "kernel": f"ckv::sparse_decode_kernel<{1 if ph else _group_tier(G)}>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},
@@ -602,6 +629,8 @@ def main() -> int:
     ap.add_argument("--async-recluster", action="store_true",
                     help="re-cluster on a second stream beside the decode steps and commit later")
     ap.add_argument("--async-lag", type=int, default=16, help="steps between starting and committing")
+    ap.add_argument("--per-head-recall", action="store_true",
+                    help="one recall and attention set per query head instead of per KV head")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")

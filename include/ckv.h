@@ -212,6 +212,33 @@ int ckv_append_select(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new
                       void* stream);
 
 /*
+ * Per-query-head recall (ClusterKV article §3.3 recall stated for a single
+ * query, applied to each query head separately; the other reading of
+ * grouped-query attention, where the G heads of a KV head do not share one
+ * set).  Exactly ckv_select with G = 1 for every query head:
+ *   sel_pos   int32 [units * group, budget] (device, written): set s = u * group + g
+ *             is the recall of query head g of unit u, scored with q_g alone
+ *   sel_count int32 [units * group] (device, written): min(budget, m)
+ * The workspace must hold ckv_workspace_bytes_per_head() bytes.  Errors as
+ * for ckv_select.
+ */
+size_t ckv_workspace_bytes_per_head(const ckv_layer* L, int32_t max_budget);
+int ckv_select_per_head(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                        int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse decode with one recalled set per query head (the output of
+ * ckv_select_per_head): out[b, h * group + g, :] attends to the sinks, the
+ * sel_count[s] rows listed in sel_pos[s, :] (s = u * group + g, row stride
+ * `budget`) and the recent rows.  Layouts, limits and errors as for
+ * ckv_sparse_decode; the workspace must hold ckv_workspace_bytes_per_head()
+ * bytes, and its first 4 * units * group bytes are arrival counters left zero.
+ */
+int ckv_sparse_decode_per_head(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos,
+                               const int32_t* sel_count, int32_t budget, float* out, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
  * Sparse decode (ClusterKV article §3.1 attention; §4.1 cluster-contiguous
  * rows): for every query head g of unit u,
  *   out[b, h * group + g, :] = softmax(q_g . K_S^T / sqrt(128)) V_S

@@ -75,3 +75,22 @@ def decode_unit(q_bits, k_tok_bits, v_tok_bits, k_clu_bits, v_clu_bits, position
         bf16.widen(q_bits), bf16.widen(k_tok_bits), bf16.widen(v_tok_bits),
         bf16.widen(k_clu_bits), bf16.widen(v_clu_bits), positions,
         n_sink, n_clustered, n_total)
+
+
+def select_per_head(q_bits: np.ndarray, cmean: np.ndarray, csize, offsets,
+                    k_clu_bits: np.ndarray, budget: int) -> list[dict]:
+    """Per-query-head recall, the other grouped-query reading of the ClusterKV
+    article's §3.3: the recall is stated for one query, so every query head g
+    runs it with q_g alone (no sum over the heads of a KV head).  One result per
+    row of ``q_bits`` [G, d]."""
+    return [select_unit(q_bits[g:g + 1], cmean, csize, offsets, k_clu_bits, budget)
+            for g in range(q_bits.shape[0])]
+
+
+def decode_per_head(q_bits, k_tok_bits, v_tok_bits, k_clu_bits, v_clu_bits, positions_per_head,
+                    n_sink: int, n_clustered: int, n_total: int) -> np.ndarray:
+    """Attention output [G, d]: head g attends to the sinks, its own recalled rows
+    and the recent rows."""
+    return np.stack([decode_unit(q_bits[g:g + 1], k_tok_bits, v_tok_bits, k_clu_bits, v_clu_bits,
+                                 positions_per_head[g], n_sink, n_clustered, n_total)[0]
+                     for g in range(q_bits.shape[0])])

@@ -20,8 +20,11 @@ from .ckv import (  # noqa: F401
     ckv_cluster_prefill,
     ckv_last_error,
     ckv_select,
+    ckv_select_per_head,
     ckv_sparse_decode,
+    ckv_sparse_decode_per_head,
     ckv_workspace_bytes,
+    ckv_workspace_bytes_per_head,
     ckv_workspace_init,
     load_library,
     library_path,

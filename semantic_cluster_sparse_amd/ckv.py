@@ -89,6 +89,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_append_select.restype = c_int
     lib.ckv_append_select.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
+    lib.ckv_workspace_bytes_per_head.restype = c_size_t
+    lib.ckv_workspace_bytes_per_head.argtypes = [LP, c_int32]
+    lib.ckv_select_per_head.restype = c_int
+    lib.ckv_select_per_head.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ckv_sparse_decode_per_head.restype = c_int
+    lib.ckv_sparse_decode_per_head.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                               c_size_t, c_void_p]
     lib.ckv_sparse_decode.restype = c_int
     lib.ckv_sparse_decode.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
@@ -168,3 +175,23 @@ def ckv_sparse_decode(layer: CkvLayerStruct, q: int, sel_pos: int, sel_count: in
     _check("ckv_sparse_decode",
            load_library().ckv_sparse_decode(_ref(layer), q, sel_pos, sel_count, budget, out, ws,
                                             ws_bytes, stream))
+
+
+def ckv_workspace_bytes_per_head(layer: CkvLayerStruct, max_budget: int) -> int:
+    n = int(load_library().ckv_workspace_bytes_per_head(_ref(layer), max_budget))
+    if n == 0:
+        raise CkvError("ckv_workspace_bytes_per_head", CKV_EINVAL, ckv_last_error())
+    return n
+
+
+def ckv_select_per_head(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, ws: int,
+                        ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_select_per_head",
+           load_library().ckv_select_per_head(_ref(layer), q, budget, sel_pos, sel_count, ws, ws_bytes, stream))
+
+
+def ckv_sparse_decode_per_head(layer: CkvLayerStruct, q: int, sel_pos: int, sel_count: int, budget: int,
+                               out: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_sparse_decode_per_head",
+           load_library().ckv_sparse_decode_per_head(_ref(layer), q, sel_pos, sel_count, budget, out, ws,
+                                                     ws_bytes, stream))

@@ -48,16 +48,19 @@ int group_tier(int g) {
   return t;
 }
 
-Layout layout_of(const ckv_layer* L) {
+// per_head: one recall / attention set per query head (units * group of them)
+// instead of one per KV head.
+Layout layout_of(const ckv_layer* L, bool per_head = false) {
   const size_t units = (size_t)L->batch * L->n_kv_heads;
+  const size_t sets = units * (per_head ? (size_t)L->group : 1);
   const size_t clu_cap = (size_t)(L->capacity - L->n_sink);
   const size_t tiles = (clu_cap + ckv::kSortTile - 1) / ckv::kSortTile;
   Layout w;
-  w.counters = align256(units * 2 * sizeof(uint32_t));
+  w.counters = align256(sets * 2 * sizeof(uint32_t));
   w.hist = align256(units * tiles * L->n_clusters * sizeof(int32_t));
   w.invn = align256(units * clu_cap * sizeof(double));
-  w.scores = align256(units * L->n_clusters * sizeof(float));
-  w.cut = align256(units * clu_cap * sizeof(uint32_t));
+  w.scores = align256(sets * L->n_clusters * sizeof(float));
+  w.cut = align256(sets * clu_cap * sizeof(uint32_t));
   w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
   w.off_hist = w.counters;
   w.off_invn = w.counters + w.hist;
@@ -108,9 +111,9 @@ int check_ptrs(const char* names, int n, ...) {
   return CKV_OK;
 }
 
-int check_ws(const ckv_layer* L, const void* ws, size_t ws_bytes) {
+int check_ws(const ckv_layer* L, const void* ws, size_t ws_bytes, bool per_head = false) {
   if (!aligned16(ws)) return fail(CKV_EINVAL, "workspace is NULL or not 16-byte aligned");
-  const Layout w = layout_of(L);
+  const Layout w = layout_of(L, per_head);
   if (ws_bytes < w.total)
     return fail(CKV_ENOSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
   return CKV_OK;
@@ -306,7 +309,8 @@ int ckv_cluster_commit(ckv_layer* L) {
 namespace {
 
 int select_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
-                void* ws, size_t ws_bytes, void* stream, const uint16_t* k_new, const uint16_t* v_new) {
+                void* ws, size_t ws_bytes, void* stream, const uint16_t* k_new, const uint16_t* v_new,
+                bool per_head = false) {
   int rc = check_layer(L);
   if (rc) return rc;
   if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
@@ -321,16 +325,58 @@ int select_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* 
     if (rc) return rc;
     if (L->n_total >= L->capacity) return fail(CKV_ENOSPACE, "cache full (capacity %d)", L->capacity);
   }
-  rc = check_ws(L, ws, ws_bytes);
+  rc = check_ws(L, ws, ws_bytes, per_head);
   if (rc) return rc;
-  const Layout w = layout_of(L);
+  const Layout w = layout_of(L, per_head);
   const int units = L->batch * L->n_kv_heads;
+  const int sets = units * (per_head ? L->group : 1);
   hipError_t e = ckv::launch_select(q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_clu,
                                     L->capacity - L->n_sink, budget, sel_pos, sel_count,
                                     (float*)((char*)ws + w.off_scores), (uint32_t*)((char*)ws + w.off_cut),
-                                    (uint32_t*)ws + units, k_new, v_new, L->k_tok, L->v_tok, L->capacity,
-                                    L->n_total, units, (hipStream_t)stream);
+                                    (uint32_t*)ws + sets, k_new, v_new, L->k_tok, L->v_tok, L->capacity,
+                                    L->n_total, units, per_head ? 1 : 0, (hipStream_t)stream);
   return hip_status(e, "select");
+}
+
+int decode_impl(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, const int32_t* sel_count,
+                int32_t budget, float* out, void* ws, size_t ws_bytes, void* stream, bool per_head) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
+  if (L->n_clustered < L->n_sink)
+    return fail(CKV_EINVAL, "n_clustered %d < n_sink %d: cluster the prefix first", L->n_clustered, L->n_sink);
+  rc = check_ptrs("q,k_tok,v_tok,sel_count,out", 5, q, L->k_tok, L->v_tok, sel_count, out);
+  if (rc) return rc;
+  const int m = clustered_tokens(L) > 0 ? clustered_tokens(L) : 0;
+  const int cmax = budget < m ? budget : m;
+  if (cmax > 0) {
+    rc = check_ptrs("sel_pos,k_clu,v_clu", 3, sel_pos, L->k_clu, L->v_clu);
+    if (rc) return rc;
+  }
+  rc = check_ws(L, ws, ws_bytes, per_head);
+  if (rc) return rc;
+  const int units = L->batch * L->n_kv_heads;
+  const int sets = units * (per_head ? L->group : 1);
+  const long long rmax = (long long)L->n_sink + cmax + (L->n_total - L->n_clustered);
+  // Split-K: about kDecodeTargetWgs workgroups per launch (all resident at once
+  // on 256 CUs), chunks of whole 16-row steps, at most kMaxChunks per unit.
+#ifndef CKV_DEC_TARGET_WGS
+#define CKV_DEC_TARGET_WGS 256
+#endif
+  const long long target = CKV_DEC_TARGET_WGS;
+  long long chunk = (rmax * sets + target - 1) / target;
+  const long long min_chunk = (rmax + ckv::kMaxChunks - 1) / ckv::kMaxChunks;
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (chunk < 64) chunk = 64;
+  chunk = (chunk + 15) / 16 * 16;
+  long long n_chunks = (rmax + chunk - 1) / chunk;
+  if (n_chunks < 1) n_chunks = 1;
+  const Layout w = layout_of(L, per_head);
+  hipError_t e = ckv::launch_sparse_decode(
+      q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
+      sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
+      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, out, units, per_head ? 1 : 0, (hipStream_t)stream);
+  return hip_status(e, "sparse_decode");
 }
 
 }  // namespace
@@ -352,44 +398,30 @@ int ckv_append_select(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new
   return CKV_OK;
 }
 
+
 int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, const int32_t* sel_count,
                       int32_t budget, float* out, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_layer(L);
-  if (rc) return rc;
-  if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
-  if (L->n_clustered < L->n_sink)
-    return fail(CKV_EINVAL, "n_clustered %d < n_sink %d: cluster the prefix first", L->n_clustered, L->n_sink);
-  rc = check_ptrs("q,k_tok,v_tok,sel_count,out", 5, q, L->k_tok, L->v_tok, sel_count, out);
-  if (rc) return rc;
-  const int m = clustered_tokens(L) > 0 ? clustered_tokens(L) : 0;
-  const int cmax = budget < m ? budget : m;
-  if (cmax > 0) {
-    rc = check_ptrs("sel_pos,k_clu,v_clu", 3, sel_pos, L->k_clu, L->v_clu);
-    if (rc) return rc;
+  return decode_impl(L, q, sel_pos, sel_count, budget, out, ws, ws_bytes, stream, false);
+}
+
+size_t ckv_workspace_bytes_per_head(const ckv_layer* L, int32_t max_budget) {
+  if (check_layer(L)) return 0;
+  if (max_budget < 0) {
+    fail(CKV_EINVAL, "max_budget %d < 0", max_budget);
+    return 0;
   }
-  rc = check_ws(L, ws, ws_bytes);
-  if (rc) return rc;
-  const int units = L->batch * L->n_kv_heads;
-  const long long rmax = (long long)L->n_sink + cmax + (L->n_total - L->n_clustered);
-  // Split-K: about kDecodeTargetWgs workgroups per launch (all resident at once
-  // on 256 CUs), chunks of whole 16-row steps, at most kMaxChunks per unit.
-#ifndef CKV_DEC_TARGET_WGS
-#define CKV_DEC_TARGET_WGS 256
-#endif
-  const long long target = CKV_DEC_TARGET_WGS;
-  long long chunk = (rmax * units + target - 1) / target;
-  const long long min_chunk = (rmax + ckv::kMaxChunks - 1) / ckv::kMaxChunks;
-  if (chunk < min_chunk) chunk = min_chunk;
-  if (chunk < 64) chunk = 64;
-  chunk = (chunk + 15) / 16 * 16;
-  long long n_chunks = (rmax + chunk - 1) / chunk;
-  if (n_chunks < 1) n_chunks = 1;
-  const Layout w = layout_of(L);
-  hipError_t e = ckv::launch_sparse_decode(
-      q, L->group, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu, L->capacity - L->n_sink, sel_pos,
-      sel_count, budget, m, L->n_sink, L->n_clustered, L->n_total, (int)chunk, (int)n_chunks,
-      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, out, units, (hipStream_t)stream);
-  return hip_status(e, "sparse_decode");
+  return layout_of(L, true).total;
+}
+
+int ckv_select_per_head(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                        int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  return select_impl(L, q, budget, sel_pos, sel_count, ws, ws_bytes, stream, nullptr, nullptr, true);
+}
+
+int ckv_sparse_decode_per_head(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos,
+                               const int32_t* sel_count, int32_t budget, float* out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return decode_impl(L, q, sel_pos, sel_count, budget, out, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const uint16_t* __restrict__ v_clu, int clu_stride, const int32_t* __restrict__ sel_pos,
     const int32_t* __restrict__ sel_count, int budget, int m, int n_sink, int n_clustered,
     int n_total, int chunk_rows, int n_chunks, float* __restrict__ partials, uint32_t* __restrict__ counters,
-    float* __restrict__ out) {
+    float* __restrict__ out, int hs) {
   // ring | row sources; the per-wave merge area reuses both afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kRingBytes + kRowSegment * 4];
   static_assert(kDecWaves * GT * kPartialStride * 4 <= kRingBytes + kRowSegment * 4,
@@ -141,7 +141,11 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   int* rowsrc = reinterpret_cast<int*>(smem + kRingBytes);
   float* red = reinterpret_cast<float*>(smem);
 
+  // attention set u (its queries, recalled positions, partials and output) of
+  // physical unit up = u / hs: hs = 1 (one set per KV head shared by its G
+  // query heads) or hs = G (one set per query head, G passed as 1)
   const int u = blockIdx.x / n_chunks;
+  const int up = u / hs;
   const int c = blockIdx.x % n_chunks;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -171,10 +175,10 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* ktu = k_tok + (size_t)u * capacity * kHeadDim;
-  const uint16_t* vtu = v_tok + (size_t)u * capacity * kHeadDim;
-  const uint16_t* kcu = k_clu + (size_t)u * clu_stride * kHeadDim;
-  const uint16_t* vcu = v_clu + (size_t)u * clu_stride * kHeadDim;
+  const uint16_t* ktu = k_tok + (size_t)up * capacity * kHeadDim;
+  const uint16_t* vtu = v_tok + (size_t)up * capacity * kHeadDim;
+  const uint16_t* kcu = k_clu + (size_t)up * clu_stride * kHeadDim;
+  const uint16_t* vcu = v_clu + (size_t)up * clu_stride * kHeadDim;
   const int32_t* sp = sel_pos + (size_t)u * budget;
   unsigned char* ring = smem + wave * kSlots * kTileBytes;
   const uint32_t ring_base = lds_addr(ring);
@@ -454,13 +458,17 @@ hipError_t launch_sparse_decode(const uint16_t* q, int G, const uint16_t* k_tok,
                                 const uint16_t* v_clu, int clu_stride, const int32_t* sel_pos,
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
-                                float* partials, uint32_t* counters, float* out, int units, hipStream_t s) {
-  const dim3 grid((unsigned)(units * n_chunks));
-#define CKV_DEC(GTV)                                                                                \
-  hipLaunchKernelGGL(sparse_decode_kernel<GTV>, grid, dim3(kDecThreads), 0, s, q, G, k_tok, v_tok, \
-                     capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m, n_sink,     \
-                     n_clustered, n_total, chunk_rows, n_chunks, partials, counters, out)
-  switch (group_tier(G)) {
+                                float* partials, uint32_t* counters, float* out, int units, int per_head,
+                                hipStream_t s) {
+  // per_head: G attention sets per unit, one per query head, each with its own recalled positions
+  const int hs = per_head ? G : 1;
+  const int Ge = per_head ? 1 : G;
+  const dim3 grid((unsigned)(units * hs * n_chunks));
+#define CKV_DEC(GTV)                                                                                 \
+  hipLaunchKernelGGL(sparse_decode_kernel<GTV>, grid, dim3(kDecThreads), 0, s, q, Ge, k_tok, v_tok, \
+                     capacity, k_clu, v_clu, clu_stride, sel_pos, sel_count, budget, m, n_sink,      \
+                     n_clustered, n_total, chunk_rows, n_chunks, partials, counters, out, hs)
+  switch (group_tier(Ge)) {
     case 1: CKV_DEC(1); break;
     case 2: CKV_DEC(2); break;
     case 4: CKV_DEC(4); break;

@@ -55,7 +55,7 @@ hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
                          int budget, int32_t* sel_pos, int32_t* sel_count, float* scores_ws,
                          uint32_t* cut_ws, uint32_t* counters, const uint16_t* k_new,
                          const uint16_t* v_new, uint16_t* k_tok, uint16_t* v_tok, int capacity, int row,
-                         int units, hipStream_t s);
+                         int units, int per_head, hipStream_t s);
 
 // Split-K sparse decode streaming rows through per-wave LDS rings; the last
 // chunk of each unit merges the chunk partials.  counters[units] must be zero
@@ -66,7 +66,7 @@ hipError_t launch_sparse_decode(const uint16_t* q, int group, const uint16_t* k_
                                 const int32_t* sel_count, int budget, int m, int n_sink,
                                 int n_clustered, int n_total, int chunk_rows, int n_chunks,
                                 float* partials, uint32_t* counters, float* out, int units,
-                                hipStream_t s);
+                                int per_head, hipStream_t s);
 
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok,
                          uint16_t* v_tok, int capacity, int row, int units, hipStream_t s);

@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count, float* __restrict__ scores_ws,
     uint32_t* __restrict__ cut_ws, uint32_t* __restrict__ counters, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_tok, uint16_t* __restrict__ v_tok, int capacity,
-    int row) {
+    int row, int hs) {
   __shared__ __attribute__((aligned(16))) uint32_t key[kMaxClusters];
   __shared__ __attribute__((aligned(16))) float csc[kMaxClusters];
   __shared__ __attribute__((aligned(16))) int sz[kMaxClusters];
@@ -407,7 +407,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ __attribute__((aligned(16))) SelScratch ws;
   __shared__ int sh_cut, sh_need, sh_last;
 
-  const int u = blockIdx.x / kSelSplit;
+  // selection v of physical unit u: hs = 1 (one recall per KV head, q_bar over
+  // its G query heads) or hs = G (one recall per query head, G passed as 1)
+  const int v = blockIdx.x / kSelSplit;
+  const int u = v / hs;
   const int part = blockIdx.x % kSelSplit;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   static_assert(kSelGroups * kRowsInFlight * kSelSplit >= kMaxClusters, "one round covers K");
   const int j_lo = part * K / kSelSplit, j_hi = (part + 1) * K / kSelSplit;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
-  float* sc_u = scores_ws + (size_t)u * K;
+  float* sc_u = scores_ws + (size_t)v * K;
   float qb[8];
   {
     float4 a[kRowsInFlight][2];
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       }
     }
     // the query sum while the centroid rows are in flight
-    qbar8(q, u, G, li, qb);
+    qbar8(q, v, G, li, qb);
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j_lo + grp + t * kSelGroups;
@@ -465,12 +468,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&counters[v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_last = prev == (uint32_t)(kSelSplit - 1) ? 1 : 0;
   }
   lds_barrier();
   if (!sh_last) return;
-  if (tid == 0) __hip_atomic_store(&counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(&counters[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   ws.bw[tid] = 0;
   ws.bc[tid] = 0;
   {
@@ -564,8 +567,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   constexpr int kCutGroups = kCutWaves * (kWave / 16);
   constexpr int kCutRows = 8;
   const uint16_t* kc = k_clu + ((size_t)u * clu_stride + lo_cut) * kHeadDim + li * 8;
-  uint32_t* cut_keys_g = cut_ws + (size_t)u * clu_stride;
-  int32_t* out = sel_pos + (size_t)u * budget;
+  uint32_t* cut_keys_g = cut_ws + (size_t)v * clu_stride;
+  int32_t* out = sel_pos + (size_t)v * budget;
   if (wave < kCutWaves) {
     float mn = INFINITY, mx = -INFINITY;
     for (int r0 = 0; r0 < n_cut; r0 += kCutRows * kCutGroups) {
@@ -652,17 +655,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
 
-  if (tid == 0) sel_count[u] = beff;
+  if (tid == 0) sel_count[v] = beff;
 }
 
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean, const int32_t* offsets,
                          int K, const uint16_t* k_clu, int clu_stride, int budget, int32_t* sel_pos,
                          int32_t* sel_count, float* scores_ws, uint32_t* cut_ws, uint32_t* counters,
                          const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok, uint16_t* v_tok,
-                         int capacity, int row, int units, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * kSelSplit)), dim3(kSelThreads), 0, s, q, group,
-                     cmean, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count, scores_ws, cut_ws,
-                     counters, k_new, v_new, k_tok, v_tok, capacity, row);
+                         int capacity, int row, int units, int per_head, hipStream_t s) {
+  // per_head: one recall per query head (group selections per unit, each from its own q_g)
+  const int hs = per_head ? group : 1;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * hs * kSelSplit)), dim3(kSelThreads), 0, s, q,
+                     per_head ? 1 : group, cmean, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count,
+                     scores_ws, cut_ws, counters, k_new, v_new, k_tok, v_tok, capacity, row, hs);
   return hipGetLastError();
 }
 

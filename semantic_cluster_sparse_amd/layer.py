@@ -21,7 +21,7 @@ def _stream() -> int:
 
 class Layer:
     def __init__(self, batch: int, n_kv_heads: int, group: int, n_clusters: int, capacity: int,
-                 n_sink: int = 16, max_budget: int = 2048, incremental: bool = True,
+                 n_sink: int = 16, max_budget: int = 2048, incremental: bool = True, per_head: bool = False,
                  device: str | torch.device = "cuda"):
         self.device = torch.device(device)
         self.units = batch * n_kv_heads
@@ -54,7 +54,9 @@ class Layer:
             batch=batch, n_kv_heads=n_kv_heads, group=group, head_dim=HEAD_DIM, n_sink=n_sink,
             n_clusters=n_clusters, capacity=capacity, n_total=0, n_clustered=0, n_pending=0)
         self._bind()
-        self.ws_bytes = ckv.ckv_workspace_bytes(self.struct, max_budget)
+        # a per-query-head workspace also serves every other call
+        self.ws_bytes = (ckv.ckv_workspace_bytes_per_head if per_head else ckv.ckv_workspace_bytes)(
+            self.struct, max_budget)
         self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=self.device)
         ckv.ckv_workspace_init(self.ws.data_ptr(), self.ws_bytes, _stream())
         self.ws_bg = None
@@ -143,3 +145,18 @@ class Layer:
         assert out.numel() == self.units * self.group * HEAD_DIM
         ckv.ckv_sparse_decode(self.struct, q.data_ptr(), sel_pos.data_ptr(), sel_count.data_ptr(),
                               budget, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def select_per_head(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor,
+                        sel_count: torch.Tensor) -> None:
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * self.group * budget
+        assert sel_count.numel() >= self.units * self.group
+        ckv.ckv_select_per_head(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
+                                self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def sparse_decode_per_head(self, q: torch.Tensor, sel_pos: torch.Tensor, sel_count: torch.Tensor,
+                               budget: int, out: torch.Tensor) -> None:
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        assert out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_sparse_decode_per_head(self.struct, q.data_ptr(), sel_pos.data_ptr(), sel_count.data_ptr(),
+                                       budget, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())

@@ -269,6 +269,57 @@ def test_select_teacher_forced():
         say(f"  budget {budget}: ok")
 
 
+def test_per_head_recall_and_decode():
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    budget = 1024
+    say(f"case: per-query-head recall + decode, Llama layer shape, units 0-3, G={cfg.group}, budget {budget}")
+    units = [0, 1, 2, 3]
+    U = len(units)
+    k, v, cen = synth.make_layer_inputs(cfg, units=units)
+    init = synth.make_init_indices(cfg.init_seed, U, cfg.m, cfg.n_clusters)
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, 2, v_bits=v[u])
+              for u in range(U)]
+    q = synth.make_queries(cfg.query_seed, cen, cfg.group)
+    Lh = Layer(batch=U, n_kv_heads=1, group=cfg.group, n_clusters=cfg.n_clusters, capacity=cfg.n_tokens,
+               max_budget=budget, incremental=False, per_head=True)
+    Lh.k_tok.copy_(dev_bf16(k))
+    Lh.v_tok.copy_(dev_bf16(v))
+    load_state(Lh, states)
+    Lh.set_counters(cfg.n_tokens, cfg.n_tokens)
+    qd = dev_bf16(q)
+    S = U * cfg.group
+    sel_pos = torch.full((S, budget), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((U, cfg.group, D), dtype=torch.float32, device="cuda")
+    Lh.select_per_head(qd, budget, sel_pos, cnt)
+    Lh.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    assert np.all(cn == budget)
+    distinct = 0
+    for u in range(U):
+        st = states[u]
+        mu32 = st["cmean"].astype(np.float32).astype(np.float64)
+        sels = pipeline.select_per_head(q[u], mu32, st["csize"], st["offsets"], st["k_clu_bits"], budget)
+        ok = True
+        for g in range(cfg.group):
+            pos_g = sp[u * cfg.group + g, :budget]
+            assert np.all(np.diff(pos_g) > 0)
+            if not np.array_equal(pos_g, sels[g]["positions"]):
+                gap = selection_boundary_gap(sels[g], bf16.widen(st["k_clu_bits"]), st["offsets"])
+                say(f"  unit {u} head {g}: recall differs, boundary gap {gap:.3g}")
+                assert gap <= SELECT_GAP
+                ok = False
+        distinct += len({tuple(x["positions"].tolist()) for x in sels}) > 1
+        if ok:
+            ref = pipeline.decode_per_head(q[u], k[u], v[u], st["k_clu_bits"], st["v_clu_bits"],
+                                           [x["positions"] for x in sels], 16, cfg.n_tokens, cfg.n_tokens)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: per-head decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+    assert distinct > 0, "the heads of every unit recalled the same set: the case does not exercise the mode"
+
+
 # ------------------------------------------------------------------ decode
 
 
