@@ -248,7 +248,9 @@ int ckv_sparse_decode_per_head(const ckv_layer* L, const uint16_t* q, const int3
  * [batch, n_kv_heads * group, 128] (device, written); an empty S gives 0.
  * sel_count[u] must be <= min(budget, m) and every listed position < m.
  * The first 4 * units bytes of the workspace are per-unit arrival counters of
- * the split-K merge; a call leaves them zero, as ckv_workspace_init does.
+ * the split-K merge; a call leaves them zero, as ckv_workspace_init does.  The
+ * workspace starts with 8 * units * group bytes of such counters for every call
+ * (both recall modes); clustering calls never write them.
  */
 int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos,
                       const int32_t* sel_count, int32_t budget, float* out, void* ws,

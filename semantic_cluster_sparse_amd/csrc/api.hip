@@ -56,7 +56,11 @@ Layout layout_of(const ckv_layer* L, bool per_head = false) {
   const size_t clu_cap = (size_t)(L->capacity - L->n_sink);
   const size_t tiles = (clu_cap + ckv::kSortTile - 1) / ckv::kSortTile;
   Layout w;
-  w.counters = align256(sets * 2 * sizeof(uint32_t));
+  // Arrival counters of both recall modes (decode at [0, sets), recall at
+  // [sets, 2 sets)), sized for the per-query-head count whatever the mode, so
+  // that the bodies below never overlap the counters of either mode when calls
+  // of both modes share one workspace.
+  w.counters = align256(units * (size_t)L->group * 2 * sizeof(uint32_t));
   w.hist = align256(units * tiles * L->n_clusters * sizeof(int32_t));
   w.invn = align256(units * clu_cap * sizeof(double));
   w.scores = align256(sets * L->n_clusters * sizeof(float));

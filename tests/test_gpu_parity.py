@@ -320,6 +320,49 @@ def test_per_head_recall_and_decode():
     assert distinct > 0, "the heads of every unit recalled the same set: the case does not exercise the mode"
 
 
+def test_per_head_after_prefill_many_units():
+    # 64 units x 4 heads: the per-head arrival counters reach past the per-KV-head ones, and the
+    # prefill on the same workspace must not disturb them (every set must come back full)
+    U, G, K, n, budget, iters = 64, 4, 40, 16 + 3000, 512, 2
+    say(f"case: per-query-head recall after a prefill on the same workspace, {U} units x {G} heads")
+    ks, vs, cs = [], [], []
+    for u in range(U):
+        kb, vb, c = synth.make_unit_inputs(131, u, n, 48)
+        ks.append(kb), vs.append(vb), cs.append(c)
+    k, v, cen = np.stack(ks), np.stack(vs), np.stack(cs)
+    init = synth.make_init_indices(132, U, n - 16, K)
+    q = synth.make_queries(133, cen, G)
+    L = Layer(batch=U, n_kv_heads=1, group=G, n_clusters=K, capacity=n, max_budget=budget, incremental=False,
+              per_head=True)
+    L.k_tok.copy_(dev_bf16(k))
+    L.v_tok.copy_(dev_bf16(v))
+    L.prefill(n, iters, to_dev(init, torch.int32))
+    sel_pos = torch.full((U * G, budget), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((U * G,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((U, G, D), dtype=torch.float32, device="cuda")
+    qd = dev_bf16(q)
+    for _ in range(2):              # twice: the counters must come back to zero
+        L.select_per_head(qd, budget, sel_pos, cnt)
+        L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    cn, sp, og = cnt.cpu().numpy(), sel_pos.cpu().numpy(), out.cpu().numpy()
+    assert np.all(cn == budget), f"{int((cn != budget).sum())} sets came back short"
+    assert np.all(np.diff(sp, axis=1) > 0)
+    for u in (0, 37, 63):
+        ora = pipeline.prefill_unit(k[u], n, init[u], K, iters, v_bits=v[u], history=True)
+        x = bf16.widen(k[u][16:n])
+        if check_state(L, u, ora, x, ora["history"][-2][1], tag="ph") > 0:
+            continue
+        sels = pipeline.select_per_head(q[u], ora["cmean"].astype(np.float32).astype(np.float64), ora["csize"],
+                                        ora["offsets"], ora["k_clu_bits"], budget)
+        if all(np.array_equal(sp[u * G + g], sels[g]["positions"]) for g in range(G)):
+            ref = pipeline.decode_per_head(q[u], k[u], v[u], ora["k_clu_bits"], ora["v_clu_bits"],
+                                           [x_["positions"] for x_ in sels], 16, n, n)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: per-head decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+
+
 # ------------------------------------------------------------------ decode
 
 
