@@ -618,6 +618,38 @@ def test_edge_zero_and_duplicate_keys(K, T):
         compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
 
 
+@pytest.mark.parametrize("n_sink", [0, 16])
+def test_edge_every_key_its_own_cluster(n_sink):
+    # K = m: every clustered key starts as its own direction; with no sinks, token 0 is clustered too
+    m = 300
+    n = n_sink + m
+    K, T, G = m, 2, 2
+    say(f"case: K = m = {m}, n_sink = {n_sink}, {T} rounds, recall + decode")
+    kb, vb, cen = synth.make_unit_inputs(141, 0, n, 24)
+    init = np.arange(m, dtype=np.int32)
+    ora = pipeline.prefill_unit(kb, n, init, K, T, n_sink=n_sink, v_bits=vb, history=True)
+    L = gpu_layer(kb[None], vb[None], G, K, n_sink=n_sink)
+    L.prefill(n, T, to_dev(init[None], torch.int32))
+    torch.cuda.synchronize()
+    x = bf16.widen(kb[n_sink:n])
+    assert check_state(L, 0, ora, x, ora["history"][-2][1], n_sink=n_sink, tag="K=m") == 0
+    q = synth.make_queries(142, cen[None], G)
+    for budget in (1, 37, m):
+        sel_pos = torch.zeros((1, budget), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        out = torch.zeros((1, G, D), dtype=torch.float32, device="cuda")
+        L.select(dev_bf16(q), budget, sel_pos, cnt)
+        L.sparse_decode(dev_bf16(q), sel_pos, cnt, budget, out)
+        torch.cuda.synchronize()
+        sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+        if compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget) == 0:
+            ref = pipeline.decode_unit(q[0], kb, vb, ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
+                                       n_sink, n, n)
+            err = np.abs(out.cpu().numpy()[0] - ref).max()
+            say(f"  budget {budget}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+
+
 def test_determinism():
     say("case: bitwise determinism of prefill, select, decode")
     cfg = synth.CONFIGS["single-head-2k"]
