@@ -17,10 +17,13 @@
 // index).  The partial fill inside the cut cluster is the same selection with
 // unit weights over the q_bar.k scores of its tokens.  A crossing bucket with
 // more than 64 members, or a degenerate score range, falls back to a
-// wave-synchronous weighted radix select on the keys.  One workgroup of 1024
-// threads per unit; the barriers wait on LDS only, so global loads stay in
-// flight across them.  Recalled positions are written by whole waves, 64
-// consecutive slots per store instruction.
+// wave-synchronous weighted radix select on the keys.  Four workgroups of
+// 1024 threads per recalled set each score a quarter of the clusters; the
+// last of them to finish (device-scope arrival counter) makes the selection.
+// A set is one KV head's recall (q_bar over its G query heads) or, in the
+// per-query-head mode, one query head's (q_g alone).  The barriers wait on LDS
+// only, so global loads stay in flight across them.  Recalled positions are
+// written by whole waves, 64 consecutive slots per store instruction.
 #include "common.hpp"
 #include "launch.hpp"
 
