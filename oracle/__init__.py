@@ -38,7 +38,13 @@ and the Gaussian closed form of the centroid approximation (§3.1);
 total-order formulation, exact count, prefix property, budget >= m;
 ``attention.attend`` -- torch's float64 SDPA, |S| = 1, q = 0, order and shift
 invariance, a hand-worked golden example; ``kmeans.incremental`` --
-brute-force assignment and from-scratch recomputation of the running sums.
+brute-force assignment and from-scratch recomputation of the running sums;
+``kmeans.drift`` -- the brute-force mean distance over the members, identical
+and antipodal members; ``kmeans.split`` -- two planted groups separated
+exactly, no change above the largest drift or without an empty slot, the most
+drifted cluster served first, drift ties, seed ties, label and size
+invariants; reserved slots -- Lloyd with reserves equals Lloyd without them
+when no key is an outlier, and an outlier lands in the reserve.
 """
 
 from . import bf16, kmeans, select, attention, pipeline  # noqa: F401

@@ -27,6 +27,9 @@ Readings taken where the pages are silent:
 * Incremental pass: the new keys are assigned to the current directions, then
   folded into ``S``, ``M``, ``n``; the touched clusters' directions and means
   are refreshed; old tokens are never reassigned and ``K`` does not change.
+* Drift split (``split``): ``K`` is a slot count; a split moves part of a
+  drifted cluster into an empty slot.  Prefill may leave slots empty on
+  purpose (init index -1, zero direction).
 """
 
 from __future__ import annotations
@@ -87,9 +90,20 @@ def directions(S: np.ndarray, n: np.ndarray, prev: np.ndarray, round_bf16: bool 
 
 
 def init_directions(x: np.ndarray, init_idx: np.ndarray, round_bf16: bool = True):
-    """Initial directions from the caller's distinct indices into the clustered keys."""
-    xh = normalise(x[np.asarray(init_idx, np.int64)])
-    return bf16.round_value(xh) if round_bf16 else xh
+    """Initial directions from the caller's distinct indices into the clustered keys.
+
+    An index of -1 reserves the slot: its direction is the zero vector, which
+    scores exactly 0 against every key, so the slot stays empty unless some
+    key's best score against the live directions is negative (an outlier,
+    which then gets the slot).  Reserved slots are where ``split`` puts the
+    halves it creates.
+    """
+    idx = np.asarray(init_idx, np.int64)
+    out = np.zeros((len(idx), x.shape[1]))
+    live = idx >= 0
+    xh = normalise(x[idx[live]])
+    out[live] = bf16.round_value(xh) if round_bf16 else xh
+    return out
 
 
 def objective(x: np.ndarray, a: np.ndarray, cdir: np.ndarray) -> float:
@@ -172,3 +186,81 @@ def incremental(state: dict, x_new: np.ndarray, round_bf16: bool = True) -> dict
     c[touched] = upd[touched]
     return dict(assign=np.concatenate([np.asarray(state["assign"], np.int64), a_new]),
                 cdir=c, csum=S, msum=M, csize=n, new_assign=a_new)
+
+
+def drift(S: np.ndarray, n: np.ndarray) -> np.ndarray:
+    """Mean cosine distance of each cluster's members to its centre direction.
+
+    The drift test of the ClusterKV article (§3.2, decoding-phase updates)
+    compares a cluster's mean intra-cluster distance with a threshold.  Under
+    cosine distance to the exact centre direction ``S_j / |S_j|`` that mean is
+    ``(1/n_j) sum_i (1 - x^_i . S_j/|S_j|) = 1 - |S_j| / n_j`` because the
+    members' unit keys sum to ``S_j``.  It lies in [0, 1]; NaN for an empty
+    cluster.
+    """
+    S = np.asarray(S, np.float64)
+    n = np.asarray(n, np.int64)
+    out = np.full(len(n), np.nan)
+    nz = n > 0
+    out[nz] = 1.0 - np.sqrt(np.sum(S[nz] * S[nz], axis=1)) / n[nz]
+    return out
+
+
+def split(state: dict, x: np.ndarray, threshold: float, round_bf16: bool = True) -> dict:
+    """Drift-triggered split (ClusterKV article §3.2: a cluster whose mean
+    intra-cluster distance exceeds a threshold is split).
+
+    ``state`` holds ``assign`` (labels of the clustered keys ``x`` [m, d], in
+    token order), ``cdir``, ``csum`` and ``csize``; the number of clusters
+    stays ``K`` (the slot count).  Readings taken where the article is silent:
+
+    * drift is ``drift(S, n)``; a cluster is a candidate when it has at least
+      two members and its drift is strictly above ``threshold``;
+    * a split needs an empty slot (``n_f = 0``: a reserved slot, or a cluster
+      that K-means left empty).  Candidates in decreasing drift (ties: smaller
+      index) are paired with the empty slots in increasing index, as far as the
+      slots go;
+    * splitting ``j`` into ``f``: the seed is the member whose cosine to the
+      current direction ``c~_j`` is smallest (ties: earliest token); ``f``
+      gets the direction ``bf16(x^_seed)``; every member of ``j`` then takes
+      the cosine argmax between ``c~_j`` and that seed direction (ties: the
+      smaller slot index).  One such round, members of other clusters are not
+      moved;
+    * afterwards the sums, sizes and directions of every cluster are those of
+      the new labels (an empty cluster keeps its previous direction).
+
+    Cosines and scores are float64 dot products of bfloat16 values (exact
+    products); the decisions are taken on those values.  Returns the new
+    state plus ``pairs`` [(j, f)] and ``seeds`` (token-order index of each
+    pair's seed).
+    """
+    x = np.asarray(x, np.float64)
+    a = np.asarray(state["assign"], np.int64).copy()
+    c = np.asarray(state["cdir"], np.float64)
+    n = np.asarray(state["csize"], np.int64)
+    k = c.shape[0]
+    dr = drift(state["csum"], n)
+    cands = [j for j in range(k) if n[j] >= 2 and dr[j] > threshold]
+    cands.sort(key=lambda j: (-dr[j], j))
+    free = [j for j in range(k) if n[j] == 0]
+    pairs = list(zip(cands, free))
+    seeds = []
+    norms = np.sqrt(np.sum(x * x, axis=1))
+    for j, f in pairs:
+        members = np.flatnonzero(a == j)
+        xm = x[members]
+        cos = np.zeros(len(members))
+        nz = norms[members] > 0
+        cos[nz] = (xm[nz] @ c[j]) / norms[members][nz]
+        seed = int(members[int(np.argmin(cos))])
+        seeds.append(seed)
+        cf = normalise(x[seed:seed + 1])[0]
+        if round_bf16:
+            cf = bf16.round_value(cf)
+        lo, hi = (j, f) if j < f else (f, j)
+        two = np.stack([c[lo], cf] if lo == j else [cf, c[hi]])
+        pick = np.argmax(xm @ two.T, axis=1)
+        a[members] = np.where(pick == 0, lo, hi)
+    S, M, n_new = unit_sums(x, a, k)
+    c_new = directions(S, n_new, c, round_bf16)
+    return dict(assign=a, cdir=c_new, csum=S, msum=M, csize=n_new, pairs=pairs, seeds=seeds, drift=dr)

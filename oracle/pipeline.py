@@ -61,6 +61,26 @@ def incremental_unit(state: dict, k_bits: np.ndarray, n_total: int,
     return out
 
 
+def split_unit(state: dict, k_bits: np.ndarray, threshold: float, n_sink: int = kmeans.N_SINK,
+               v_bits: np.ndarray | None = None) -> dict:
+    """Drift-triggered split of the clusters of tokens ``[n_sink, state['n_clustered'])``
+    (ClusterKV article §3.2), then the cluster-contiguous index and rows (§4.1)."""
+    n = state["n_clustered"]
+    x = bf16.widen(k_bits[n_sink:n])
+    out = kmeans.split(state, x, threshold)
+    k = out["cdir"].shape[0]
+    perm, offsets = kmeans.build_index(out["assign"], k, n_sink)
+    out["cdir_bits"] = bf16.round_rne(out["cdir"])
+    out["cmean"] = kmeans.scoring_centroids(out["msum"], out["csize"])
+    out["perm"] = perm
+    out["offsets"] = offsets
+    out["k_clu_bits"] = np.asarray(k_bits)[perm]
+    if v_bits is not None:
+        out["v_clu_bits"] = np.asarray(v_bits)[perm]
+    out["n_clustered"] = n
+    return out
+
+
 def select_unit(q_bits: np.ndarray, cmean: np.ndarray, csize, offsets,
                 k_clu_bits: np.ndarray, budget: int) -> dict:
     """Recall for one unit: ``q_bits`` [G, d] bf16 bits, ``cmean`` float values."""
