@@ -116,7 +116,9 @@ int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   init     c_j = bf16(x_I(j) / |x_I(j)|) with I = init_idx[u, :] -- K distinct
  *            indices in [0, m) into the clustered tokens, drawn by the caller
  *            (device int32 [units, K]); an index outside [0, m) gives a zero
- *            direction;
+ *            direction: -1 holds slot j in reserve for ckv_cluster_split (a
+ *            zero direction scores 0 against every key, so the slot stays
+ *            empty unless a key scores below 0 against every other direction);
  *   iters rounds of: a_i = argmax_j x_i . c_j (ties -> smallest j);
  *            S_j = sum of unit keys of members; c_j = bf16_rne(S_j / |S_j|)
  *            (empty or zero-sum clusters keep c_j);
@@ -183,6 +185,33 @@ int ckv_cluster_incremental_async(ckv_layer* L, void* ws, size_t ws_bytes, void*
  * the other stream).  CKV_EINVAL if nothing is pending.
  */
 int ckv_cluster_commit(ckv_layer* L);
+
+/*
+ * Drift-triggered split (ClusterKV article §3.2, decoding-stage updates: a
+ * cluster whose mean intra-cluster distance passes a threshold is split).
+ * Per unit, over the clustered tokens [n_sink, n_clustered):
+ *   drift_j  = 1 - |csum_j| / csize_j, the mean cosine distance of the members
+ *              to the centre direction csum_j / |csum_j| (in [0, 1]);
+ *   pairs    clusters with csize_j >= 2 and drift_j > threshold, in decreasing
+ *              drift (ties -> smaller j), are paired with the empty slots
+ *              (csize_f == 0) in increasing f, as far as the empty slots go;
+ *   split    the member of j with the smallest cosine to c_j (ties -> earliest
+ *              token) gives c_f = bf16_rne(x / |x|); each member of j moves to
+ *              f when x . c_f > x . c_j (>= when f < j).
+ * These dot products and cosines are f64 over the bf16 values.  Then, as after
+ * the last prefill round, assign, csize, offsets, perm, csum, msum, cmean, cdir
+ * (nonempty clusters; an empty one keeps its direction) and k_clu / v_clu are
+ * rewritten in place from the labels of all clustered tokens.  Clusters no
+ * split touched keep their members; their sums are added again in another
+ * order and may change in the last bits.
+ * Empty slots come from prefill (init_idx -1) or from clusters K-means left
+ * empty; without one nothing splits.  The caller picks threshold (any non-NaN
+ * value) and when to call (e.g. after each incremental pass).  Requires the
+ * state of a prefill or incremental call and n_pending == 0 (CKV_EINVAL
+ * otherwise); no other call on the layer may run meanwhile on another stream.
+ * n_total and n_clustered are unchanged.
+ */
+int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Cluster-granularity recall (ClusterKV article §3.3; GQA reading: one recall

@@ -18,6 +18,7 @@ from .ckv import (  # noqa: F401
     ckv_cluster_incremental,
     ckv_cluster_incremental_async,
     ckv_cluster_prefill,
+    ckv_cluster_split,
     ckv_last_error,
     ckv_select,
     ckv_select_per_head,

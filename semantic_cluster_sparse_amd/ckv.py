@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_int, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_double, c_int, c_int32, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_lib", "libckv.so")
@@ -84,6 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_cluster_incremental_async.argtypes = [LP, c_void_p, c_size_t, c_void_p]
     lib.ckv_cluster_commit.restype = c_int
     lib.ckv_cluster_commit.argtypes = [LP]
+    lib.ckv_cluster_split.restype = c_int
+    lib.ckv_cluster_split.argtypes = [LP, c_double, c_void_p, c_size_t, c_void_p]
     lib.ckv_select.restype = c_int
     lib.ckv_select.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.ckv_append_select.restype = c_int
@@ -156,6 +158,11 @@ def ckv_cluster_incremental_async(layer: CkvLayerStruct, ws: int, ws_bytes: int,
 
 def ckv_cluster_commit(layer: CkvLayerStruct) -> None:
     _check("ckv_cluster_commit", load_library().ckv_cluster_commit(_ref(layer)))
+
+
+def ckv_cluster_split(layer: CkvLayerStruct, threshold: float, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_cluster_split",
+           load_library().ckv_cluster_split(_ref(layer), float(threshold), ws, ws_bytes, stream))
 
 
 def ckv_select(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, ws: int,

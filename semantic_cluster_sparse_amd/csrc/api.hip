@@ -308,6 +308,47 @@ int ckv_cluster_commit(ckv_layer* L) {
   return CKV_OK;
 }
 
+int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (threshold != threshold) return fail(CKV_EINVAL, "threshold is NaN");
+  if (L->n_pending != 0)
+    return fail(CKV_EINVAL, "an asynchronous incremental call is pending (n_pending %d): commit it first",
+                L->n_pending);
+  if (L->n_clustered < L->n_sink) return fail(CKV_EINVAL, "no cluster state (n_clustered < n_sink)");
+  rc = check_ptrs("k_tok,v_tok,k_clu,v_clu,cdir,csum,msum,cmean,csize,offsets,assign,perm", 12, L->k_tok,
+                  L->v_tok, L->k_clu, L->v_clu, L->cdir, L->csum, L->msum, L->cmean, L->csize, L->offsets,
+                  L->assign, L->perm);
+  if (rc) return rc;
+  rc = check_ws(L, ws, ws_bytes);
+  if (rc) return rc;
+  const int m = L->n_clustered - L->n_sink;
+  if (m == 0) return CKV_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  const int units = L->batch * L->n_kv_heads;
+  const int K = L->n_clusters;
+  const int clu_stride = L->capacity - L->n_sink;
+  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
+  const Layout w = layout_of(L);
+  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
+  double* invn = (double*)((char*)ws + w.off_invn);
+
+  hipError_t e = ckv::launch_split(L->k_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K, L->csum,
+                                   L->csize, L->cdir, threshold, L->assign, units, s);
+  if (e != hipSuccess) return hip_status(e, "split");
+  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, 0, m, invn, clu_stride, units, s);
+  if (e != hipSuccess) return hip_status(e, "norms");
+  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
+  if (e != hipSuccess) return hip_status(e, "hist");
+  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
+  if (e != hipSuccess) return hip_status(e, "scatter");
+  e = ckv::launch_update(ckv::kUpdFinal, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride,
+                         L->offsets, K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu,
+                         units, s);
+  if (e != hipSuccess) return hip_status(e, "update");
+  return CKV_OK;
+}
+
 }  // extern "C"
 
 namespace {

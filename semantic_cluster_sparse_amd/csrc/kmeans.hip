@@ -634,6 +634,153 @@ __global__ __launch_bounds__(256) void update_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Drift split: one workgroup per unit.  The drift of cluster j is
+// 1 - |S_j| / n_j (f64 unit-key sums).  Clusters with n_j >= 2 and drift above
+// the threshold are ranked by drift (descending, ties to the smaller index) and
+// paired with the empty slots in index order.  For a pair (j, f) the member
+// with the smallest cosine to c~_j (ties to the earliest position, which is the
+// earliest token inside a cluster) seeds f with bf16(x / |x|); then every
+// member of j takes the larger of x . c~_j and x . c~_f (ties to the smaller
+// slot).  Every dot product is f64 over bf16 values, one lane per 2 dims and a
+// wave butterfly: the products are exact, so these decisions do not depend on
+// the summation order.  Only the labels are written here; the caller rebuilds
+// the index, sums, directions, means and cluster-ordered rows from them.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 4;
+constexpr int kSplitMaxK = 1024;  // the layer's cluster limit; per-unit lists live in LDS
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(kSplitWaves * 64) void split_kernel(
+    const uint16_t* __restrict__ k_tok, int capacity, int n_sink, const int32_t* __restrict__ perm,
+    int clu_stride, const int32_t* __restrict__ offsets, int K, const double* __restrict__ csum,
+    const int32_t* __restrict__ csize, const uint16_t* __restrict__ cdir, double threshold,
+    int32_t* __restrict__ assign) {
+  __shared__ double s_drift[kSplitMaxK];   // drift of a candidate, -inf otherwise
+  __shared__ int s_free[kSplitMaxK];       // empty slots, ascending
+  __shared__ int s_pair[kSplitMaxK];       // candidates by rank
+  __shared__ double s_bc[kSplitWaves];
+  __shared__ int s_bp[kSplitWaves];
+  __shared__ int s_counts[1];
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid >> 6;
+  const int32_t* nu = csize + (size_t)u * K;
+
+  for (int j = wv; j < K; j += kSplitWaves) {
+    const double2 sv = *reinterpret_cast<const double2*>(csum + ((size_t)u * K + j) * kHeadDim + 2 * lane);
+    const double ss = wave_sum_f64(sv.x * sv.x + sv.y * sv.y);
+    if (lane == 0) {
+      const int n = nu[j];
+      const double d = n > 0 ? 1.0 - sqrt(ss) / (double)n : 0.0;
+      s_drift[j] = (n >= 2 && d > threshold) ? d : -INFINITY;
+    }
+  }
+  if (wv == 0) {
+    int nfree = 0;
+    for (int base = 0; base < K; base += kWave) {
+      const int j = base + lane;
+      const bool empty = j < K && nu[j] == 0;
+      const unsigned long long fm = __ballot(empty);
+      if (empty) s_free[nfree + __popcll(fm & ((1ull << lane) - 1ull))] = j;
+      nfree += __popcll(fm);
+    }
+    if (lane == 0) s_counts[0] = nfree;
+  }
+  __syncthreads();
+  int my_cand = 0;
+  for (int j = tid; j < K; j += kSplitWaves * 64) {
+    const double dj = s_drift[j];
+    if (dj == -INFINITY) continue;
+    ++my_cand;
+    int r = 0;
+    for (int i = 0; i < K; ++i) {
+      const double di = s_drift[i];
+      r += (di > dj || (di == dj && i < j)) ? 1 : 0;
+    }
+    s_pair[r] = j;
+  }
+  for (int o = 1; o < kWave; o <<= 1) my_cand += __shfl_xor(my_cand, o);
+  if (lane == 0) s_bp[wv] = my_cand;
+  __syncthreads();
+  int pairs = 0;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) pairs += s_bp[w];
+  if (pairs > s_counts[0]) pairs = s_counts[0];
+
+  const int32_t* pu = perm + (size_t)u * clu_stride;
+  const uint16_t* ku = k_tok + (size_t)u * capacity * kHeadDim + 2 * lane;
+  for (int r = 0; r < pairs; ++r) {
+    __syncthreads();  // s_bc / s_bp of the previous pair (and the counts above) are consumed
+    const int j = s_pair[r];
+    const int f = s_free[r];
+    const int lo = min(max(offsets[(size_t)u * (K + 1) + j], 0), clu_stride);
+    const int hi = min(max(offsets[(size_t)u * (K + 1) + j + 1], lo), clu_stride);
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(cdir + ((size_t)u * K + j) * kHeadDim + 2 * lane);
+    const double c0 = (double)bf16_lo(cw), c1 = (double)bf16_hi(cw);
+
+    double best = INFINITY;
+    int bestp = 0x7fffffff;
+    for (int p = lo + wv; p < hi; p += kSplitWaves) {
+      int tk = pu[p];
+      tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
+      const uint32_t xw = *reinterpret_cast<const uint32_t*>(ku + (size_t)tk * kHeadDim);
+      const double x0 = (double)bf16_lo(xw), x1 = (double)bf16_hi(xw);
+      const double dot = wave_sum_f64(x0 * c0 + x1 * c1);
+      const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
+      const double cs = ss > 0.0 ? dot / sqrt(ss) : 0.0;
+      if (cs < best) {  // positions ascend per wave: the first minimum stays
+        best = cs;
+        bestp = p;
+      }
+    }
+    if (lane == 0) {
+      s_bc[wv] = best;
+      s_bp[wv] = bestp;
+    }
+    __syncthreads();
+    int sp = s_bp[0];
+    double sb = s_bc[0];
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) {
+      if (s_bc[w] < sb || (s_bc[w] == sb && s_bp[w] < sp)) {
+        sb = s_bc[w];
+        sp = s_bp[w];
+      }
+    }
+    if (sp < lo || sp >= hi) continue;  // no members (cannot happen for n_j >= 2)
+    int ts = pu[sp];
+    ts = ts < n_sink ? n_sink : (ts >= capacity ? capacity - 1 : ts);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(ku + (size_t)ts * kHeadDim);
+    const double s0 = (double)bf16_lo(sw), s1 = (double)bf16_hi(sw);
+    const double sss = wave_sum_f64(s0 * s0 + s1 * s1);
+    double f0 = 0.0, f1 = 0.0;
+    if (sss > 0.0) {
+      const double nrm = sqrt(sss);
+      f0 = (double)bf16_to_f32(f64_to_bf16_rne(s0 / nrm));
+      f1 = (double)bf16_to_f32(f64_to_bf16_rne(s1 / nrm));
+    }
+    int32_t* au = assign + (size_t)u * clu_stride;
+    for (int p = lo + wv; p < hi; p += kSplitWaves) {
+      int tk = pu[p];
+      tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
+      const uint32_t xw = *reinterpret_cast<const uint32_t*>(ku + (size_t)tk * kHeadDim);
+      const double x0 = (double)bf16_lo(xw), x1 = (double)bf16_hi(xw);
+      const double sj = wave_sum_f64(x0 * c0 + x1 * c1);
+      const double sf = wave_sum_f64(x0 * f0 + x1 * f1);
+      const bool move = f < j ? (sf >= sj) : (sf > sj);
+      if (move && lane == 0) au[tk - n_sink] = f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int m,
@@ -716,6 +863,15 @@ hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
   else
     CKV_UPD(kUpdIncr);
 #undef CKV_UPD
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const uint16_t* k_tok, int capacity, int n_sink, const int32_t* perm, int clu_stride,
+                        const int32_t* offsets, int K, const double* csum, const int32_t* csize,
+                        const uint16_t* cdir, double threshold, int32_t* assign, int units, hipStream_t s) {
+  if (K > kSplitMaxK) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_kernel, dim3((unsigned)units), dim3(kSplitWaves * 64), 0, s, k_tok, capacity, n_sink,
+                     perm, clu_stride, offsets, K, csum, csize, cdir, threshold, assign);
   return hipGetLastError();
 }
 

@@ -185,3 +185,29 @@ def test_commit_swaps_the_second_buffers():
     for n in names:
         assert (getattr(L, n), getattr(L, n + "_alt")) == before[n][::-1], n
     assert L.n_clustered == 120 and L.n_pending == 0 and L.n_total == 130
+
+
+def test_split_host_rules():
+    L = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_split(L, float("nan"), FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and "NaN" in e.value.message
+    P = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=120))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_split(P, 0.5, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and "pending" in e.value.message
+    N = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=10, n_clustered=10))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_split(N, 0.5, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and "no cluster state" in e.value.message
+    L.assign = None
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_cluster_split(L, 0.5, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    S = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100))
+    with pytest.raises(ckv.CkvError):
+        ckv.ckv_cluster_split(S, 0.5, FAKE, 64)            # workspace too small
+    # nothing clustered beyond the sinks: nothing to do, nothing enqueued
+    E = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=16, n_clustered=16))
+    ckv.ckv_cluster_split(E, 0.5, FAKE, 1 << 40)
+    assert E.n_clustered == 16 and E.n_total == 16

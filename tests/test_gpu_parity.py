@@ -794,3 +794,135 @@ def test_incremental_full_size_sampled():
             say(f"  unit {u}: decode max abs err {err:.3g}")
             assert err <= DECODE_ATOL
     assert compared >= 1, "no sampled unit could be compared"
+
+
+# ------------------------------------------------------------------ drift split
+
+
+def _reserve_init(cfg, units, reserve):
+    init = synth.make_init_indices(cfg.init_seed, units, cfg.m, cfg.n_clusters)
+    return np.concatenate([init, np.full((units, reserve), -1, np.int32)], axis=1)
+
+
+def _split_threshold(states, q):
+    """A threshold halfway between two neighbouring drifts (near quantile ``q`` of
+    unit 0's clusters with >= 2 members), checked against every unit: no drift
+    lies within 1e-12 of it, and no two candidate drifts are within 1e-12 (so the
+    pairing order cannot hinge on summation order)."""
+    from oracle import kmeans
+    d0 = kmeans.drift(states[0]["csum"], states[0]["csize"])
+    d = np.sort(d0[states[0]["csize"] >= 2])
+    i = int(q * (len(d) - 1))
+    tau = 0.5 * (d[i] + d[i + 1])
+    for st in states:
+        dr = kmeans.drift(st["csum"], st["csize"])[st["csize"] >= 2]
+        assert np.min(np.abs(dr - tau)) > 1e-12
+        c = np.sort(dr[dr > tau])
+        assert len(c) < 2 or np.min(np.diff(c)) > 1e-12
+    return float(tau)
+
+
+def _check_split(L, states, k, v, tau, tag):
+    oras = [pipeline.split_unit(st, k[u], tau, v_bits=v[u]) for u, st in enumerate(states)]
+    L.split(tau)
+    torch.cuda.synchronize()
+    total_pairs = 0
+    for u, ora in enumerate(oras):
+        m = len(ora["assign"])
+        total_pairs += len(ora["pairs"])
+        a_g = L.assign[u, :m].cpu().numpy()
+        say(f"  {tag} unit {u}: {len(ora['pairs'])} splits, labels differing {int(np.sum(a_g != ora['assign']))}")
+        assert np.array_equal(a_g, ora["assign"]), "split labels differ"
+        x = bf16.widen(k[u][16:ora["n_clustered"]])
+        assert check_state(L, u, ora, x, ora["cdir"], tag=tag) == 0
+    return oras, total_pairs
+
+
+def test_split_after_prefill_with_reserved_slots():
+    cfg = synth.CONFIGS["single-head-2k"]
+    say("case: drift split, teacher-forced prefill state with 8 reserved slots, 3 units")
+    U, R = 3, 8
+    k, v, _ = synth.make_layer_inputs(cfg, units=list(range(U)))
+    init = _reserve_init(cfg, U, R)
+    K = cfg.n_clusters + R
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], K, cfg.iters, v_bits=v[u]) for u in range(U)]
+    for st in states:
+        assert np.all(st["csize"][cfg.n_clusters:] == 0)
+    for q in (0.5, 0.9):
+        L = gpu_layer(k, v, 1, K)
+        load_state(L, states)
+        L.set_counters(cfg.n_tokens, cfg.n_tokens)
+        _, pairs = _check_split(L, states, k, v, _split_threshold(states, q), f"q={q}")
+        assert pairs > 0
+
+
+def test_split_on_gpu_prefill_with_reserved_slots():
+    cfg = synth.CONFIGS["single-head-2k"]
+    say("case: GPU prefill with 8 reserved slots, then drift split, 3 units")
+    U, R = 3, 8
+    k, v, _ = synth.make_layer_inputs(cfg, units=list(range(U)))
+    init = _reserve_init(cfg, U, R)
+    K = cfg.n_clusters + R
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], K, cfg.iters, v_bits=v[u]) for u in range(U)]
+    L = gpu_layer(k, v, 1, K)
+    L.prefill(cfg.n_tokens, cfg.iters, to_dev(init, torch.int32))
+    torch.cuda.synchronize()
+    for u in range(U):
+        x = bf16.widen(k[u][16:cfg.n_tokens])
+        assert check_state(L, u, states[u], x, states[u]["cdir"], tag="prefill") == 0
+    _check_split(L, states, k, v, _split_threshold(states, 0.5), "split")
+
+
+def test_split_without_free_slot_only_rebuilds():
+    cfg = synth.CONFIGS["single-head-2k"]
+    say("case: drift split with no empty slot (every cluster a candidate)")
+    k, v, _ = synth.make_layer_inputs(cfg, units=[0, 1])
+    init = synth.make_init_indices(cfg.init_seed, 2, cfg.m, cfg.n_clusters)
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, cfg.iters, v_bits=v[u])
+              for u in range(2)]
+    assert all(np.all(st["csize"] > 0) for st in states)
+    L = gpu_layer(k, v, 1, cfg.n_clusters)
+    load_state(L, states)
+    L.set_counters(cfg.n_tokens, cfg.n_tokens)
+    _, pairs = _check_split(L, states, k, v, -1.0, "no-slot")
+    assert pairs == 0
+
+
+def test_split_after_incremental_new_components_then_recall_and_decode():
+    cfg = synth.CONFIGS["llama8b-incremental-b16"]
+    U, R = 2, 16
+    say(f"case: drift split after +{cfg.new_tokens} keys from {cfg.new_components} new components, "
+        f"Llama layer shape, K = {cfg.n_clusters} + {R} reserved, units 0-1, then recall and decode")
+    n_new = cfg.n_tokens + cfg.new_tokens
+    k, v, cen = synth.make_layer_inputs(cfg, units=list(range(U)), capacity=n_new + 4)
+    init = _reserve_init(cfg, U, R)
+    K = cfg.n_clusters + R
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], K, 3, v_bits=v[u]) for u in range(U)]
+    kn, vn, newc = synth.make_new_tokens(cfg.data_seed, cen, cfg.new_tokens, cfg.new_components,
+                                         cfg.new_fraction)
+    k[:, cfg.n_tokens:n_new] = kn
+    v[:, cfg.n_tokens:n_new] = vn
+    states = [pipeline.incremental_unit(states[u], k[u], n_new, v_bits=v[u]) for u in range(U)]
+    L = gpu_layer(k, v, cfg.group, K, max_budget=cfg.budget)
+    load_state(L, states)
+    L.set_counters(n_new, n_new)
+    oras, pairs = _check_split(L, states, k, v, _split_threshold(states, 0.5), "split")
+    assert pairs == U * R                       # more candidates than reserved slots
+    q = synth.make_queries(cfg.query_seed, np.concatenate([cen, newc], axis=1), cfg.group)
+    qd = dev_bf16(q)
+    sel_pos = torch.zeros((U, cfg.budget), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((U,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((U, cfg.group, D), dtype=torch.float32, device="cuda")
+    L.select(qd, cfg.budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, cfg.budget, out)
+    torch.cuda.synchronize()
+    sp, cn, og = sel_pos.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    for u, ora in enumerate(oras):
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"],
+                                   cfg.budget)
+        if compare_selection(L, u, sp, cn, ora, sel, cfg.budget) == 0:
+            ref = pipeline.decode_unit(q[u], k[u], v[u], ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
+                                       16, n_new, n_new)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
