@@ -163,6 +163,46 @@ def incremental_bytes(units: int, K: int, m_old: int, m_new: int) -> int:
     return units * (m_new * (2 * 2 * d + 4) + m * (4 + 4 + 4 + 4 * 2 * d) + K * per_cluster)
 
 
+def split_bytes(units: int, K: int, m: int, split_rows: int) -> int:
+    """Algorithmic HBM bytes of one ckv_cluster_split call.
+
+    The split itself reads every cluster's f64 sum and size and, for each split
+    cluster, its members' keys once (256 B per row; the seed search and the
+    move both need them, but one read suffices) and their token ids, and
+    writes their labels (4 + 4 B per row).  The rebuild that
+    follows is the incremental call's without new keys: norms of every
+    clustered key (256 B read, 8 B written), labels read twice and the index
+    written, K and V rows gathered and written in cluster order, and the
+    per-cluster state rewritten.
+    """
+    d = 128
+    per_cluster = 8 * d + 4 + 2 * 2 * d + 8 * d * 2 + 4 * d + 4 * 2 + 4
+    split = split_rows * (2 * d + 4 + 4)
+    rebuild = m * (2 * d + 8 + 4 + 4 + 4 + 4 * 2 * d)
+    return units * (K * per_cluster + rebuild) + split
+
+
+def split_plan(L, reserve: int):
+    """Threshold for the split measurement (the median drift 1 - |S|/n over the
+    clusters with at least two members) and the number of rows in the clusters
+    it will split: per unit the min(reserve + already-empty slots, candidates)
+    most drifted candidates.  Device tensors, outside the timed region."""
+    import torch
+
+    n = L.csize.to(torch.float64)
+    drift = 1.0 - torch.linalg.vector_norm(L.csum, dim=-1) / n.clamp(min=1.0)
+    ok = L.csize >= 2
+    tau = float(drift[ok].median())
+    cand = torch.where(ok & (drift > tau), drift, torch.full_like(drift, -1.0))
+    free = (L.csize == 0).sum(dim=1)
+    order = torch.argsort(cand, dim=1, descending=True)
+    rank = torch.empty_like(order)
+    rank.scatter_(1, order, torch.arange(order.shape[1], device=order.device).expand_as(order))
+    take = (cand > tau) & (rank < free[:, None])
+    rows = int((L.csize * take).sum())
+    return tau, rows
+
+
 def setup(args):
     import torch
 
@@ -526,13 +566,17 @@ def run_incremental(cfg, args) -> dict:
     cap = n0 + n_new
     so = seed_offset(cfg)
     stream = torch.cuda.current_stream()
-    L = Layer(batch=cfg.batch, n_kv_heads=cfg.n_kv_heads, group=G, n_clusters=cfg.n_clusters,
+    R = args.split_reserve
+    L = Layer(batch=cfg.batch, n_kv_heads=cfg.n_kv_heads, group=G, n_clusters=cfg.n_clusters + R,
               capacity=cap, max_budget=budget, incremental=True, device=dev)
     cen = dgen.fill_mixture(L.k_tok, L.v_tok, n0, cfg.components, seed=10_000 + so)
     k_add, v_add = dgen.new_rows(cen, n_new, cfg.new_components, cfg.new_fraction,
                                  seed=60_000 + so)
     q = dgen.queries(cen, G, seed=20_000 + so)
     init = dgen.init_indices(units, cfg.m, cfg.n_clusters, seed=30_000 + so, device=dev)
+    if R:
+        # slots held empty at prefill (init index -1) for the drift split to fill
+        init = torch.cat([init, torch.full((units, R), -1, dtype=torch.int32, device=dev)], 1).contiguous()
     del cen
     sel_pos = torch.zeros((units, budget), dtype=torch.int32, device=dev)
     cnt = torch.zeros((units,), dtype=torch.int32, device=dev)
@@ -541,7 +585,7 @@ def run_incremental(cfg, args) -> dict:
     log(f"[bench] {cfg.name}: {units} units, {n0} clustered + {n_new} new tokens; "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
-    t_inc, t_sel, t_dec, t_sel0 = [], [], [], []
+    t_inc, t_sel, t_dec, t_sel0, t_split, split_rows = [], [], [], [], [], []
     for r in range(W + reps):
         L.prefill(n0, cfg.iters, init)
         L.k_tok[:, n0:cap].copy_(k_add)
@@ -559,6 +603,16 @@ def run_incremental(cfg, args) -> dict:
         L.sparse_decode(q, sel_pos, cnt, budget, out)
         e[4].record(stream)
         torch.cuda.synchronize()
+        if R:
+            tau, rows = split_plan(L, R)
+            es = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            es[0].record(stream)
+            L.split(tau)
+            es[1].record(stream)
+            torch.cuda.synchronize()
+            if r >= W:
+                t_split.append(es[0].elapsed_time(es[1]))
+                split_rows.append(rows)
         if r >= W:
             t_sel0.append(e[0].elapsed_time(e[1]))
             t_inc.append(e[1].elapsed_time(e[2]))
@@ -573,6 +627,17 @@ def run_incremental(cfg, args) -> dict:
     achieved = ibytes / (inc_ms * 1e-3) / 1e9
     log(f"[bench] ckv_cluster_incremental {inc_ms * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic; "
         f"select {med(t_sel) * 1e3:.1f} us; decode {med(t_dec) * 1e3:.1f} us")
+    extra = {}
+    if R:
+        sp_ms = med(t_split)
+        rows = split_rows[0]
+        sbytes = split_bytes(units, L.n_clusters, cfg.m + n_new, rows)
+        extra["split"] = {"reserved_slots": R, "threshold": "median drift of the clusters with >= 2 members",
+                          "us": sp_ms * 1e3, "candidate_rows": rows, "bytes": sbytes,
+                          "achieved_gbs": sbytes / (sp_ms * 1e-3) / 1e9,
+                          "frac": sbytes / (sp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] ckv_cluster_split {sp_ms * 1e3:.1f} us ({R} reserved slots per unit, "
+            f"{rows} rows in split clusters), {extra['split']['achieved_gbs']:.0f} GB/s algorithmic")
     return {
         "metric": "incremental clustering latency (320 new keys per KV head), then budget-1024 recall",
         "value": inc_ms * 1e3,
@@ -596,6 +661,7 @@ def run_incremental(cfg, args) -> dict:
         "select_us": med(t_sel) * 1e3,
         "select_before_incremental_us": med(t_sel0) * 1e3,
         "sparse_decode_us": med(t_dec) * 1e3,
+        **extra,
     }
 
 
@@ -631,6 +697,9 @@ def main() -> int:
     ap.add_argument("--async-lag", type=int, default=16, help="steps between starting and committing")
     ap.add_argument("--per-head-recall", action="store_true",
                     help="one recall and attention set per query head instead of per KV head")
+    ap.add_argument("--split-reserve", type=int, default=0,
+                    help="llama8b-incremental-b16 only: hold this many cluster slots empty at prefill and "
+                         "time ckv_cluster_split after the incremental call")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")

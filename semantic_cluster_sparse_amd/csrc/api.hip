@@ -333,8 +333,12 @@ int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes,
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
   double* invn = (double*)((char*)ws + w.off_invn);
 
-  hipError_t e = ckv::launch_split(L->k_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K, L->csum,
-                                   L->csize, L->cdir, threshold, L->assign, units, s);
+  // The pair plan, units x (2K + 1) int32, sits at the start of the histogram
+  // and norm regions (at least 12 K bytes per unit between them); the norm and
+  // histogram kernels below overwrite it only after the split has used it.
+  int32_t* plan = hist;
+  hipError_t e = ckv::launch_split(L->k_clu, L->n_sink, L->perm, clu_stride, L->offsets, K, L->csum,
+                                   L->csize, L->cdir, threshold, plan, L->assign, units, s);
   if (e != hipSuccess) return hip_status(e, "split");
   e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, 0, m, invn, clu_stride, units, s);
   if (e != hipSuccess) return hip_status(e, "norms");

@@ -634,20 +634,33 @@ __global__ __launch_bounds__(256) void update_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Drift split: one workgroup per unit.  The drift of cluster j is
-// 1 - |S_j| / n_j (f64 unit-key sums).  Clusters with n_j >= 2 and drift above
-// the threshold are ranked by drift (descending, ties to the smaller index) and
-// paired with the empty slots in index order.  For a pair (j, f) the member
-// with the smallest cosine to c~_j (ties to the earliest position, which is the
-// earliest token inside a cluster) seeds f with bf16(x / |x|); then every
-// member of j takes the larger of x . c~_j and x . c~_f (ties to the smaller
-// slot).  Every dot product is f64 over bf16 values, one lane per 2 dims and a
-// wave butterfly: the products are exact, so these decisions do not depend on
-// the summation order.  Only the labels are written here; the caller rebuilds
-// the index, sums, directions, means and cluster-ordered rows from them.
+// Drift split.  The drift of cluster j is 1 - |S_j| / n_j (f64 unit-key sums).
+// Clusters with n_j >= 2 and drift above the threshold are ranked by drift
+// (descending, ties to the smaller index) and paired with the empty slots in
+// index order.  For a pair (j, f) the member with the smallest cosine to c~_j
+// (ties to the earliest position, which is the earliest token inside a
+// cluster) seeds f with bf16(x / |x|); then every member of j takes the larger
+// of x . c~_j and x . c~_f (ties to the smaller slot).  Every dot product is
+// f64 over bf16 values: the products are exact, so these decisions do not
+// depend on the summation order.  Only the labels are written here; the caller
+// rebuilds the index, sums, directions, means and cluster-ordered rows.
+//
+// split_plan_kernel (one workgroup per unit) writes the pairs to a plan
+// [units, 2K + 1] int32: the pair count, then j of each pair, then f.
+// split_move_kernel spreads a unit's pairs over kSplitPar workgroups.  Pairs
+// touch disjoint members, so the workgroups write disjoint labels.  A member
+// row is read from the cluster-ordered copy (a cluster's rows are contiguous
+// there) as one 16-byte load per lane (16 lanes per row, 8 dims each); a wave
+// holds 16 rows in flight and a workgroup 64.  A cluster of at most 64 rows is
+// read once: its rows stay in registers from the seed search to the move.
 // ---------------------------------------------------------------------------
 constexpr int kSplitWaves = 4;
 constexpr int kSplitMaxK = 1024;  // the layer's cluster limit; per-unit lists live in LDS
+constexpr int kSplitPar = 16;     // workgroups per unit in the move kernel
+constexpr int kSplitPlanUnroll = 4;
+constexpr int kSplitMoveWaves = 4;
+constexpr int kSplitSlotRows = 4;                              // rows per 16-lane slot in flight
+constexpr int kSplitRows = kSplitMoveWaves * 4 * kSplitSlotRows;  // rows per workgroup step
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -655,15 +668,11 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-__global__ __launch_bounds__(kSplitWaves * 64) void split_kernel(
-    const uint16_t* __restrict__ k_tok, int capacity, int n_sink, const int32_t* __restrict__ perm,
-    int clu_stride, const int32_t* __restrict__ offsets, int K, const double* __restrict__ csum,
-    const int32_t* __restrict__ csize, const uint16_t* __restrict__ cdir, double threshold,
-    int32_t* __restrict__ assign) {
+__global__ __launch_bounds__(kSplitWaves * 64) void split_plan_kernel(
+    int K, const double* __restrict__ csum, const int32_t* __restrict__ csize, double threshold,
+    int32_t* __restrict__ plan) {
   __shared__ double s_drift[kSplitMaxK];   // drift of a candidate, -inf otherwise
   __shared__ int s_free[kSplitMaxK];       // empty slots, ascending
-  __shared__ int s_pair[kSplitMaxK];       // candidates by rank
-  __shared__ double s_bc[kSplitWaves];
   __shared__ int s_bp[kSplitWaves];
   __shared__ int s_counts[1];
 
@@ -672,14 +681,34 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_kernel(
   const int lane = lane_id();
   const int wv = tid >> 6;
   const int32_t* nu = csize + (size_t)u * K;
+  int32_t* pl = plan + (size_t)u * (2 * K + 1);
 
-  for (int j = wv; j < K; j += kSplitWaves) {
-    const double2 sv = *reinterpret_cast<const double2*>(csum + ((size_t)u * K + j) * kHeadDim + 2 * lane);
-    const double ss = wave_sum_f64(sv.x * sv.x + sv.y * sv.y);
-    if (lane == 0) {
-      const int n = nu[j];
-      const double d = n > 0 ? 1.0 - sqrt(ss) / (double)n : 0.0;
-      s_drift[j] = (n >= 2 && d > threshold) ? d : -INFINITY;
+  // |S_j|^2: 16 lanes per cluster (8 f64 each), 4 clusters per wave, and
+  // kSplitPlanUnroll of them per lane slot in flight at once
+  {
+    const int grp = lane >> 4, sub = lane & 15;
+    for (int j0 = wv * 4 + grp; j0 < K; j0 += kSplitWaves * 4 * kSplitPlanUnroll) {
+      double2 sv[kSplitPlanUnroll][4];
+#pragma unroll
+      for (int t = 0; t < kSplitPlanUnroll; ++t) {
+        const int j = min(j0 + t * kSplitWaves * 4, K - 1);
+        const double2* row = reinterpret_cast<const double2*>(csum + ((size_t)u * K + j) * kHeadDim + 8 * sub);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[t][i] = row[i];
+      }
+#pragma unroll
+      for (int t = 0; t < kSplitPlanUnroll; ++t) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fma(sv[t][i].x, sv[t][i].x, fma(sv[t][i].y, sv[t][i].y, ss));
+        ss = xor_sum16(ss);
+        const int j = j0 + t * kSplitWaves * 4;
+        if (sub == 0 && j < K) {
+          const int n = nu[j];
+          const double d = n > 0 ? 1.0 - sqrt(ss) / (double)n : 0.0;
+          s_drift[j] = (n >= 2 && d > threshold) ? d : -INFINITY;
+        }
+      }
     }
   }
   if (wv == 0) {
@@ -694,6 +723,7 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_kernel(
     if (lane == 0) s_counts[0] = nfree;
   }
   __syncthreads();
+  const int nfree = s_counts[0];
   int my_cand = 0;
   for (int j = tid; j < K; j += kSplitWaves * 64) {
     const double dj = s_drift[j];
@@ -704,78 +734,133 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_kernel(
       const double di = s_drift[i];
       r += (di > dj || (di == dj && i < j)) ? 1 : 0;
     }
-    s_pair[r] = j;
+    if (r < nfree) {
+      pl[1 + r] = j;
+      pl[1 + K + r] = s_free[r];
+    }
   }
   for (int o = 1; o < kWave; o <<= 1) my_cand += __shfl_xor(my_cand, o);
   if (lane == 0) s_bp[wv] = my_cand;
   __syncthreads();
-  int pairs = 0;
+  if (tid == 0) {
+    int pairs = 0;
 #pragma unroll
-  for (int w = 0; w < kSplitWaves; ++w) pairs += s_bp[w];
-  if (pairs > s_counts[0]) pairs = s_counts[0];
+    for (int w = 0; w < kSplitWaves; ++w) pairs += s_bp[w];
+    pl[0] = pairs < nfree ? pairs : nfree;
+  }
+}
 
+// 8 dims of one bf16 row as f64 (exact).
+__device__ __forceinline__ void widen8(const uint4 w, double* x) {
+  x[0] = (double)bf16_lo(w.x); x[1] = (double)bf16_hi(w.x);
+  x[2] = (double)bf16_lo(w.y); x[3] = (double)bf16_hi(w.y);
+  x[4] = (double)bf16_lo(w.z); x[5] = (double)bf16_hi(w.z);
+  x[6] = (double)bf16_lo(w.w); x[7] = (double)bf16_hi(w.w);
+}
+
+__device__ __forceinline__ double dot8(const double* a, const double* b) {
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fma(a[i], b[i], s);
+  return s;
+}
+
+__global__ __launch_bounds__(kSplitMoveWaves * 64) void split_move_kernel(
+    const uint16_t* __restrict__ k_clu, int n_sink, const int32_t* __restrict__ perm, int clu_stride,
+    const int32_t* __restrict__ offsets, int K, const uint16_t* __restrict__ cdir,
+    const int32_t* __restrict__ plan, int32_t* __restrict__ assign) {
+  __shared__ double s_bc[kSplitMoveWaves * 4];
+  __shared__ int s_bp[kSplitMoveWaves * 4];
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = tid >> 6;
+  const int grp = lane >> 4;   // row slot of the wave
+  const int sub = lane & 15;   // 8-dim slice of the row
+  const int32_t* pl = plan + (size_t)u * (2 * K + 1);
+  const int pairs = pl[0];
   const int32_t* pu = perm + (size_t)u * clu_stride;
-  const uint16_t* ku = k_tok + (size_t)u * capacity * kHeadDim + 2 * lane;
-  for (int r = 0; r < pairs; ++r) {
-    __syncthreads();  // s_bc / s_bp of the previous pair (and the counts above) are consumed
-    const int j = s_pair[r];
-    const int f = s_free[r];
+  // the cluster-ordered copy: position p holds the key of token perm[p]
+  const uint16_t* ku = k_clu + (size_t)u * clu_stride * kHeadDim + 8 * sub;
+  int32_t* au = assign + (size_t)u * clu_stride;
+  const int slot0 = wv * 4 * kSplitSlotRows + grp;
+
+  for (int r = blockIdx.y; r < pairs; r += gridDim.y) {
+    const int j = pl[1 + r];
+    const int f = pl[1 + K + r];
     const int lo = min(max(offsets[(size_t)u * (K + 1) + j], 0), clu_stride);
     const int hi = min(max(offsets[(size_t)u * (K + 1) + j + 1], lo), clu_stride);
-    const uint32_t cw = *reinterpret_cast<const uint32_t*>(cdir + ((size_t)u * K + j) * kHeadDim + 2 * lane);
-    const double c0 = (double)bf16_lo(cw), c1 = (double)bf16_hi(cw);
+    const bool one_step = hi - lo <= kSplitRows;  // rows stay in registers for the move
+    double cj[8];
+    widen8(*reinterpret_cast<const uint4*>(cdir + ((size_t)u * K + j) * kHeadDim + 8 * sub), cj);
 
+    // seed: the member with the smallest cosine to c~_j, earliest position on ties
     double best = INFINITY;
     int bestp = 0x7fffffff;
-    for (int p = lo + wv; p < hi; p += kSplitWaves) {
-      int tk = pu[p];
-      tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
-      const uint32_t xw = *reinterpret_cast<const uint32_t*>(ku + (size_t)tk * kHeadDim);
-      const double x0 = (double)bf16_lo(xw), x1 = (double)bf16_hi(xw);
-      const double dot = wave_sum_f64(x0 * c0 + x1 * c1);
-      const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
-      const double cs = ss > 0.0 ? dot / sqrt(ss) : 0.0;
-      if (cs < best) {  // positions ascend per wave: the first minimum stays
-        best = cs;
-        bestp = p;
+    uint4 w[kSplitSlotRows];
+    for (int base = lo + slot0; base < hi; base += kSplitRows) {
+#pragma unroll
+      for (int t = 0; t < kSplitSlotRows; ++t) {
+        const int p = min(base + 4 * t, hi - 1);
+        w[t] = *reinterpret_cast<const uint4*>(ku + (size_t)p * kHeadDim);
+      }
+#pragma unroll
+      for (int t = 0; t < kSplitSlotRows; ++t) {
+        double x[8];
+        widen8(w[t], x);
+        const double dot = xor_sum16(dot8(x, cj));
+        const double ss = xor_sum16(dot8(x, x));
+        const double cs = ss > 0.0 ? dot / sqrt(ss) : 0.0;
+        if (base + 4 * t < hi && cs < best) {  // a slot's positions ascend: the first minimum stays
+          best = cs;
+          bestp = base + 4 * t;
+        }
       }
     }
-    if (lane == 0) {
-      s_bc[wv] = best;
-      s_bp[wv] = bestp;
+    if (sub == 0) {
+      s_bc[wv * 4 + grp] = best;
+      s_bp[wv * 4 + grp] = bestp;
     }
     __syncthreads();
     int sp = s_bp[0];
     double sb = s_bc[0];
 #pragma unroll
-    for (int w = 1; w < kSplitWaves; ++w) {
-      if (s_bc[w] < sb || (s_bc[w] == sb && s_bp[w] < sp)) {
-        sb = s_bc[w];
-        sp = s_bp[w];
+    for (int g = 1; g < kSplitMoveWaves * 4; ++g) {
+      if (s_bc[g] < sb || (s_bc[g] == sb && s_bp[g] < sp)) {
+        sb = s_bc[g];
+        sp = s_bp[g];
       }
     }
-    if (sp < lo || sp >= hi) continue;  // no members (cannot happen for n_j >= 2)
-    int ts = pu[sp];
-    ts = ts < n_sink ? n_sink : (ts >= capacity ? capacity - 1 : ts);
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(ku + (size_t)ts * kHeadDim);
-    const double s0 = (double)bf16_lo(sw), s1 = (double)bf16_hi(sw);
-    const double sss = wave_sum_f64(s0 * s0 + s1 * s1);
-    double f0 = 0.0, f1 = 0.0;
-    if (sss > 0.0) {
-      const double nrm = sqrt(sss);
-      f0 = (double)bf16_to_f32(f64_to_bf16_rne(s0 / nrm));
-      f1 = (double)bf16_to_f32(f64_to_bf16_rne(s1 / nrm));
-    }
-    int32_t* au = assign + (size_t)u * clu_stride;
-    for (int p = lo + wv; p < hi; p += kSplitWaves) {
-      int tk = pu[p];
-      tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
-      const uint32_t xw = *reinterpret_cast<const uint32_t*>(ku + (size_t)tk * kHeadDim);
-      const double x0 = (double)bf16_lo(xw), x1 = (double)bf16_hi(xw);
-      const double sj = wave_sum_f64(x0 * c0 + x1 * c1);
-      const double sf = wave_sum_f64(x0 * f0 + x1 * f1);
-      const bool move = f < j ? (sf >= sj) : (sf > sj);
-      if (move && lane == 0) au[tk - n_sink] = f;
+    __syncthreads();  // s_bc / s_bp are rewritten by the next pair
+    if (sp < lo || sp >= hi) continue;  // no members (cannot happen for n_j >= 2); uniform
+    double sx[8];
+    widen8(*reinterpret_cast<const uint4*>(ku + (size_t)sp * kHeadDim), sx);
+    const double sss = xor_sum16(dot8(sx, sx));
+    double cf[8];
+    const double nrm = sqrt(sss);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cf[i] = sss > 0.0 ? (double)bf16_to_f32(f64_to_bf16_rne(sx[i] / nrm)) : 0.0;
+
+    // move: each member of j takes the larger score of c~_j and c~_f
+    for (int base = lo + slot0; base < hi; base += kSplitRows) {
+      int tk[kSplitSlotRows];
+#pragma unroll
+      for (int t = 0; t < kSplitSlotRows; ++t) {
+        const int p = min(base + 4 * t, hi - 1);
+        tk[t] = pu[p];
+        if (!one_step) w[t] = *reinterpret_cast<const uint4*>(ku + (size_t)p * kHeadDim);
+      }
+#pragma unroll
+      for (int t = 0; t < kSplitSlotRows; ++t) {
+        double x[8];
+        widen8(w[t], x);
+        const double sj = xor_sum16(dot8(x, cj));
+        const double sf = xor_sum16(dot8(x, cf));
+        const bool move = f < j ? (sf >= sj) : (sf > sj);
+        const int row = tk[t] - n_sink;
+        if (base + 4 * t < hi && move && sub == 0 && row >= 0 && row < clu_stride) au[row] = f;
+      }
     }
   }
 }
@@ -866,12 +951,15 @@ hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
   return hipGetLastError();
 }
 
-hipError_t launch_split(const uint16_t* k_tok, int capacity, int n_sink, const int32_t* perm, int clu_stride,
+hipError_t launch_split(const uint16_t* k_clu, int n_sink, const int32_t* perm, int clu_stride,
                         const int32_t* offsets, int K, const double* csum, const int32_t* csize,
-                        const uint16_t* cdir, double threshold, int32_t* assign, int units, hipStream_t s) {
+                        const uint16_t* cdir, double threshold, int32_t* plan, int32_t* assign, int units,
+                        hipStream_t s) {
   if (K > kSplitMaxK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(split_kernel, dim3((unsigned)units), dim3(kSplitWaves * 64), 0, s, k_tok, capacity, n_sink,
-                     perm, clu_stride, offsets, K, csum, csize, cdir, threshold, assign);
+  hipLaunchKernelGGL(split_plan_kernel, dim3((unsigned)units), dim3(kSplitWaves * 64), 0, s, K, csum, csize,
+                     threshold, plan);
+  hipLaunchKernelGGL(split_move_kernel, dim3((unsigned)units, (unsigned)kSplitPar), dim3(kSplitMoveWaves * 64), 0, s,
+                     k_clu, n_sink, perm, clu_stride, offsets, K, cdir, plan, assign);
   return hipGetLastError();
 }
 

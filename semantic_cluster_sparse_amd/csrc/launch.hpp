@@ -46,14 +46,17 @@ hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
                          int32_t* csize, uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst,
                          int units, hipStream_t s);
 
+// Drift split: the pairs go to plan [units, 2K + 1] int32 (workspace), then
+// the labels of the split clusters' members are rewritten.
+hipError_t launch_split(const uint16_t* k_clu, int n_sink, const int32_t* perm, int clu_stride,
+                        const int32_t* offsets, int K, const double* csum, const int32_t* csize,
+                        const uint16_t* cdir, double threshold, int32_t* plan, int32_t* assign, int units,
+                        hipStream_t s);
+
 // Recall: cluster scores (several workgroups per unit), then the last of them
 // finds the cut, the partial top-k and writes the positions.  counters[units]
 // must be zero on entry and are zero again on exit.  With k_new non-null the
 // same launch also writes k_new / v_new into row `row` of k_tok / v_tok.
-hipError_t launch_split(const uint16_t* k_tok, int capacity, int n_sink, const int32_t* perm, int clu_stride,
-                        const int32_t* offsets, int K, const double* csum, const int32_t* csize,
-                        const uint16_t* cdir, double threshold, int32_t* assign, int units, hipStream_t s);
-
 hipError_t launch_select(const uint16_t* q, int group, const float* cmean,
                          const int32_t* offsets, int K, const uint16_t* k_clu, int clu_stride,
                          int budget, int32_t* sel_pos, int32_t* sel_count, float* scores_ws,

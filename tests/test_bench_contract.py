@@ -34,3 +34,15 @@ def test_select_and_incremental_bytes():
     b = bench.incremental_bytes(128, 400, 32752, 320)
     rows = 128 * (32752 + 320) * 4 * 256
     assert rows < b < 1.1 * rows
+
+
+def test_split_bytes():
+    # split: per split-cluster row the key once plus token id and label; the rebuild
+    # (norms, counting sort, K and V gathered and written in cluster order) dominates
+    units, K, m, rows = 128, 416, 33072, 284019
+    b = bench.split_bytes(units, K, m, rows)
+    d = 128
+    per_cluster = 8 * d + 4 + 2 * 2 * d + 2 * 8 * d + 4 * d + 4 * 2 + 4
+    assert b == units * (K * per_cluster + m * (2 * d + 8 + 12 + 8 * d)) + rows * (2 * d + 8)
+    gather = units * m * 4 * 2 * d
+    assert gather < b < 1.4 * gather
