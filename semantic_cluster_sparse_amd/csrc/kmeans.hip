@@ -235,15 +235,20 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
     }
   };
   auto compute_tile = [&](const bf16x8 (&a)[kAsResMt][4], int t) {
-    float best[kAsResMt][4];
-    int bidx[kAsResMt][4];
+    // The MFMA takes the directions as its A operand and the keys as B, so
+    // lane (r16 + 16 kg) gets directions 4 kg .. 4 kg + 3 of a block for key
+    // r16 of each M-tile: the running best of a key over a block's 4 scores
+    // is two max3 operations, and only the block index and its 4 scores are
+    // kept when the best improves (strictly, so an earlier block wins ties).
+    float best[kAsResMt];
+    int bblk[kAsResMt];
+    f32x4 bsc[kAsResMt];
 #pragma unroll
-    for (int mt = 0; mt < kAsResMt; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        best[mt][i] = -INFINITY;
-        bidx[mt][i] = 0;
-      }
+    for (int mt = 0; mt < kAsResMt; ++mt) {
+      best[mt] = -INFINITY;
+      bblk[mt] = 0;
+      bsc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
     // B operands (16 directions x 128 dims) of column block ct
     auto load_b = [&](bf16x8 (&b)[4], int ct) {
       const uint16_t* bp = csr + (ct * 16 + r16) * kAsLds + kg * 8;
@@ -257,23 +262,23 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int mt = 0; mt < kAsResMt; ++mt)
-          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt][s], b[s], o[mt], 0, 0, 0);
+          o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[s], a[mt][s], o[mt], 0, 0, 0);
     };
-    auto argmax_tile = [&](const f32x4* in, int j) {
+    auto argmax_tile = [&](const f32x4* in, int blk) {
 #pragma unroll
-      for (int mt = 0; mt < kAsResMt; ++mt)
+      for (int mt = 0; mt < kAsResMt; ++mt) {
+        const float m3 = __builtin_fmaxf(__builtin_fmaxf(in[mt][0], in[mt][1]), in[mt][2]);
+        const float m = __builtin_fmaxf(__builtin_fmaxf(m3, in[mt][3]), best[mt]);
+        const bool gt = m > best[mt];
+        bblk[mt] = gt ? blk : bblk[mt];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = in[mt][i];
-          const bool gt = v > best[mt][i];
-          best[mt][i] = gt ? v : best[mt][i];
-          bidx[mt][i] = gt ? j : bidx[mt][i];
-        }
+        for (int e = 0; e < 4; ++e) bsc[mt][e] = gt ? in[mt][e] : bsc[mt][e];
+        best[mt] = m;
+      }
     };
-    // Two accumulator sets alternate (no copies, which would wait for the
-    // MFMAs); two B buffers alternate with blocks of the same parity, each
-    // refilled right after its MFMAs issue, so an LDS read has a whole block of
-    // MFMAs and argmax work to land in.
+    // Two accumulator sets alternate; two B buffers alternate with blocks of
+    // the same parity, each refilled right after its MFMAs issue, so an LDS
+    // read has a whole block of MFMAs and argmax work to land in.
     const int nblk = (K + 15) >> 4;  // the last block may be partial (padded rows are zero)
     f32x4 acc0[kAsResMt], acc1[kAsResMt];
     bf16x8 b0[4], b1[4];
@@ -285,46 +290,48 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
     for (; ct + 1 < nblk; ct += 2) {
       mfma_tile(b1, acc1);                      // block ct (odd)
       if (ct + 2 < nblk) load_b(b1, ct + 2);
-      argmax_tile(acc0, (ct - 1) * 16 + r16);   // block ct-1
+      argmax_tile(acc0, ct - 1);                // block ct-1
       mfma_tile(b0, acc0);                      // block ct+1 (even)
       if (ct + 3 < nblk) load_b(b0, ct + 3);
-      argmax_tile(acc1, ct * 16 + r16);         // block ct
+      argmax_tile(acc1, ct);                    // block ct
     }
     // acc0 holds block ct-1; block ct (odd, in b1), if any, is the last
     const bool tail = ct < nblk;
     if (tail) mfma_tile(b1, acc1);
     auto mask_pad = [&](f32x4* acc, int blk) {  // padded directions of a partial block never win
-      if (blk * 16 + r16 >= K) {
 #pragma unroll
-        for (int mt = 0; mt < kAsResMt; ++mt) acc[mt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      }
+      for (int e = 0; e < 4; ++e)
+        if (blk * 16 + 4 * kg + e >= K) {
+#pragma unroll
+          for (int mt = 0; mt < kAsResMt; ++mt) acc[mt][e] = -INFINITY;
+        }
     };
     mask_pad(acc0, ct - 1);
-    argmax_tile(acc0, (ct - 1) * 16 + r16);
+    argmax_tile(acc0, ct - 1);
     if (tail) {
       mask_pad(acc1, ct);
-      argmax_tile(acc1, ct * 16 + r16);
+      argmax_tile(acc1, ct);
     }
-    // row results over the 16 lanes of each row group (DPP, no LDS round
-    // trips); ties go to the smaller index
+    // per key: the first of the kept block's 4 scores equal to the best, then
+    // the best over the 4 lanes of the key (xor 16, 32); ties go to the
+    // smaller index
 #pragma unroll
-    for (int mt = 0; mt < kAsResMt; ++mt)
+    for (int mt = 0; mt < kAsResMt; ++mt) {
+      float bv = best[mt];
+      const f32x4 sc = bsc[mt];
+      const int e = sc[0] == bv ? 0 : (sc[1] == bv ? 1 : (sc[2] == bv ? 2 : 3));
+      int bi = bblk[mt] * 16 + 4 * kg + e;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float bv = best[mt][i];
-        int bi = bidx[mt][i];
-        auto step = [&](float ov, int oi) {
-          const bool take = ov > bv || (ov == bv && oi < bi);
-          bv = take ? ov : bv;
-          bi = take ? oi : bi;
-        };
-        step(dpp_f32<kDppXor1>(bv), dpp_row_i32<kDppXor1>(bi));
-        step(dpp_f32<kDppXor2>(bv), dpp_row_i32<kDppXor2>(bi));
-        step(dpp_f32<kDppHalfMirror>(bv), dpp_row_i32<kDppHalfMirror>(bi));
-        step(dpp_f32<kDppMirror>(bv), dpp_row_i32<kDppMirror>(bi));
-        const int r = t * kAsResTile + mt * 16 + kg * 4 + i;
-        if (r16 == i && r < count) out[r] = bi;
+      for (int o = 16; o < 64; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        const bool take = ov > bv || (ov == bv && oi < bi);
+        bv = take ? ov : bv;
+        bi = take ? oi : bi;
       }
+      const int r = t * kAsResTile + mt * 16 + r16;
+      if (kg == 0 && r < count) out[r] = bi;
+    }
   };
 
   // tiles of this wave: t0 + wave, t0 + wave + 8, ...; two register sets alternate
