@@ -51,6 +51,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "sparse-decode tokens/s & %HBM peak at 32k ctx, 2k budget; K-means keys/s"
 
 
@@ -256,6 +257,41 @@ def full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs
             "decode_speedup": full_ms / dec_ms}
 
 
+def assign_flops(units: int, m: int, K: int) -> int:
+    """Algorithmic flops of one assignment pass: 2 m K d per unit (the distance
+    matmul; the argmax and padded directions are not counted)."""
+    return 2 * units * m * K * 128
+
+
+def time_assign(layers, cfg, units: int, stream) -> dict:
+    """The assignment step alone (ckv_assign) on every layer after the prefill,
+    between HIP events on the stream it runs on: one untimed pass over the
+    layers, then one timed pass.  The labels are saved before and put back
+    after, so the layers' state is the prefill's."""
+    import torch
+
+    saved = [L.assign.clone() for L in layers]
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for L in layers:
+        L.assign_only(cfg.n_tokens)
+    ea.record(stream)
+    for L in layers:
+        L.assign_only(cfg.n_tokens)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    for L, a in zip(layers, saved):
+        L.assign.copy_(a)
+    torch.cuda.synchronize()
+    us = ea.elapsed_time(eb) * 1e3 / len(layers)
+    flops = assign_flops(units, cfg.m, cfg.n_clusters)
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"[bench] ckv_assign {us:.1f} us per layer ({flops / 1e9:.1f} GFLOP): {tf:.0f} TFLOP/s, "
+        f"{tf / MFMA_BF16_PEAK_TFS:.3f} of the bf16 MFMA peak")
+    kernel = "ckv::assign_resident_kernel" if cfg.n_clusters <= 512 else "ckv::assign_kernel"
+    return {"bound": "mfma", "kernel": kernel, "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_BF16_PEAK_TFS, "launch_us": us, "flops_per_launch": flops}
+
+
 def run_stack(cfg, args) -> dict:
     """Decode steps through a layer stack (append_select + sparse_decode per layer),
     with ckv_cluster_incremental on every layer whenever 320 recent tokens have built up."""
@@ -306,6 +342,7 @@ def run_stack(cfg, args) -> dict:
     log(f"[bench] prefill {prefill_s * 1e3:.1f} ms wall, {prefill_ev_s * 1e3:.1f} ms events; "
         f"{keys / prefill_ev_s / 1e6:.1f} M keys/s")
     del inits
+    assign = time_assign(layers, cfg, units, stream)
     # the recent tokens past the clustered prefix are already in the token-order rows
     for L in layers:
         L.set_counters(n_fill, cfg.n_tokens)
@@ -514,6 +551,7 @@ def run_stack(cfg, args) -> dict:
         "step_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kmeans_keys_per_s": keys / prefill_ev_s,
         "prefill_ms": prefill_ev_s * 1e3,
+        "assign_roofline": assign,
         "full_attention": full,
     }
     if per_step:

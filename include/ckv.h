@@ -187,6 +187,20 @@ int ckv_cluster_incremental_async(ckv_layer* L, void* ws, size_t ws_bytes, void*
 int ckv_cluster_commit(ckv_layer* L);
 
 /*
+ * The assignment step alone (ClusterKV article §3.2 prefill, cosine K-means;
+ * §4.1 half-precision distance computation): for the tokens [n_sink, n) of
+ * every unit, a_i = argmax_j k_i . cdir_j (ties -> smallest j), written to
+ * assign[u, 0 : n - n_sink].  It is the first step of every Lloyd round of
+ * ckv_cluster_prefill (bf16 MFMA distances with the argmax fused, scores never
+ * stored), exported so that callers can run or time it on its own.  Reads
+ * k_tok rows [n_sink, n) and cdir; writes only assign, so csize, offsets,
+ * perm, the sums and the cluster-ordered rows no longer describe the labels
+ * until the next ckv_cluster_prefill.  Requires n_sink < n <= capacity and
+ * no pending ckv_cluster_incremental_async result; no workspace.
+ */
+int ckv_assign(const ckv_layer* L, int32_t n, void* stream);
+
+/*
  * Drift-triggered split (ClusterKV article §3.2, decoding-stage updates: a
  * cluster whose mean intra-cluster distance passes a threshold is split).
  * Per unit, over the clustered tokens [n_sink, n_clustered):

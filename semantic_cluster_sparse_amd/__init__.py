@@ -13,6 +13,7 @@ from .ckv import (  # noqa: F401
     CkvLayerStruct,
     ckv_abi_layer_bytes,
     ckv_append,
+    ckv_assign,
     ckv_append_select,
     ckv_cluster_commit,
     ckv_cluster_incremental,

@@ -84,6 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_cluster_incremental_async.argtypes = [LP, c_void_p, c_size_t, c_void_p]
     lib.ckv_cluster_commit.restype = c_int
     lib.ckv_cluster_commit.argtypes = [LP]
+    lib.ckv_assign.restype = c_int
+    lib.ckv_assign.argtypes = [LP, c_int32, c_void_p]
     lib.ckv_cluster_split.restype = c_int
     lib.ckv_cluster_split.argtypes = [LP, c_double, c_void_p, c_size_t, c_void_p]
     lib.ckv_select.restype = c_int
@@ -158,6 +160,10 @@ def ckv_cluster_incremental_async(layer: CkvLayerStruct, ws: int, ws_bytes: int,
 
 def ckv_cluster_commit(layer: CkvLayerStruct) -> None:
     _check("ckv_cluster_commit", load_library().ckv_cluster_commit(_ref(layer)))
+
+
+def ckv_assign(layer: CkvLayerStruct, n: int, stream: int = 0) -> None:
+    _check("ckv_assign", load_library().ckv_assign(_ref(layer), n, stream))
 
 
 def ckv_cluster_split(layer: CkvLayerStruct, threshold: float, ws: int, ws_bytes: int, stream: int = 0) -> None:

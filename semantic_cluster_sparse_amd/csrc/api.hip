@@ -308,6 +308,22 @@ int ckv_cluster_commit(ckv_layer* L) {
   return CKV_OK;
 }
 
+int ckv_assign(const ckv_layer* L, int32_t n, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (n > L->capacity) return fail(CKV_EINVAL, "n %d > capacity %d", n, L->capacity);
+  if (n <= L->n_sink) return fail(CKV_EINVAL, "n %d <= n_sink %d: no clustered token", n, L->n_sink);
+  if (L->n_pending != 0)
+    return fail(CKV_EINVAL, "an asynchronous incremental call is pending (n_pending %d): commit it first",
+                L->n_pending);
+  rc = check_ptrs("k_tok,cdir,assign", 3, L->k_tok, L->cdir, L->assign);
+  if (rc) return rc;
+  const int units = L->batch * L->n_kv_heads;
+  const hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, n - L->n_sink, L->cdir, L->n_clusters,
+                                          L->assign, L->capacity - L->n_sink, 0, units, (hipStream_t)stream);
+  return hip_status(e, "assign");
+}
+
 int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;

@@ -118,6 +118,10 @@ class Layer:
                 setattr(self, cur, t_alt)
                 setattr(self, alt, t_cur)
 
+    def assign_only(self, n: int) -> None:
+        """The assignment step alone over tokens [n_sink, n): labels only."""
+        ckv.ckv_assign(self.struct, n, _stream())
+
     def split(self, threshold: float) -> None:
         """Split drifted clusters into empty slots, then rebuild the index and rows in place."""
         ckv.ckv_cluster_split(self.struct, threshold, self.ws.data_ptr(), self.ws_bytes, _stream())

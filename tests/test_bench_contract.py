@@ -46,3 +46,8 @@ def test_split_bytes():
     assert b == units * (K * per_cluster + m * (2 * d + 8 + 12 + 8 * d)) + rows * (2 * d + 8)
     gather = units * m * 4 * 2 * d
     assert gather < b < 1.4 * gather
+
+
+def test_assign_flops_of_the_benchmark_launch():
+    # one layer of the Llama-shaped stack: 64 units x 32752 keys x 400 directions x 128 dims x 2
+    assert bench.assign_flops(64, 32752, 400) == 2 * 64 * 32752 * 400 * 128 == 214_643_507_200

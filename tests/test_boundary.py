@@ -211,3 +211,19 @@ def test_split_host_rules():
     E = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=16, n_clustered=16))
     ckv.ckv_cluster_split(E, 0.5, FAKE, 1 << 40)
     assert E.n_clustered == 16 and E.n_total == 16
+
+
+def test_assign_host_rules():
+    L = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100))
+    for n, what in ((201, "capacity"), (16, "n_sink"), (3, "n_sink")):
+        with pytest.raises(ckv.CkvError) as e:
+            ckv.ckv_assign(L, n)
+        assert e.value.code == ckv.CKV_EINVAL and what in e.value.message
+    P = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=120))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_assign(P, 100)
+    assert e.value.code == ckv.CKV_EINVAL and "pending" in e.value.message
+    L.cdir = None
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_assign(L, 100)
+    assert e.value.code == ckv.CKV_EINVAL and "cdir" in e.value.message

@@ -152,6 +152,34 @@ def test_teacher_forced_lloyd_rounds():
             assert check_state(L, u, st, xs[u], oras[u]["history"][t - 1][1], tag=f"t={t}") == 0
 
 
+@pytest.mark.parametrize("K", [400, 23])
+def test_assign_entry_teacher_forced(K):
+    """ckv_assign alone: labels of every clustered key against oracle directions
+    (a ragged last direction block at K = 23), to the assignment bar."""
+    cfg = synth.CONFIGS["llama8b-layer-32k"]
+    say(f"case: ckv_assign teacher-forced, Llama layer shape, K = {K}, units 0-1")
+    k, v, _ = synth.make_layer_inputs(cfg, units=[0, 1])
+    init = synth.make_init_indices(cfg.init_seed, 2, cfg.m, K)
+    from oracle import kmeans
+    L = gpu_layer(k, v, cfg.group, K)
+    dirs = []
+    for u in range(2):
+        xs = bf16.widen(k[u][16:cfg.n_tokens])
+        c = kmeans.init_directions(xs, init[u], K)
+        dirs.append((xs, c))
+        L.cdir[u].copy_(dev_bf16(bf16.round_rne(c)))
+    L.assign.fill_(-7)
+    L.assign_only(cfg.n_tokens)
+    torch.cuda.synchronize()
+    for u, (xs, c) in enumerate(dirs):
+        a_o = kmeans.assign(xs, c)
+        a_g = L.assign[u, :cfg.m].cpu().numpy()
+        mism, unexc = compare_assign(a_g, a_o, xs, c)
+        say(f"  unit {u}: label mismatches {mism} (unexcused {unexc}) of {cfg.m}")
+        assert unexc == 0 and mism <= MISMATCH_FRACTION * cfg.m
+    assert int((L.assign[:, cfg.m:] != -7).sum()) == 0, "ckv_assign wrote past the clustered tokens"
+
+
 def test_llama_layer_end_to_end():
     cfg = synth.CONFIGS["llama8b-layer-32k"]
     say(f"case: end-to-end {cfg.name}")
