@@ -152,10 +152,11 @@ def test_teacher_forced_lloyd_rounds():
             assert check_state(L, u, st, xs[u], oras[u]["history"][t - 1][1], tag=f"t={t}") == 0
 
 
-@pytest.mark.parametrize("K", [400, 23])
+@pytest.mark.parametrize("K", [400, 23, 700])
 def test_assign_entry_teacher_forced(K):
     """ckv_assign alone: labels of every clustered key against oracle directions
-    (a ragged last direction block at K = 23), to the assignment bar."""
+    (a ragged last direction block at K = 23; the LDS-chunked kernel at K = 700),
+    to the assignment bar."""
     cfg = synth.CONFIGS["llama8b-layer-32k"]
     say(f"case: ckv_assign teacher-forced, Llama layer shape, K = {K}, units 0-1")
     k, v, _ = synth.make_layer_inputs(cfg, units=[0, 1])
