@@ -287,6 +287,20 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
     mfma_tile(b0, acc0);                        // block 0
     if (nblk > 2) load_b(b0, 2);
     int ct = 1;
+    for (; ct + 3 < nblk; ct += 4) {            // four blocks per trip: fewer accumulator copies
+      mfma_tile(b1, acc1);                      // block ct
+      load_b(b1, ct + 2);
+      argmax_tile(acc0, ct - 1);
+      mfma_tile(b0, acc0);                      // block ct+1
+      load_b(b0, ct + 3);
+      argmax_tile(acc1, ct);
+      mfma_tile(b1, acc1);                      // block ct+2
+      if (ct + 4 < nblk) load_b(b1, ct + 4);
+      argmax_tile(acc0, ct + 1);
+      mfma_tile(b0, acc0);                      // block ct+3
+      if (ct + 5 < nblk) load_b(b0, ct + 5);
+      argmax_tile(acc1, ct + 2);
+    }
     for (; ct + 1 < nblk; ct += 2) {
       mfma_tile(b1, acc1);                      // block ct (odd)
       if (ct + 2 < nblk) load_b(b1, ct + 2);

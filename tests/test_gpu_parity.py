@@ -917,6 +917,39 @@ def test_split_without_free_slot_only_rebuilds():
     assert pairs == 0
 
 
+def test_split_more_pairs_than_workgroups_without_sinks():
+    """Every cluster with two or more members splits (threshold -1), 40 reserved
+    slots: more pairs per unit than the move kernel's 16 workgroups, so some
+    take two pairs; no sinks (token 0 is clustered too)."""
+    cfg = synth.CONFIGS["single-head-2k"]
+    U, R, n_sink = 2, 40, 0
+    say(f"case: drift split of every cluster, {R} reserved slots, n_sink = 0, {U} units")
+    from oracle import kmeans
+    k, v, _ = synth.make_layer_inputs(cfg, units=list(range(U)))
+    m = cfg.n_tokens - n_sink
+    init = np.concatenate([synth.make_init_indices(cfg.init_seed, U, m, cfg.n_clusters),
+                           np.full((U, R), -1, np.int32)], axis=1)
+    K = cfg.n_clusters + R
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], K, cfg.iters, n_sink=n_sink, v_bits=v[u])
+              for u in range(U)]
+    for st in states:   # the pairing order must not hinge on summation order
+        dr = np.sort(kmeans.drift(st["csum"], st["csize"])[st["csize"] >= 2])
+        assert len(dr) > 16 and np.min(np.diff(dr)) > 1e-12
+    oras = [pipeline.split_unit(st, k[u], -1.0, n_sink=n_sink, v_bits=v[u]) for u, st in enumerate(states)]
+    L = gpu_layer(k, v, 1, K, n_sink=n_sink)
+    load_state(L, states, n_sink=n_sink)
+    L.set_counters(cfg.n_tokens, cfg.n_tokens)
+    L.split(-1.0)
+    torch.cuda.synchronize()
+    for u, ora in enumerate(oras):
+        assert len(ora["pairs"]) > 16
+        a_g = L.assign[u, :m].cpu().numpy()
+        say(f"  unit {u}: {len(ora['pairs'])} splits, labels differing {int(np.sum(a_g != ora['assign']))}")
+        assert np.array_equal(a_g, ora["assign"]), "split labels differ"
+        x = bf16.widen(k[u][n_sink:cfg.n_tokens])
+        assert check_state(L, u, ora, x, ora["cdir"], n_sink=n_sink, tag="split-all") == 0
+
+
 def test_split_after_incremental_new_components_then_recall_and_decode():
     cfg = synth.CONFIGS["llama8b-incremental-b16"]
     U, R = 2, 16
