@@ -22,7 +22,9 @@ old clusters plus a growing recent window).
 units), 32768 clustered tokens, then 320 new keys per KV head (10% from 8
 new mixture components): times ckv_cluster_incremental, then a budget-1024
 ckv_select and ckv_sparse_decode on batch-16 queries.  Reports the
-incremental latency.
+incremental latency.  With ``--split-reserve R`` the prefill holds R cluster
+slots per unit empty and ckv_cluster_split is timed after the incremental
+call (threshold: the median drift).
 
 ``--per-head-recall`` switches the stack workloads to the other grouped-query
 reading: ckv_append + ckv_select_per_head + ckv_sparse_decode_per_head, one
@@ -30,7 +32,9 @@ recalled set per query head.
 
 The stack workloads also time a dense-decode baseline on the same harness
 (``full_attention``): budget >= m, so recall takes every cluster and the
-decode kernel attends to all cached tokens.
+decode kernel attends to all cached tokens; and the assignment step alone
+(``assign_roofline``: ckv_assign over every layer after the prefill, against
+the bf16 MFMA peak).
 
 Inputs are synthetic (seeded Gaussian-mixture keys on the GPU) and resident
 in HBM before the timed region.  Decode steps are captured once each as a HIP
