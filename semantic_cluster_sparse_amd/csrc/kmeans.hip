@@ -8,6 +8,8 @@
 // clustering during decoding), §3.1 (the centroid as the members' mean),
 // §4.1 (half-precision matrix multiply for the distances; cluster-contiguous
 // KV storage).
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -911,14 +913,16 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
     if (wpu < 1) wpu = 1;
     const int tpw = (ntiles + wpu - 1) / wpu;
     const size_t lds = (size_t)((K + 15) & ~15) * kAsLds * sizeof(uint16_t);
-    static bool lds_attr = false;  // dynamic LDS above 64 KiB must be allowed explicitly
-    if (!lds_attr) {
-      const hipError_t e = hipFuncSetAttribute((const void*)assign_resident_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)(kAsResMaxK * kAsLds * sizeof(uint16_t)));
-      if (e != hipSuccess) return e;
-      lds_attr = true;
-    }
+    // dynamic LDS above 64 KiB must be allowed explicitly; set once per
+    // process (calls may come from several host threads)
+    static std::once_flag lds_once;
+    static hipError_t lds_status = hipSuccess;
+    std::call_once(lds_once, [] {
+      lds_status = hipFuncSetAttribute((const void*)assign_resident_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kAsResMaxK * kAsLds * sizeof(uint16_t)));
+    });
+    if (lds_status != hipSuccess) return lds_status;
     hipLaunchKernelGGL(assign_resident_kernel, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds, s,
                        k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw);
     return hipGetLastError();

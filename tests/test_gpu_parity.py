@@ -220,6 +220,67 @@ def test_llama_layer_end_to_end():
     assert total_diff <= MISMATCH_FRACTION * 2 * 3 * cfg.budget
 
 
+def _random_case(rng):
+    U = int(rng.integers(1, 4))
+    n_sink = int(rng.choice([0, 5, 16]))
+    K = int(rng.integers(1, 97))
+    m = int(rng.integers(max(K, 40), 5001))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    T = int(rng.choice([1, 3]))
+    u01 = rng.random()
+    budget = 0 if u01 < 0.15 else (m + 7 if u01 > 0.85 else int(rng.integers(1, m + 1)))
+    r = int(rng.integers(0, 41))
+    C = int(rng.integers(4, 65))
+    return U, n_sink, K, m, G, T, budget, r, C
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_shapes_end_to_end(case):
+    """Seeded random shapes (units, sinks, K, m, G, rounds, budget, recent rows,
+    mixture size) through prefill, recall and decode, against the oracle; the
+    last tile, direction block, chunk and position segment are ragged."""
+    rng = np.random.default_rng(9000 + case)
+    U, n_sink, K, m, G, T, budget, r, C = _random_case(rng)
+    n = n_sink + m
+    say(f"case {case}: units {U}, n_sink {n_sink}, K {K}, m {m}, G {G}, rounds {T}, budget {budget}, "
+        f"recent {r}, components {C}")
+    parts = [synth.make_unit_inputs(9100 + case, u, n + r, C) for u in range(U)]
+    k = np.stack([p[0] for p in parts])
+    v = np.stack([p[1] for p in parts])
+    cen = np.stack([p[2] for p in parts])
+    init = synth.make_init_indices(9200 + case, U, m, K)
+    q = synth.make_queries(9300 + case, cen, G)
+    L = gpu_layer(k, v, G, K, n_sink=n_sink, max_budget=max(budget, 1))
+    L.prefill(n, T, to_dev(init, torch.int32))
+    L.set_counters(n + r, n)
+    qd = dev_bf16(q)
+    sel_pos = torch.zeros((U, max(budget, 1)), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((U,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((U, G, D), dtype=torch.float32, device="cuda")
+    L.select(qd, budget, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    sp = sel_pos.cpu().numpy()[:, :budget]
+    cn, og = cnt.cpu().numpy(), out.cpu().numpy()
+    total_mism = 0
+    for u in range(U):
+        ora = pipeline.prefill_unit(k[u], n, init[u], K, T, n_sink=n_sink, v_bits=v[u], history=True)
+        x = bf16.widen(k[u][n_sink:n])
+        mism = check_state(L, u, ora, x, ora["history"][-2][1], n_sink=n_sink, tag=f"case {case}")
+        total_mism += mism
+        if mism:
+            continue
+        assert int(cn[u]) == min(budget, m)
+        sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+        if compare_selection(L, u, sp, cn, ora, sel, budget) == 0:
+            ref = pipeline.decode_unit(q[u], k[u], v[u], ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
+                                       n_sink, n, n + r)
+            err = np.abs(og[u] - ref).max()
+            say(f"  unit {u}: decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+    assert total_mism <= max(1, MISMATCH_FRACTION * U * m)
+
+
 @pytest.mark.parametrize("K", [700, 1024])
 def test_large_k_end_to_end(K):
     # K > 512 takes the LDS-chunked assignment kernel; 1024 is the largest K the library accepts
