@@ -227,3 +227,9 @@ def test_assign_host_rules():
     with pytest.raises(ckv.CkvError) as e:
         ckv.ckv_assign(L, 100)
     assert e.value.code == ckv.CKV_EINVAL and "cdir" in e.value.message
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # the binding has no fallback: without the built library every call path raises
+    with pytest.raises(RuntimeError, match="libckv.so not found"):
+        ckv.load_library(str(tmp_path / "libckv.so"))
