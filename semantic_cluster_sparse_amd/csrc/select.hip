@@ -17,9 +17,10 @@
 // index).  The partial fill inside the cut cluster is the same selection with
 // unit weights over the q_bar.k scores of its tokens.  A crossing bucket with
 // more than 64 members, or a degenerate score range, falls back to a
-// wave-synchronous weighted radix select on the keys.  Four workgroups of
-// 1024 threads per recalled set each score a quarter of the clusters; the
-// last of them to finish (device-scope arrival counter) makes the selection.
+// wave-synchronous weighted radix select on the keys.  Several workgroups of
+// 1024 threads per recalled set (4 up to 64 sets, then about 256 per launch,
+// never fewer than K / 256) each score a share of the clusters; the last of
+// them to finish (device-scope arrival counter) makes the selection.
 // A set is one KV head's recall (q_bar over its G query heads) or, in the
 // per-query-head mode, one query head's (q_g alone).  The barriers wait on LDS
 // only, so global loads stay in flight across them.  Recalled positions are
@@ -30,7 +31,13 @@
 namespace ckv {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelSplit = 4;                  // workgroups per unit for the cluster scores
+// Workgroups per recalled set for the cluster scores: about 256 scoring
+// workgroups per launch (one per CU) when there are fewer sets, at least
+// enough to cover K with one round of row loads per workgroup, at most
+// kSelSplitMax (8 per set measured slower than 4 at 32 sets: the hand-off
+// waits for more arrivals).
+constexpr int kSelSplitMax = 4;
+constexpr int kSelRowsPerWg = 256;  // cluster rows one scoring workgroup covers
 constexpr int kSelGroups = kSelThreads / 16;  // 16-lane row groups
 constexpr int kCutLds = 4096;                 // cut-cluster keys kept in LDS up to this size
 
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int budget, int32_t* __restrict__ sel_pos, int32_t* __restrict__ sel_count, float* __restrict__ scores_ws,
     uint32_t* __restrict__ cut_ws, uint32_t* __restrict__ counters, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_tok, uint16_t* __restrict__ v_tok, int capacity,
-    int row, int hs) {
+    int row, int hs, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint32_t key[kMaxClusters];
   __shared__ __attribute__((aligned(16))) float csc[kMaxClusters];
   __shared__ __attribute__((aligned(16))) int sz[kMaxClusters];
@@ -412,9 +419,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // selection v of physical unit u: hs = 1 (one recall per KV head, q_bar over
   // its G query heads) or hs = G (one recall per query head, G passed as 1)
-  const int v = blockIdx.x / kSelSplit;
+  const int v = blockIdx.x / nsplit;
   const int u = v / hs;
-  const int part = blockIdx.x % kSelSplit;
+  const int part = blockIdx.x % nsplit;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
@@ -437,8 +444,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // centroid row, every row of the share in flight at once), stored
   // device-scope; the last workgroup of the unit to finish goes on
   constexpr int kRowsInFlight = 4;
-  static_assert(kSelGroups * kRowsInFlight * kSelSplit >= kMaxClusters, "one round covers K");
-  const int j_lo = part * K / kSelSplit, j_hi = (part + 1) * K / kSelSplit;
+  static_assert(kSelGroups * kRowsInFlight == kSelRowsPerWg, "one round of row loads covers the share");
+  const int j_lo = part * K / nsplit, j_hi = (part + 1) * K / nsplit;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
   float* sc_u = scores_ws + (size_t)v * K;
   float qb[8];
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   lds_barrier();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&counters[v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = prev == (uint32_t)(kSelSplit - 1) ? 1 : 0;
+    sh_last = prev == (uint32_t)(nsplit - 1) ? 1 : 0;
   }
   lds_barrier();
   if (!sh_last) return;
@@ -668,9 +675,14 @@ hipError_t launch_select(const uint16_t* q, int group, const float* cmean, const
                          int capacity, int row, int units, int per_head, hipStream_t s) {
   // per_head: one recall per query head (group selections per unit, each from its own q_g)
   const int hs = per_head ? group : 1;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(units * hs * kSelSplit)), dim3(kSelThreads), 0, s, q,
+  const int sets = units * hs;
+  const int need = (K + kSelRowsPerWg - 1) / kSelRowsPerWg;  // <= 4 for K <= 1024
+  int nsplit = (256 + sets - 1) / sets;
+  if (nsplit > kSelSplitMax) nsplit = kSelSplitMax;
+  if (nsplit < need) nsplit = need;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(sets * nsplit)), dim3(kSelThreads), 0, s, q,
                      per_head ? 1 : group, cmean, offsets, K, k_clu, clu_stride, budget, sel_pos, sel_count,
-                     scores_ws, cut_ws, counters, k_new, v_new, k_tok, v_tok, capacity, row, hs);
+                     scores_ws, cut_ws, counters, k_new, v_new, k_tok, v_tok, capacity, row, hs, nsplit);
   return hipGetLastError();
 }
 
