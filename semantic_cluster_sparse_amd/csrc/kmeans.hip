@@ -680,7 +680,7 @@ __global__ __launch_bounds__(256) void update_kernel(
 constexpr int kSplitWaves = 4;
 constexpr int kSplitMaxK = 1024;  // the layer's cluster limit; per-unit lists live in LDS
 constexpr int kSplitPar = 16;     // workgroups per unit in the move kernel
-constexpr int kSplitPlanUnroll = 4;
+constexpr int kSplitPlanUnroll = 8;
 constexpr int kSplitMoveWaves = 4;
 constexpr int kSplitSlotRows = 4;                              // rows per 16-lane slot in flight
 constexpr int kSplitRows = kSplitMoveWaves * 4 * kSplitSlotRows;  // rows per workgroup step
@@ -694,10 +694,11 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 __global__ __launch_bounds__(kSplitWaves * 64) void split_plan_kernel(
     int K, const double* __restrict__ csum, const int32_t* __restrict__ csize, double threshold,
     int32_t* __restrict__ plan) {
+  constexpr int kPer = kSplitMaxK / (kSplitWaves * 64);  // clusters per thread for sizes and free slots
   __shared__ double s_drift[kSplitMaxK];   // drift of a candidate, -inf otherwise
   __shared__ int s_free[kSplitMaxK];       // empty slots, ascending
+  __shared__ int s_scan[kSplitWaves + 1];
   __shared__ int s_bp[kSplitWaves];
-  __shared__ int s_counts[1];
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -706,8 +707,16 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_plan_kernel(
   const int32_t* nu = csize + (size_t)u * K;
   int32_t* pl = plan + (size_t)u * (2 * K + 1);
 
-  // |S_j|^2: 16 lanes per cluster (8 f64 each), 4 clusters per wave, and
-  // kSplitPlanUnroll of them per lane slot in flight at once
+  // sizes of clusters kPer t .. kPer t + kPer - 1 (all loads in flight), and
+  // this thread's empty ones
+  int n_own[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = kPer * tid + i;
+    n_own[i] = j < K ? nu[j] : -1;
+  }
+  // |S_j|^2 into s_drift: 16 lanes per cluster (8 f64 each), 4 clusters per
+  // wave, and kSplitPlanUnroll of them per lane slot in flight at once
   {
     const int grp = lane >> 4, sub = lane & 15;
     for (int j0 = wv * 4 + grp; j0 < K; j0 += kSplitWaves * 4 * kSplitPlanUnroll) {
@@ -726,27 +735,30 @@ __global__ __launch_bounds__(kSplitWaves * 64) void split_plan_kernel(
         for (int i = 0; i < 4; ++i) ss = fma(sv[t][i].x, sv[t][i].x, fma(sv[t][i].y, sv[t][i].y, ss));
         ss = xor_sum16(ss);
         const int j = j0 + t * kSplitWaves * 4;
-        if (sub == 0 && j < K) {
-          const int n = nu[j];
-          const double d = n > 0 ? 1.0 - sqrt(ss) / (double)n : 0.0;
-          s_drift[j] = (n >= 2 && d > threshold) ? d : -INFINITY;
-        }
+        if (sub == 0 && j < K) s_drift[j] = ss;
       }
     }
   }
-  if (wv == 0) {
-    int nfree = 0;
-    for (int base = 0; base < K; base += kWave) {
-      const int j = base + lane;
-      const bool empty = j < K && nu[j] == 0;
-      const unsigned long long fm = __ballot(empty);
-      if (empty) s_free[nfree + __popcll(fm & ((1ull << lane) - 1ull))] = j;
-      nfree += __popcll(fm);
+  int my_free = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) my_free += n_own[i] == 0 ? 1 : 0;
+  int nfree = 0;
+  // (its barriers also order the |S_j|^2 writes above before the reads below)
+  const int fo = block_exclusive_scan(my_free, s_scan, &nfree);
+#pragma unroll
+  for (int i = 0, f = fo; i < kPer; ++i)
+    if (n_own[i] == 0) s_free[f++] = kPer * tid + i;
+  // drift 1 - |S_j| / n_j of this thread's clusters; -inf unless a candidate
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = kPer * tid + i;
+    if (j < K) {
+      const int n = n_own[i];
+      const double d = n > 0 ? 1.0 - sqrt(s_drift[j]) / (double)n : 0.0;
+      s_drift[j] = (n >= 2 && d > threshold) ? d : -INFINITY;
     }
-    if (lane == 0) s_counts[0] = nfree;
   }
   __syncthreads();
-  const int nfree = s_counts[0];
   int my_cand = 0;
   for (int j = tid; j < K; j += kSplitWaves * 64) {
     const double dj = s_drift[j];
