@@ -8,7 +8,7 @@
 
 namespace ckv {
 
-constexpr int kSortTile = 2048;     // clustered tokens per histogram / scatter tile
+constexpr int kSortTile = 4096;     // clustered tokens per histogram / scatter tile
 constexpr int kMaxClusters = 1024;  // K limit of the LDS-resident per-cluster arrays
 constexpr int kMaxGroup = 16;
 constexpr int kMaxChunks = 64;      // split-K chunks per unit in sparse decode
