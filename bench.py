@@ -175,15 +175,14 @@ def split_bytes(units: int, K: int, m: int, split_rows: int) -> int:
     cluster, its members' keys once (256 B per row; the seed search and the
     move both need them, but one read suffices) and their token ids, and
     writes their labels (4 + 4 B per row).  The rebuild that
-    follows is the incremental call's without new keys: norms of every
-    clustered key (256 B read, 8 B written), labels read twice and the index
-    written, K and V rows gathered and written in cluster order, and the
-    per-cluster state rewritten.
+    follows: labels read twice and the index written, K and V rows gathered
+    and written in cluster order (each key's norm is taken from the row as it
+    passes), and the per-cluster state rewritten.
     """
     d = 128
     per_cluster = 8 * d + 4 + 2 * 2 * d + 8 * d * 2 + 4 * d + 4 * 2 + 4
     split = split_rows * (2 * d + 4 + 4)
-    rebuild = m * (2 * d + 8 + 4 + 4 + 4 + 4 * 2 * d)
+    rebuild = m * (4 + 4 + 4 + 4 * 2 * d)
     return units * (K * per_cluster + rebuild) + split
 
 

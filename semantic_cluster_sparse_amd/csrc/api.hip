@@ -347,23 +347,21 @@ int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes,
   const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
   const Layout w = layout_of(L);
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
-  double* invn = (double*)((char*)ws + w.off_invn);
 
   // The pair plan, units x (2K + 1) int32, sits at the start of the histogram
-  // and norm regions (at least 12 K bytes per unit between them); the norm and
-  // histogram kernels below overwrite it only after the split has used it.
+  // and norm regions (at least 12 K bytes per unit between them); the
+  // histogram kernel below overwrites it only after the split has used it.
   int32_t* plan = hist;
   hipError_t e = ckv::launch_split(L->k_clu, L->n_sink, L->perm, clu_stride, L->offsets, K, L->csum,
                                    L->csize, L->cdir, threshold, plan, L->assign, units, s);
   if (e != hipSuccess) return hip_status(e, "split");
-  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, 0, m, invn, clu_stride, units, s);
-  if (e != hipSuccess) return hip_status(e, "norms");
+  // one pass over the keys follows: the update takes each key's norm from the row itself
   e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
   if (e != hipSuccess) return hip_status(e, "hist");
   e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
   if (e != hipSuccess) return hip_status(e, "scatter");
   e = ckv::launch_update(ckv::kUpdFinal, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride,
-                         L->offsets, K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu,
+                         L->offsets, K, nullptr, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu,
                          units, s);
   if (e != hipSuccess) return hip_status(e, "update");
   return CKV_OK;

@@ -535,7 +535,11 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restric
 // sort last in their cluster), keeps the old sums, refreshes touched clusters
 // and rewrites every row.
 // ---------------------------------------------------------------------------
-template <int MODE>
+// OWN_NORMS: 1/|x| of each row is computed from the row itself (the 16 lanes
+// that hold it, in the same order as inv_norm_kernel, so the value is the
+// same) instead of being read from invn; for a single pass over the keys this
+// saves the separate norm pass.
+template <int MODE, bool OWN_NORMS>
 __global__ __launch_bounds__(256) void update_kernel(
     const uint16_t* __restrict__ k_tok, const uint16_t* __restrict__ v_tok, int capacity, int n_sink,
     const int32_t* __restrict__ perm, int clu_stride, const int32_t* __restrict__ offsets, int K,
@@ -561,7 +565,7 @@ __global__ __launch_bounds__(256) void update_kernel(
   for (int t = 0; t < 8; ++t) s[t] = mm[t] = 0.0;
 
   const int32_t* pu = perm + (size_t)u * clu_stride;
-  const double* iu = invn + (size_t)u * clu_stride;
+  const double* iu = OWN_NORMS ? nullptr : invn + (size_t)u * clu_stride;
   const uint16_t* ku = k_tok + (size_t)u * capacity * kHeadDim + li * 8;
   const uint16_t* vu = v_tok + (size_t)u * capacity * kHeadDim + li * 8;
   for (int p0 = lo; p0 < hi; p0 += 16) {
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(256) void update_kernel(
     if (lane < 16 && pl < hi) {
       tk = pu[pl];
       tk = tk < n_sink ? n_sink : (tk >= capacity ? capacity - 1 : tk);
-      if (pl >= acc_from) iv = iu[tk - n_sink];
+      if (!OWN_NORMS && pl >= acc_from) iv = iu[tk - n_sink];
     }
     int tks[4];
     double ivs[4];
@@ -603,9 +607,17 @@ __global__ __launch_bounds__(256) void update_kernel(
       x[2] = bf16_lo(kx[k].y); x[3] = bf16_hi(kx[k].y);
       x[4] = bf16_lo(kx[k].z); x[5] = bf16_hi(kx[k].z);
       x[6] = bf16_lo(kx[k].w); x[7] = bf16_hi(kx[k].w);
+      double ivk = ivs[k];
+      if (OWN_NORMS) {
+        double n2 = 0.0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
+        n2 = xor_sum16(n2);
+        ivk = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+      }
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        s[t] = fma(x[t], ivs[k], s[t]);
+        s[t] = fma(x[t], ivk, s[t]);
         if (MODE != kUpdIter) mm[t] += x[t];
       }
     }
@@ -975,15 +987,20 @@ hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok,
                          uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units, hipStream_t s) {
   const long waves = (long)units * K;
   const dim3 grid((unsigned)((waves + 3) / 4));
-#define CKV_UPD(M)                                                                                  \
-  hipLaunchKernelGGL(update_kernel<M>, grid, dim3(256), 0, s, k_tok, v_tok, capacity, n_sink, perm, \
-                     clu_stride, offsets, K, invn, csum, msum, cmean, csize, cdir, k_dst, v_dst, units)
-  if (mode == kUpdIter)
-    CKV_UPD(kUpdIter);
-  else if (mode == kUpdFinal)
-    CKV_UPD(kUpdFinal);
-  else
-    CKV_UPD(kUpdIncr);
+#define CKV_UPD(M, O)                                                                                     \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(update_kernel<M, O>), grid, dim3(256), 0, s, k_tok, v_tok, capacity, \
+                     n_sink, perm, clu_stride, offsets, K, invn, csum, msum, cmean, csize, cdir, k_dst, v_dst, \
+                     units)
+  if (invn == nullptr) {  // norms from the rows themselves: the final mode only
+    if (mode != kUpdFinal) return hipErrorInvalidValue;
+    CKV_UPD(kUpdFinal, true);
+  } else if (mode == kUpdIter) {
+    CKV_UPD(kUpdIter, false);
+  } else if (mode == kUpdFinal) {
+    CKV_UPD(kUpdFinal, false);
+  } else {
+    CKV_UPD(kUpdIncr, false);
+  }
 #undef CKV_UPD
   return hipGetLastError();
 }
