@@ -1049,3 +1049,62 @@ def test_split_after_incremental_new_components_then_recall_and_decode():
             err = np.abs(og[u] - ref).max()
             say(f"  unit {u}: decode max abs err {err:.3g}")
             assert err <= DECODE_ATOL
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+
+def test_graph_replay_matches_eager():
+    """Recall + decode captured once in a HIP graph and replayed three times, with
+    other eager recall / decode work and torch work between the replays: every
+    replay's positions, counts and outputs equal the eager call's bit for bit."""
+    U, G, K, m, r, budget = 6, 4, 48, 4000, 9, 512
+    n = 16 + m
+    say(f"case: graph replay of recall + decode, {U} units, G = {G}, K = {K}, m = {m}, {r} recent rows")
+    parts = [synth.make_unit_inputs(7100, u, n + r, 32) for u in range(U)]
+    k = np.stack([p[0] for p in parts])
+    v = np.stack([p[1] for p in parts])
+    cen = np.stack([p[2] for p in parts])
+    init = synth.make_init_indices(7200, U, m, K)
+    L = gpu_layer(k, v, G, K, max_budget=budget)
+    L.prefill(n, 3, to_dev(init, torch.int32))
+    L.set_counters(n + r, n)
+    q0 = dev_bf16(synth.make_queries(7300, cen, G))
+    q1 = dev_bf16(synth.make_queries(7301, cen, G))
+
+    def buffers():
+        return (torch.zeros((U, budget), dtype=torch.int32, device="cuda"),
+                torch.zeros((U,), dtype=torch.int32, device="cuda"),
+                torch.zeros((U, G, D), dtype=torch.float32, device="cuda"))
+
+    def run(q, bufs):
+        L.select(q, budget, bufs[0], bufs[1])
+        L.sparse_decode(q, bufs[0], bufs[1], budget, bufs[2])
+
+    eager, other, static = buffers(), buffers(), buffers()
+    run(q0, eager)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(q0, static)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(q0, static)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run(q1, other)                      # eager work on the same layer and workspace
+        _ = (other[2] * 2.0).sum()          # and some torch work
+        for t in static:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}: positions equal {torch.equal(static[0], eager[0])}, "
+            f"outputs equal {torch.equal(static[2], eager[2])}")
+        assert torch.equal(static[1], eager[1])
+        assert torch.equal(static[0], eager[0])
+        assert torch.equal(static[2], eager[2])
+    assert not torch.equal(other[2], eager[2])      # the other query really differs
