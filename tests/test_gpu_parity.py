@@ -1054,14 +1054,17 @@ def test_split_after_incremental_new_components_then_recall_and_decode():
 # ------------------------------------------------------------------ HIP graphs
 
 
-def test_graph_replay_matches_eager():
-    """Recall + decode captured once in a HIP graph and replayed three times, with
-    other eager recall / decode work and torch work between the replays: every
-    replay's positions, counts and outputs equal the eager call's bit for bit."""
+@pytest.mark.parametrize("append", [False, True])
+def test_graph_replay_matches_eager(append):
+    """Recall + decode (or the bench's step: fused append + recall, then decode)
+    captured once in a HIP graph and replayed three times, with other eager
+    recall / decode work and torch work between the replays: every replay's
+    positions, counts and outputs equal the eager call's bit for bit."""
     U, G, K, m, r, budget = 6, 4, 48, 4000, 9, 512
     n = 16 + m
-    say(f"case: graph replay of recall + decode, {U} units, G = {G}, K = {K}, m = {m}, {r} recent rows")
-    parts = [synth.make_unit_inputs(7100, u, n + r, 32) for u in range(U)]
+    say(f"case: graph replay of {'append + ' if append else ''}recall + decode, {U} units, G = {G}, "
+        f"K = {K}, m = {m}, {r} recent rows")
+    parts = [synth.make_unit_inputs(7100, u, n + r, 32, capacity=n + r + 1) for u in range(U)]
     k = np.stack([p[0] for p in parts])
     v = np.stack([p[1] for p in parts])
     cen = np.stack([p[2] for p in parts])
@@ -1071,28 +1074,35 @@ def test_graph_replay_matches_eager():
     L.set_counters(n + r, n)
     q0 = dev_bf16(synth.make_queries(7300, cen, G))
     q1 = dev_bf16(synth.make_queries(7301, cen, G))
+    new_rows = synth.make_unit_inputs(7400, 0, U, 32)
+    k_new, v_new = dev_bf16(new_rows[0]), dev_bf16(new_rows[1])
 
     def buffers():
         return (torch.zeros((U, budget), dtype=torch.int32, device="cuda"),
                 torch.zeros((U,), dtype=torch.int32, device="cuda"),
                 torch.zeros((U, G, D), dtype=torch.float32, device="cuda"))
 
-    def run(q, bufs):
-        L.select(q, budget, bufs[0], bufs[1])
+    def run(q, bufs, with_append=False):
+        if with_append:   # the decoded token's row n + r, then n_total = n + r + 1
+            L.append_select(k_new, v_new, q, budget, bufs[0], bufs[1])
+        else:
+            L.select(q, budget, bufs[0], bufs[1])
         L.sparse_decode(q, bufs[0], bufs[1], budget, bufs[2])
 
     eager, other, static = buffers(), buffers(), buffers()
-    run(q0, eager)
+    run(q0, eager, append)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
+    L.set_counters(n + r, n)
     with torch.cuda.stream(side):
-        run(q0, static)
+        run(q0, static, append)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    L.set_counters(n + r, n)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        run(q0, static)
+        run(q0, static, append)
     torch.cuda.synchronize()
     for rep in range(3):
         run(q1, other)                      # eager work on the same layer and workspace
