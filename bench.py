@@ -291,8 +291,11 @@ def time_assign(layers, cfg, units: int, stream) -> dict:
     log(f"[bench] ckv_assign {us:.1f} us per layer ({flops / 1e9:.1f} GFLOP): {tf:.0f} TFLOP/s, "
         f"{tf / MFMA_BF16_PEAK_TFS:.3f} of the bf16 MFMA peak")
     kernel = "ckv::assign_resident_kernel" if cfg.n_clusters <= 512 else "ckv::assign_kernel"
+    # keys through the assignment step per second (one pass per Lloyd round)
+    keys_per_s = units * cfg.m / (us * 1e-6)
     return {"bound": "mfma", "kernel": kernel, "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-            "frac": tf / MFMA_BF16_PEAK_TFS, "launch_us": us, "flops_per_launch": flops}
+            "frac": tf / MFMA_BF16_PEAK_TFS, "launch_us": us, "flops_per_launch": flops,
+            "keys_per_s": keys_per_s}
 
 
 def run_stack(cfg, args) -> dict:
