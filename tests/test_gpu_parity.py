@@ -359,23 +359,29 @@ def test_select_teacher_forced():
         say(f"  budget {budget}: ok")
 
 
-def test_per_head_recall_and_decode():
-    cfg = synth.CONFIGS["llama8b-layer-32k"]
-    budget = 1024
-    say(f"case: per-query-head recall + decode, Llama layer shape, units 0-3, G={cfg.group}, budget {budget}")
-    units = [0, 1, 2, 3]
+@pytest.mark.parametrize("shape", ["llama8b-layer-32k", "glm4-stack-32k-b16"])
+def test_per_head_recall_and_decode(shape):
+    """Per-query-head recall + decode, teacher-forced: the Llama layer (G = 4, units 0-3,
+    budget 1024) and the GLM4-shaped layer (G = 16, 410 clusters, 300 recent rows, units
+    0-1, budget 2048)."""
+    cfg = synth.CONFIGS[shape]
+    budget = 1024 if shape.startswith("llama") else cfg.budget
+    units = [0, 1, 2, 3] if shape.startswith("llama") else [0, 1]
+    n_all = cfg.n_tokens + cfg.n_recent
+    say(f"case: per-query-head recall + decode, {shape}, units {units}, G={cfg.group}, budget {budget}, "
+        f"{cfg.n_recent} recent rows")
     U = len(units)
     k, v, cen = synth.make_layer_inputs(cfg, units=units)
     init = synth.make_init_indices(cfg.init_seed, U, cfg.m, cfg.n_clusters)
     states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], cfg.n_clusters, 2, v_bits=v[u])
               for u in range(U)]
     q = synth.make_queries(cfg.query_seed, cen, cfg.group)
-    Lh = Layer(batch=U, n_kv_heads=1, group=cfg.group, n_clusters=cfg.n_clusters, capacity=cfg.n_tokens,
+    Lh = Layer(batch=U, n_kv_heads=1, group=cfg.group, n_clusters=cfg.n_clusters, capacity=k.shape[1],
                max_budget=budget, incremental=False, per_head=True)
     Lh.k_tok.copy_(dev_bf16(k))
     Lh.v_tok.copy_(dev_bf16(v))
     load_state(Lh, states)
-    Lh.set_counters(cfg.n_tokens, cfg.n_tokens)
+    Lh.set_counters(n_all, cfg.n_tokens)
     qd = dev_bf16(q)
     S = U * cfg.group
     sel_pos = torch.full((S, budget), -1, dtype=torch.int32, device="cuda")
@@ -403,7 +409,7 @@ def test_per_head_recall_and_decode():
         distinct += len({tuple(x["positions"].tolist()) for x in sels}) > 1
         if ok:
             ref = pipeline.decode_per_head(q[u], k[u], v[u], st["k_clu_bits"], st["v_clu_bits"],
-                                           [x["positions"] for x in sels], 16, cfg.n_tokens, cfg.n_tokens)
+                                           [x["positions"] for x in sels], 16, cfg.n_tokens, n_all)
             err = np.abs(og[u] - ref).max()
             say(f"  unit {u}: per-head decode max abs err {err:.3g}")
             assert err <= DECODE_ATOL
