@@ -1017,6 +1017,24 @@ def test_split_more_pairs_than_workgroups_without_sinks():
         assert check_state(L, u, ora, x, ora["cdir"], n_sink=n_sink, tag="split-all") == 0
 
 
+def test_split_many_clusters():
+    """700 slots (600 clusters of about 3 keys plus 100 reserved): the plan kernel's
+    size, free-slot and ranking passes cover more clusters than its 256 threads."""
+    cfg = synth.CONFIGS["single-head-2k"]
+    U, R, K0 = 2, 100, 600
+    say(f"case: drift split with {K0} clusters + {R} reserved slots, {U} units")
+    k, v, _ = synth.make_layer_inputs(cfg, units=list(range(U)))
+    init = np.concatenate([synth.make_init_indices(cfg.init_seed, U, cfg.m, K0),
+                           np.full((U, R), -1, np.int32)], axis=1)
+    K = K0 + R
+    states = [pipeline.prefill_unit(k[u], cfg.n_tokens, init[u], K, 3, v_bits=v[u]) for u in range(U)]
+    L = gpu_layer(k, v, 1, K)
+    load_state(L, states)
+    L.set_counters(cfg.n_tokens, cfg.n_tokens)
+    _, pairs = _check_split(L, states, k, v, _split_threshold(states, 0.5), "split-700")
+    assert pairs == U * R
+
+
 def test_split_after_incremental_new_components_then_recall_and_decode():
     cfg = synth.CONFIGS["llama8b-incremental-b16"]
     U, R = 2, 16
