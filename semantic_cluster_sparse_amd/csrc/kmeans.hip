@@ -501,9 +501,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Inverse key norms 1/|x| (f64) of clustered tokens [first, first + count):
-// 16 lanes per row.  Computed once per prefill / incremental call; the
-// update kernels reuse them every Lloyd round.
+// 16 lanes per row, kNormRows rows per 16-lane group with all their loads in
+// flight (a workgroup covers 16 * kNormRows consecutive rows, each load
+// instruction of it 16 consecutive rows).  Computed once per prefill /
+// incremental call; the update kernels reuse them every Lloyd round.
 // ---------------------------------------------------------------------------
+constexpr int kNormRows = 4;
+
 __global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restrict__ k_tok, int capacity,
                                                        int n_sink, int first, int count,
                                                        double* __restrict__ invn, int clu_stride,
@@ -511,18 +515,26 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restric
   const int u = blockIdx.x / rows_per_unit_blocks;
   const int b = blockIdx.x % rows_per_unit_blocks;
   const int li = threadIdx.x & 15;
-  const int i = b * 16 + (threadIdx.x >> 4);
-  const bool ok = i < count;
-  const int tok = n_sink + first + (ok ? i : 0);
-  const uint4 w = *reinterpret_cast<const uint4*>(k_tok + ((size_t)u * capacity + tok) * kHeadDim + li * 8);
-  double x[8];
-  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  double n2 = 0.0;
+  const int i0 = b * (16 * kNormRows) + (threadIdx.x >> 4);
+  const uint16_t* ku = k_tok + ((size_t)u * capacity + n_sink + first) * kHeadDim + li * 8;
+  uint4 w[kNormRows];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
-  n2 = xor_sum16(n2);
-  if (ok && li == 0) invn[(size_t)u * clu_stride + first + i] = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+  for (int k = 0; k < kNormRows; ++k) {
+    const int i = i0 + 16 * k;
+    w[k] = *reinterpret_cast<const uint4*>(ku + (size_t)(i < count ? i : 0) * kHeadDim);
+  }
+#pragma unroll
+  for (int k = 0; k < kNormRows; ++k) {
+    const int i = i0 + 16 * k;
+    double x[8];
+    x[0] = bf16_lo(w[k].x); x[1] = bf16_hi(w[k].x); x[2] = bf16_lo(w[k].y); x[3] = bf16_hi(w[k].y);
+    x[4] = bf16_lo(w[k].z); x[5] = bf16_hi(w[k].z); x[6] = bf16_lo(w[k].w); x[7] = bf16_hi(w[k].w);
+    double n2 = 0.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
+    n2 = xor_sum16(n2);
+    if (i < count && li == 0) invn[(size_t)u * clu_stride + first + i] = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -975,7 +987,7 @@ hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int 
 hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int first, int count,
                            double* invn, int clu_stride, int units, hipStream_t s) {
   if (count <= 0) return hipSuccess;
-  const int blocks = (count + 15) / 16;
+  const int blocks = (count + 16 * kNormRows - 1) / (16 * kNormRows);
   hipLaunchKernelGGL(inv_norm_kernel, dim3((unsigned)(units * blocks)), dim3(256), 0, s, k_tok, capacity,
                      n_sink, first, count, invn, clu_stride, blocks);
   return hipGetLastError();
