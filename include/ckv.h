@@ -133,9 +133,12 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Append one decoded token per unit: k_new, v_new are bf16 [units, 128]
+ * Append one decoded token per unit (ClusterKV article §3.2, decoding-stage
+ * updates: every generated token's key and value join the cache; it stays
+ * unclustered, and is attended as a recent row, until the next incremental
+ * clustering pass takes it in).  k_new, v_new are bf16 [units, 128]
  * (device).  Writes row n_total of k_tok / v_tok and advances n_total.
- * CKV_ENOSPACE if n_total == capacity.
+ * CKV_ENOSPACE if n_total == capacity (nothing is written).
  */
 int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void* stream);
 

@@ -106,12 +106,6 @@ def init_directions(x: np.ndarray, init_idx: np.ndarray, round_bf16: bool = True
     return out
 
 
-def objective(x: np.ndarray, a: np.ndarray, cdir: np.ndarray) -> float:
-    """Cosine K-means objective ``J = sum_i (1 - x^_i . c_{a_i})``."""
-    xh = normalise(x)
-    return float(np.sum(1.0 - np.sum(xh * np.asarray(cdir)[a], axis=1)))
-
-
 def lloyd(x: np.ndarray, init_idx: np.ndarray, iters: int, round_bf16: bool = True,
           history: bool = False):
     """``iters`` Lloyd rounds of cosine K-means on the clustered keys ``x`` [m, d].

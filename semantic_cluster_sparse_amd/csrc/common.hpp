@@ -37,6 +37,16 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(sign | (__float_as_uint((float)r) >> 16));
 }
 
+// Wait until every vector memory operation this wave has issued is complete
+// (on gfx9 vmcnt counts stores too, so stores are acknowledged by the memory
+// side), and keep the compiler from moving any memory access across this
+// point.  A workgroup runs it before moving a device-scope arrival counter,
+// so its agent-scope stores (which write through to the coherence point) are
+// visible to whichever workgroup sees the counter's final value.
+__device__ __forceinline__ void drain_memory_ops() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
 // Lane id within the wave.
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 

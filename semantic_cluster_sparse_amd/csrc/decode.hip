@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
       __hip_atomic_store(&outp[kHeadDim + 1], wL, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  drain_memory_ops();
   __syncthreads();
   __shared__ int sh_last;
   if (tid == 0) {

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
   }
   // this workgroup's stores are complete before the arrival count moves
-  __builtin_amdgcn_s_waitcnt(0);
+  drain_memory_ops();
   lds_barrier();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(&counters[v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -20,4 +20,5 @@ from .mixture import (  # noqa: F401
     make_queries,
     make_init_indices,
     make_new_tokens,
+    make_planted_groups,
 )

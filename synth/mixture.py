@@ -223,3 +223,27 @@ def make_new_tokens(seed: int, centres: np.ndarray, count: int, new_components: 
         ks[i] = f64_to_bf16_bits(k)
         vs[i] = f64_to_bf16_bits(v)
     return ks, vs, nc
+
+
+def make_planted_groups(seed: int, sizes: list[int], n_sink: int = 16, d: int = HEAD_DIM,
+                        radius: float = 8.0, sigma: float = 1.0, extra_rows: int = 0):
+    """One unit whose clustered keys form well separated groups of the given sizes.
+
+    Group ``g`` has centre ``radius * c_g`` with ``c_g`` a random unit vector;
+    its keys are ``centre + N(0, sigma^2 I)``.  The ``n_sink`` sink keys and
+    ``extra_rows`` rows after the clustered ones come from the groups too.  The
+    clustered tokens' group labels are shuffled over token order.  Returns
+    ``(k_bits [n, d], v_bits [n, d], centres [G, d], labels [m])`` with
+    ``n = n_sink + sum(sizes) + extra_rows`` and ``labels`` the group of
+    clustered token ``i`` (token id ``n_sink + i``).
+    """
+    rng = np.random.default_rng([seed, 11])
+    centres = _centres(rng, len(sizes), d, radius)
+    labels = np.concatenate([np.full(sz, g, np.int64) for g, sz in enumerate(sizes)])
+    labels = labels[rng.permutation(len(labels))]
+    z_sink = rng.integers(0, len(sizes), size=n_sink)
+    z_extra = rng.integers(0, len(sizes), size=extra_rows)
+    z = np.concatenate([z_sink, labels, z_extra])
+    k = centres[z] + sigma * rng.standard_normal((len(z), d))
+    v = rng.standard_normal((len(z), d))
+    return f64_to_bf16_bits(k), f64_to_bf16_bits(v), centres, labels

@@ -1,0 +1,200 @@
+"""GPU parity on the long paths the benchmark launches, against the float64 oracle.
+
+The decode kernel stages the positions of a chunk in segments of 1024 rows;
+a chunk longer than that restages them between segments.  The recall kernel
+keeps the scores of a cut cluster of up to 4096 tokens in LDS and goes
+through the workspace above that.  These tests run exactly those launches:
+
+* the dense decode (budget >= m) on one full Llama-stack layer: 64 units,
+  chunks of 8208 rows (nine segments);
+* per-query-head recall + decode at the same layer shape: 256 sets, one
+  chunk of 2096 rows per set (three segments);
+* a recall whose cut cluster holds 6000 tokens.
+
+Bars as in test_gpu_parity: same recalled token sets unless the oracle's
+boundary has a near-tie, decode within 2e-3 of float64.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import DECODE_ATOL, SELECT_GAP, dev_bf16, host_bits, say, selection_boundary_gap, to_dev
+from oracle import attention, bf16, pipeline
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from semantic_cluster_sparse_amd.layer import Layer  # noqa: E402
+
+D = 128
+RECENT = 25          # unclustered rows after the prefix, as after some decode steps
+SAMPLED = (9, 50)    # units checked against the oracle
+
+
+@pytest.fixture(scope="module")
+def stack_layer():
+    """One full layer of the 32-layer Llama stack: 64 units x 32768 clustered
+    tokens (10 Lloyd rounds on the GPU) plus RECENT unclustered rows, and the
+    oracle's prefill of the sampled units."""
+    cfg = synth.CONFIGS["llama8b-stack-32k-b8"]
+    n, cap = cfg.n_tokens, cfg.n_tokens + RECENT + 7
+    say(f"setup: full layer of {cfg.name} ({cfg.units} units, {n} + {RECENT} rows)")
+    k, v, cen = synth.make_layer_inputs(cfg, capacity=cap)
+    kr, vr, _ = synth.make_new_tokens(cfg.data_seed + 5, cen, RECENT, 0, 0.0)
+    k[:, n:n + RECENT] = kr
+    v[:, n:n + RECENT] = vr
+    init = synth.make_init_indices(cfg.init_seed, cfg.units, cfg.m, cfg.n_clusters)
+    q = synth.make_queries(cfg.query_seed, cen, cfg.group)
+    L = Layer(batch=cfg.units, n_kv_heads=1, group=cfg.group, n_clusters=cfg.n_clusters, capacity=cap,
+              max_budget=cfg.m, per_head=True)
+    L.k_tok.copy_(dev_bf16(k))
+    L.v_tok.copy_(dev_bf16(v))
+    L.prefill(n, cfg.iters, to_dev(init, torch.int32))
+    L.set_counters(n + RECENT, n)
+    torch.cuda.synchronize()
+    oras = {}
+    for u in SAMPLED:
+        oras[u] = pipeline.prefill_unit(k[u], n, init[u], cfg.n_clusters, cfg.iters, v_bits=v[u])
+        labels = L.assign[u, :cfg.m].cpu().numpy()
+        say(f"  unit {u}: prefill labels differ from the oracle's in {int((labels != oras[u]['assign']).sum())}")
+    return dict(cfg=cfg, L=L, k=k, v=v, q=q, oras=oras, n=n, n_total=n + RECENT)
+
+
+def test_dense_decode_full_layer(stack_layer):
+    """budget >= m: recall takes every cluster and decode attends to every token,
+    in the launch the benchmark's dense baseline uses (4 chunks of 8208 rows per unit)."""
+    st = stack_layer
+    cfg, L, q = st["cfg"], st["L"], st["q"]
+    m, units, n_total = cfg.m, cfg.units, st["n_total"]
+    say(f"case: dense decode, {units} units, budget {m}, {n_total} attended rows per unit")
+    qd = dev_bf16(q)
+    sel_pos = torch.full((units, m), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((units,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((units, cfg.group, D), dtype=torch.float32, device="cuda")
+    L.select(qd, m, sel_pos, cnt)
+    L.sparse_decode(qd, sel_pos, cnt, m, out)
+    torch.cuda.synchronize()
+    assert np.all(cnt.cpu().numpy() == m)
+    assert torch.equal(sel_pos, torch.arange(m, dtype=torch.int32, device="cuda").expand(units, m))
+    og = out.cpu().numpy()
+    for u in (0, 21, 63) + SAMPLED:
+        ref = attention.attend(bf16.widen(q[u]), bf16.widen(st["k"][u][:n_total]), bf16.widen(st["v"][u][:n_total]))
+        err = float(np.abs(og[u] - ref).max())
+        say(f"  unit {u}: dense decode max abs err {err:.3g}")
+        assert err <= DECODE_ATOL
+
+
+def test_per_head_recall_decode_full_layer(stack_layer):
+    """One recalled set per query head at the benchmark's layer shape: 256 sets,
+    one chunk of 2096 rows each."""
+    st = stack_layer
+    cfg, L, q = st["cfg"], st["L"], st["q"]
+    G, units, budget, n, n_total = cfg.group, cfg.units, cfg.budget, st["n"], st["n_total"]
+    say(f"case: per-head recall + decode, {units * G} sets, budget {budget}, {RECENT} recent rows")
+    qd = dev_bf16(q)
+    sel_pos = torch.full((units * G, budget), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((units * G,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((units, G, D), dtype=torch.float32, device="cuda")
+    L.select_per_head(qd, budget, sel_pos, cnt)
+    L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    assert np.all(cnt.cpu().numpy() == budget)
+    sp, og = sel_pos.cpu().numpy(), out.cpu().numpy()
+    compared = 0
+    for u, ora in st["oras"].items():
+        if not np.array_equal(L.assign[u, :cfg.m].cpu().numpy(), ora["assign"]):
+            continue
+        assert np.array_equal(host_bits(L.k_clu[u, :cfg.m]), ora["k_clu_bits"])
+        sels = pipeline.select_per_head(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+        positions = []
+        for g, sel in enumerate(sels):
+            pos_g = sp[u * G + g, :budget]
+            assert np.all(np.diff(pos_g) > 0)
+            if not np.array_equal(pos_g, sel["positions"]):
+                gap = selection_boundary_gap(sel, bf16.widen(ora["k_clu_bits"]), ora["offsets"])
+                say(f"  unit {u} head {g}: recall differs; boundary gap {gap:.3g}")
+                assert gap <= SELECT_GAP
+            positions.append(pos_g)
+        ref = pipeline.decode_per_head(q[u], st["k"][u], st["v"][u], ora["k_clu_bits"], ora["v_clu_bits"],
+                                       positions, 16, n, n_total)
+        err = float(np.abs(og[u] - ref).max())
+        say(f"  unit {u}: per-head decode max abs err {err:.3g}")
+        assert err <= DECODE_ATOL
+        compared += 1
+    assert compared >= 1, "no sampled unit's state matched the oracle's"
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_recall_cut_cluster_above_lds(per_head):
+    """Three well separated groups of 1000, 6000 and 5000 keys, ranked in that
+    order by the query; budget 3000 takes the first whole and cuts the 6000-key
+    cluster, whose token scores go through the workspace (more than 4096)."""
+    sizes, G, budget, n_sink, recent = [1000, 6000, 5000], 4, 3000, 16, 9
+    say(f"case: cut cluster of {sizes[1]} tokens, budget {budget}, per_head={per_head}")
+    k0, v0, cen, labels = synth.make_planted_groups(61, sizes, n_sink=n_sink, extra_rows=recent)
+    nc = n_sink + sum(sizes)
+    n_total = nc + recent
+    init = np.array([int(np.nonzero(labels == g)[0][0]) for g in range(3)], np.int32)
+    ora = pipeline.prefill_unit(k0, nc, init, 3, 2, n_sink=n_sink, v_bits=v0)
+    assert np.array_equal(ora["assign"], labels), "the planted groups are the oracle's clusters"
+    # each head near 2 c_A + c_B (unit directions), so q_bar ranks A, then B, then C
+    rng = np.random.default_rng(62)
+    dirs = cen / np.linalg.norm(cen, axis=1, keepdims=True)
+    qv = 2.0 * dirs[0] + 1.0 * dirs[1] + 0.05 * rng.standard_normal((G, D))
+    q = synth.f64_to_bf16_bits(qv)[None]
+    L = Layer(batch=1, n_kv_heads=1, group=G, n_clusters=3, capacity=n_total + 3, max_budget=budget,
+              per_head=True)
+    L.k_tok[:, :n_total].copy_(dev_bf16(k0[None]))
+    L.v_tok[:, :n_total].copy_(dev_bf16(v0[None]))
+    m = nc - n_sink
+    L.cdir[0].copy_(dev_bf16(ora["cdir_bits"]))
+    L.csum[0].copy_(torch.from_numpy(ora["csum"]))
+    L.msum[0].copy_(torch.from_numpy(ora["msum"]))
+    L.cmean[0].copy_(torch.from_numpy(ora["cmean"].astype(np.float32)))
+    L.csize[0].copy_(torch.from_numpy(ora["csize"].astype(np.int32)))
+    L.offsets[0].copy_(torch.from_numpy(ora["offsets"].astype(np.int32)))
+    L.assign[0, :m].copy_(torch.from_numpy(ora["assign"].astype(np.int32)))
+    L.perm[0, :m].copy_(torch.from_numpy(ora["perm"].astype(np.int32)))
+    L.k_clu[0, :m].copy_(dev_bf16(ora["k_clu_bits"]))
+    L.v_clu[0, :m].copy_(dev_bf16(ora["v_clu_bits"]))
+    L.set_counters(n_total, nc)
+    sets = G if per_head else 1
+    qd = dev_bf16(q)
+    sel_pos = torch.full((sets, budget), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((sets,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, G, D), dtype=torch.float32, device="cuda")
+    if per_head:
+        L.select_per_head(qd, budget, sel_pos, cnt)
+        L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
+    else:
+        L.select(qd, budget, sel_pos, cnt)
+        L.sparse_decode(qd, sel_pos, cnt, budget, out)
+    torch.cuda.synchronize()
+    sp, og = sel_pos.cpu().numpy(), out.cpu().numpy()
+    sels = (pipeline.select_per_head(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+            if per_head else
+            [pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)])
+    positions = []
+    for s, sel in enumerate(sels):
+        assert sel["cut"] == 1 and sel["need"] == budget - sizes[0], (sel["cut"], sel["need"])
+        assert int(cnt[s]) == budget
+        pos = sp[s]
+        assert np.all(np.diff(pos) > 0)
+        if not np.array_equal(pos, sel["positions"]):
+            gap = selection_boundary_gap(sel, bf16.widen(ora["k_clu_bits"]), ora["offsets"])
+            say(f"  set {s}: recall differs in {len(set(pos) ^ set(sel['positions']))} positions; gap {gap:.3g}")
+            assert gap <= SELECT_GAP
+        positions.append(pos)
+    if per_head:
+        ref = pipeline.decode_per_head(q[0], k0, v0, ora["k_clu_bits"], ora["v_clu_bits"], positions, n_sink, nc,
+                                       n_total)
+    else:
+        ref = pipeline.decode_unit(q[0], k0, v0, ora["k_clu_bits"], ora["v_clu_bits"], positions[0], n_sink, nc,
+                                   n_total)
+    err = float(np.abs(og[0] - ref).max())
+    say(f"  decode max abs err {err:.3g}")
+    assert err <= DECODE_ATOL
