@@ -4,9 +4,11 @@ Default workload (``llama8b-stack-32k-b8``): 32 Llama-3.1-8B-shaped layers,
 batch 8, 8 KV heads x 4 query heads, head_dim 128, 32768-token context per
 sequence (16 sinks + 32752 clustered keys, 400 clusters per KV head, 10 Lloyd
 rounds), recall budget 2048.  One *step* is one decode token for the whole
-batch through all layers: per layer ckv_append_select (the new token's K/V
-row written and the recall, one launch) + ckv_sparse_decode.  Prefill
-clustering is timed separately (K-means keys/s).
+batch through all layers: per layer one ckv_append_select_decode launch (the
+new token's K/V row written, the recall and the sparse attention).  With
+``--separate`` the step runs the two-launch form instead (ckv_append_select,
+then ckv_sparse_decode).  Prefill clustering is timed separately (K-means
+keys/s).
 
 ``--workload glm4-stack-32k-b16``: 40 GLM4-9B-shaped layers (2 KV heads x 16
 query heads), batch 16, 32468 clustered + 300 recent tokens, 410 clusters,
@@ -27,8 +29,14 @@ slots per unit empty and ckv_cluster_split is timed after the incremental
 call (threshold: the median drift).
 
 ``--per-head-recall`` switches the stack workloads to the other grouped-query
-reading: ckv_append + ckv_select_per_head + ckv_sparse_decode_per_head, one
-recalled set per query head.
+reading: ckv_append + ckv_select_decode_per_head (with ``--separate``:
+ckv_append + ckv_select_per_head + ckv_sparse_decode_per_head), one recalled
+set per query head.
+
+``roofline`` prices the kernel the step spends its time in: the fused recall +
+decode launch on its algorithmic bytes (the decode's rows, positions, queries
+and output plus the recall's centroids, offsets and unkept cut-cluster keys),
+or ckv_sparse_decode on the decode's bytes in the two-launch form.
 
 The stack workloads also time a dense-decode baseline on the same harness
 (``full_attention``): budget >= m, so recall takes every cluster and the
@@ -79,30 +87,56 @@ def select_bytes(units: int, K: int, c: int, group: int, cut_rows: int) -> int:
     return units * (4 * K * d + 8 * K + 4 + 2 * group * d + cut_rows * (2 * d + 4) + 4 * c)
 
 
-# HBM bytes per ckv_sparse_decode launch on this workload, from two rocprofv3
-# --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by what the
-# same counters read for a plain 1 GiB device copy (FETCH_SIZE x 2.0,
+# Mean number of a cut cluster's tokens that recall scores but does not keep
+# (about half of an 82-token cluster at 400 clusters over 32752 keys).
+CUT_UNKEPT_ROWS = 41
+
+
+def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> int:
+    """Algorithmic HBM bytes of one ckv_select_decode launch.
+
+    Per unit: the attended K and V rows (n_sink + c + r rows of 256 B each),
+    the recalled positions written (4 c), the query heads (2 G d) and the f32
+    output (4 G d) -- exactly the decode's bytes -- plus what the recall reads
+    on top: the scoring centroids (4 K d), the cluster offsets (4 (K + 1)), the
+    recalled count written (4) and the keys of the cut cluster's tokens that
+    are scored but not kept (CUT_UNKEPT_ROWS rows of 2 d).  The centroids are
+    counted once although every chunk of a set reads them (they come from L2
+    after the first).
+    """
+    d = 128
+    return (decode_bytes(units, n_sink, c, r, group)
+            + units * (4 * K * d + 4 * (K + 1) + 4 + CUT_UNKEPT_ROWS * 2 * d))
+
+
+# HBM bytes per launch of the priced kernel on the default workload, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) scaled by
+# what the same counters read for a plain 1 GiB device copy (FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0).  Valid only for the kernel sources they were taken on:
 # when the hash of those sources differs, traffic is reported as null.
-TRAFFIC_SOURCES = ("decode.hip", "common.hpp")
-TRAFFIC = {"sha256": "53faccca59d7d4be4f07ead92406ef828798a1ad99d5f776f88fc2b8b582a3f9",
-           "fetch_kib": 34301.32, "write_kib": 762.0}
+TRAFFIC = {
+    "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
+                      "sha256": None, "fetch_kib": None, "write_kib": None},
+    "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
+                      "sha256": None, "fetch_kib": None, "write_kib": None},
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "semantic_cluster_sparse_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    if TRAFFIC["sha256"] is None or TRAFFIC["sha256"] != kernel_source_hash():
+def measured_traffic(kernel: str):
+    t = TRAFFIC[kernel]
+    if t["sha256"] is None or t["sha256"] != kernel_source_hash(t["sources"]):
         return None
-    return TRAFFIC["fetch_kib"] * 1024 * 2.0 + TRAFFIC["write_kib"] * 1024 * 1.0
+    return t["fetch_kib"] * 1024 * 2.0 + t["write_kib"] * 1024 * 1.0
 
 
 def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
@@ -255,7 +289,7 @@ def full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs
     fbytes = decode_bytes(units, 16, m_now, r_now, G)
     gbs = fbytes / (full_ms * 1e-3) / 1e9
     log(f"[bench] full-attention decode {full_ms * 1e3:.1f} us/launch ({gbs:.0f} GB/s); "
-        f"sparse decode is {full_ms / dec_ms:.1f}x faster per launch")
+        f"the sparse launch is {full_ms / dec_ms:.1f}x faster")
     return {"decode_us": full_ms * 1e3, "bytes_per_launch": fbytes, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
             "decode_speedup": full_ms / dec_ms}
 
@@ -316,6 +350,7 @@ def run_stack(cfg, args) -> dict:
     recluster = cfg.new_tokens if cfg.new_tokens > 0 else 0
     so = seed_offset(cfg)
     ph = bool(args.per_head_recall)
+    fused = not args.separate
     stream = torch.cuda.current_stream()
 
     log(f"[bench] {cfg.name}: allocating {n_layers} layers of {units} units, capacity {cap}")
@@ -371,6 +406,10 @@ def run_stack(cfg, args) -> dict:
     bg_done = {}         # start step -> event on the background stream
     busy = [False]
 
+    def nxt(li: int):
+        """The layer whose call follows layer li's on the stream (the prefetch hint)."""
+        return None if args.no_prefetch else layers[(li + 1) % n_layers]
+
     def recluster_due() -> bool:
         return bool(recluster) and layers[0].n_total - layers[0].n_clustered >= recluster
 
@@ -403,10 +442,16 @@ def run_stack(cfg, args) -> dict:
             for L in layers:
                 L.incremental()
         for li, L in enumerate(layers):
-            if ph:
+            if ph and fused:
+                L.append(k_new[s], v_new[s])
+                L.select_decode_per_head(qs[li][s], budget, sel_pos[li], cnt[li], outs[li], next_layer=nxt(li))
+            elif ph:
                 L.append(k_new[s], v_new[s])
                 L.select_per_head(qs[li][s], budget, sel_pos[li], cnt[li])
                 L.sparse_decode_per_head(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
+            elif fused:
+                L.append_select_decode(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li], outs[li],
+                                       next_layer=nxt(li))
             else:
                 L.append_select(k_new[s], v_new[s], qs[li][s], budget, sel_pos[li], cnt[li])
                 L.sparse_decode(qs[li][s], sel_pos[li], cnt[li], budget, outs[li])
@@ -474,15 +519,20 @@ def run_stack(cfg, args) -> dict:
     log(f"[bench] {ms_per_step:.3f} ms/step, {tokens_per_s:.1f} tokens/s")
 
     # ---------------------------------------------------------------- kernel timing for the roofline
-    # ckv_sparse_decode is one kernel per call.  The calls of all layers are
+    # The priced kernel (the fused recall + decode, or ckv_sparse_decode in the
+    # separate form) is one kernel per call.  The calls of all layers are
     # captured once more as a graph and replayed back to back between two
     # events on the stream they run on; the average is per launch.
     qlast = W + K - 1
 
     def decode_all() -> None:
         for li, L in enumerate(layers):
-            (L.sparse_decode_per_head if ph else L.sparse_decode)(qs[li][qlast], sel_pos[li], cnt[li], budget,
-                                                                  outs[li])
+            if fused:
+                (L.select_decode_per_head if ph else L.select_decode)(qs[li][qlast], budget, sel_pos[li], cnt[li],
+                                                                      outs[li], next_layer=nxt(li))
+            else:
+                (L.sparse_decode_per_head if ph else L.sparse_decode)(qs[li][qlast], sel_pos[li], cnt[li], budget,
+                                                                      outs[li])
 
     if graphs:
         dg = torch.cuda.CUDAGraph()
@@ -510,8 +560,16 @@ def run_stack(cfg, args) -> dict:
         srt = sel_pos[n_layers - 1].view(units, G * budget).sort(dim=1).values
         distinct = int((1 + (srt[:, 1:] != srt[:, :-1]).sum(dim=1)).sum())
         dbytes = (units * (16 + r_now) + distinct) * 2 * 128 * 2 + sets * (4 * budget + 2 * 128 + 4 * 128)
+        if fused:
+            # every set's recall reads its unit's centroids and offsets (once per unit
+            # from HBM: the sets of a unit share them through the caches), writes its
+            # count and scores its cut cluster's unkept tokens
+            dbytes += units * (4 * cfg.n_clusters * 128 + 4 * (cfg.n_clusters + 1)) + sets * (
+                4 + CUT_UNKEPT_ROWS * 2 * 128)
         log(f"[bench] per-head recall: {distinct / units:.0f} distinct recalled rows per unit "
             f"(of {G * budget} recalled)")
+    elif fused:
+        dbytes = fused_bytes(units, 16, budget, r_now, G, cfg.n_clusters)
     else:
         dbytes = decode_bytes(units, 16, budget, r_now, G)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
@@ -521,10 +579,13 @@ def run_stack(cfg, args) -> dict:
     if ph:
         step_bytes = n_layers * (decode_bytes(sets, 16, budget, r_mean, 1)
                                  + select_bytes(sets, cfg.n_clusters, budget, 1, 82) + units * 2 * 256)
+    elif fused:
+        step_bytes = n_layers * (fused_bytes(units, 16, budget, r_mean, G, cfg.n_clusters) + units * 2 * 256)
     else:
         step_bytes = n_layers * (decode_bytes(units, 16, budget, r_mean, G)
                                  + select_bytes(units, cfg.n_clusters, budget, G, 82) + units * 2 * 256)
-    log(f"[bench] ckv_sparse_decode {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
+    priced = "ckv_select_decode" if fused else "ckv_sparse_decode"
+    log(f"[bench] {priced}{'_per_head' if ph else ''} {dec_ms * 1e3:.1f} us/launch, {achieved:.0f} GB/s algorithmic")
 
     # ---------------------------------------------------------------- full-attention baseline
     full = None
@@ -532,7 +593,8 @@ def run_stack(cfg, args) -> dict:
         full = full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs if graphs else None,
                                        stream, dev)
         full["step_speedup"] = n_layers * full["decode_us"] * 1e-3 / ms_per_step
-    traffic = measured_traffic() if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph else None
+    traffic = (measured_traffic("recall_decode" if fused else "sparse_decode")
+               if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph else None)
 
     result = {
         "metric": METRIC,
@@ -549,8 +611,13 @@ def run_stack(cfg, args) -> dict:
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": n_layers, "batch": cfg.batch, "kv_heads": cfg.n_kv_heads,
                    "group": G, "context": n_fill, "clusters": cfg.n_clusters, "budget": budget,
-                   "graphs": not args.no_graph, "recall": "per query head" if ph else "per KV head (summed query)"},
-        "roofline": {"bound": "hbm", "kernel": f"ckv::sparse_decode_kernel<{1 if ph else _group_tier(G)}>",
+                   "graphs": not args.no_graph, "recall": "per query head" if ph else "per KV head (summed query)",
+                   "launches_per_layer": ("2 (ckv_append + ckv_select_decode_per_head)" if ph else "1") if fused
+                   else ("3" if ph else "2 (ckv_append_select + ckv_sparse_decode)"),
+                   "prefetch_next_layer": fused and not args.no_prefetch},
+        "roofline": {"bound": "hbm",
+                     "kernel": f"ckv::{'recall_decode_kernel' if fused else 'sparse_decode_kernel'}"
+                               f"<{1 if ph else _group_tier(G)}>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},
@@ -741,6 +808,11 @@ def main() -> int:
     ap.add_argument("--async-lag", type=int, default=16, help="steps between starting and committing")
     ap.add_argument("--per-head-recall", action="store_true",
                     help="one recall and attention set per query head instead of per KV head")
+    ap.add_argument("--no-prefetch", action="store_true",
+                    help="fused form: do not pass the next layer as the centroid prefetch hint")
+    ap.add_argument("--separate", action="store_true",
+                    help="recall and decode as two launches per layer (ckv_append_select + ckv_sparse_decode) "
+                         "instead of the fused ckv_append_select_decode")
     ap.add_argument("--split-reserve", type=int, default=0,
                     help="llama8b-incremental-b16 only: hold this many cluster slots empty at prefill and "
                          "time ckv_cluster_split after the incremental call")

@@ -302,6 +302,58 @@ int ckv_sparse_decode(const ckv_layer* L, const uint16_t* q, const int32_t* sel_
                       const int32_t* sel_count, int32_t budget, float* out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Recall and sparse decode of one decode step in a single launch (ClusterKV
+ * article §3.3 selection procedure, §3.1 attention over the recalled tokens,
+ * §4.1 cluster-contiguous rows).  Computes exactly what ckv_select followed by
+ * ckv_sparse_decode computes:
+ *   sel_pos   int32 [units, budget] (device, written): the recalled
+ *             cluster-order positions, ascending, in the first sel_count[u]
+ *             slots -- the same positions ckv_select writes;
+ *   sel_count int32 [units] (device, written): min(budget, m);
+ *   out       f32 [batch, n_kv_heads * group, 128] (device, written): every
+ *             query head's attention over the sinks, the recalled rows and the
+ *             recent rows [n_clustered, n_total).
+ * The recalled positions are not read back: each of the set's workgroups
+ * recalls the set itself and streams its share of the rows straight from the
+ * index, so no hand-off between a recall launch and a decode launch sits
+ * between the query and the output.  The decode's floating-point sums run in
+ * another order than ckv_sparse_decode's, so out may differ from it in the
+ * last bits.  Requirements and errors as for ckv_select and
+ * ckv_sparse_decode; the workspace holds ckv_workspace_bytes() bytes and its
+ * arrival counters are left zero.
+ *   next      a layer whose call follows this one on the stream (the next
+ *             layer of the model), or NULL: a hint only.  When it has the same
+ *             batch, n_kv_heads and n_clusters as L, the workgroups that finish
+ *             early read its cmean and offsets into the device caches, so that
+ *             its own call starts from cached centroids.  Nothing of *next is
+ *             written; results never depend on it.
+ */
+int ckv_select_decode(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                      int32_t* sel_count, float* out, const ckv_layer* next, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * ckv_append, then ckv_select_decode, in one launch (one decode step of one
+ * layer): k_new / v_new (bf16 [units, 128], device) become row n_total of
+ * k_tok / v_tok and are attended as the newest recent row; n_total advances.
+ * Errors as for either call; nothing is enqueued on error.
+ */
+int ckv_append_select_decode(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                             int32_t budget, int32_t* sel_pos, int32_t* sel_count, float* out, const ckv_layer* next,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ckv_select_per_head followed by ckv_sparse_decode_per_head in one launch
+ * (ClusterKV article §3.3 applied to every query head): sel_pos int32
+ * [units * group, budget], sel_count int32 [units * group], out as for
+ * ckv_sparse_decode, next as for ckv_select_decode.  The workspace must hold
+ * ckv_workspace_bytes_per_head() bytes.
+ */
+int ckv_select_decode_per_head(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                               int32_t* sel_count, float* out, const ckv_layer* next, void* ws, size_t ws_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ from .ckv import (  # noqa: F401
     ckv_append,
     ckv_assign,
     ckv_append_select,
+    ckv_append_select_decode,
     ckv_cluster_commit,
     ckv_cluster_incremental,
     ckv_cluster_incremental_async,
@@ -22,6 +23,8 @@ from .ckv import (  # noqa: F401
     ckv_cluster_split,
     ckv_last_error,
     ckv_select,
+    ckv_select_decode,
+    ckv_select_decode_per_head,
     ckv_select_per_head,
     ckv_sparse_decode,
     ckv_sparse_decode_per_head,

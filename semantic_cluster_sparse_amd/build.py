@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libckv.so")
-SOURCES = ["api.hip", "kmeans.hip", "select.hip", "decode.hip"]
+SOURCES = ["api.hip", "kmeans.hip", "select.hip", "decode.hip", "recall_decode.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

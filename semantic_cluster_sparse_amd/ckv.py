@@ -103,6 +103,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_sparse_decode.restype = c_int
     lib.ckv_sparse_decode.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                       c_size_t, c_void_p]
+    lib.ckv_select_decode.restype = c_int
+    lib.ckv_select_decode.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, LP, c_void_p, c_size_t,
+                                      c_void_p]
+    lib.ckv_append_select_decode.restype = c_int
+    lib.ckv_append_select_decode.argtypes = [LP, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                             c_void_p, LP, c_void_p, c_size_t, c_void_p]
+    lib.ckv_select_decode_per_head.restype = c_int
+    lib.ckv_select_decode_per_head.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, LP, c_void_p,
+                                               c_size_t, c_void_p]
     if lib.ckv_abi_layer_bytes() != ctypes.sizeof(CkvLayerStruct):
         raise RuntimeError("ckv_layer layout mismatch between libckv.so and the binding")
     if path is None:
@@ -208,3 +217,28 @@ def ckv_sparse_decode_per_head(layer: CkvLayerStruct, q: int, sel_pos: int, sel_
     _check("ckv_sparse_decode_per_head",
            load_library().ckv_sparse_decode_per_head(_ref(layer), q, sel_pos, sel_count, budget, out, ws,
                                                      ws_bytes, stream))
+
+
+def _opt_ref(layer):
+    return ctypes.byref(layer) if layer is not None else None
+
+
+def ckv_select_decode(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, out: int,
+                      next_layer, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_select_decode",
+           load_library().ckv_select_decode(_ref(layer), q, budget, sel_pos, sel_count, out, _opt_ref(next_layer), ws,
+                                            ws_bytes, stream))
+
+
+def ckv_append_select_decode(layer: CkvLayerStruct, k_new: int, v_new: int, q: int, budget: int, sel_pos: int,
+                             sel_count: int, out: int, next_layer, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_append_select_decode",
+           load_library().ckv_append_select_decode(_ref(layer), k_new, v_new, q, budget, sel_pos, sel_count, out,
+                                                   _opt_ref(next_layer), ws, ws_bytes, stream))
+
+
+def ckv_select_decode_per_head(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, out: int,
+                               next_layer, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_select_decode_per_head",
+           load_library().ckv_select_decode_per_head(_ref(layer), q, budget, sel_pos, sel_count, out,
+                                                     _opt_ref(next_layer), ws, ws_bytes, stream))

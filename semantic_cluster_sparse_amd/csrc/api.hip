@@ -40,6 +40,7 @@ struct Layout {
   size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
   size_t total;
   size_t off_hist, off_invn, off_scores, off_cut, off_partials;
+  size_t off_rd_cut;  // fused recall + decode: cut scores after the partials
 };
 
 int group_tier(int g) {
@@ -71,9 +72,10 @@ Layout layout_of(const ckv_layer* L, bool per_head = false) {
   w.off_scores = w.counters;
   w.off_cut = w.counters + w.scores;
   w.off_partials = w.counters;
+  w.off_rd_cut = w.counters + w.partials;
   size_t body = w.hist + w.invn;
   if (w.scores + w.cut > body) body = w.scores + w.cut;
-  if (w.partials > body) body = w.partials;
+  if (w.partials + w.cut > body) body = w.partials + w.cut;
   w.total = w.counters + body;
   return w;
 }
@@ -442,9 +444,72 @@ int decode_impl(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, c
   return hip_status(e, "sparse_decode");
 }
 
+int select_decode_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                       int32_t* sel_count, float* out, void* ws, size_t ws_bytes, void* stream,
+                       const uint16_t* k_new, const uint16_t* v_new, bool per_head, const ckv_layer* next) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
+  if (clustered_tokens(L) < L->n_clusters)
+    return fail(CKV_EINVAL, "no cluster state: clustered tokens %d < n_clusters %d", clustered_tokens(L),
+                L->n_clusters);
+  rc = check_ptrs("q,cmean,offsets,k_tok,v_tok,k_clu,v_clu,sel_count,out", 9, q, L->cmean, L->offsets, L->k_tok,
+                  L->v_tok, L->k_clu, L->v_clu, sel_count, out);
+  if (rc) return rc;
+  if (budget > 0 && !aligned16(sel_pos)) return fail(CKV_EINVAL, "sel_pos is NULL or not 16-byte aligned");
+  if (k_new != nullptr) {
+    rc = check_ptrs("k_new,v_new", 2, k_new, v_new);
+    if (rc) return rc;
+    if (L->n_total >= L->capacity) return fail(CKV_ENOSPACE, "cache full (capacity %d)", L->capacity);
+  }
+  rc = check_ws(L, ws, ws_bytes, per_head);
+  if (rc) return rc;
+  const Layout w = layout_of(L, per_head);
+  const int units = L->batch * L->n_kv_heads;
+  const int n_total = L->n_total + (k_new != nullptr ? 1 : 0);
+  // the prefetch hint is used only for a layer laid out like this one
+  const float* pf_cmean = nullptr;
+  const int32_t* pf_offsets = nullptr;
+  if (next != nullptr && next->batch == L->batch && next->n_kv_heads == L->n_kv_heads &&
+      next->n_clusters == L->n_clusters && aligned16(next->cmean) && aligned16(next->offsets)) {
+    pf_cmean = next->cmean;
+    pf_offsets = next->offsets;
+  }
+  hipError_t e = ckv::launch_recall_decode(
+      q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu,
+      L->capacity - L->n_sink, budget, L->n_sink, L->n_clustered, n_total, sel_pos, sel_count,
+      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, (uint32_t*)((char*)ws + w.off_rd_cut), out, k_new, v_new,
+      pf_cmean, pf_offsets, units, per_head ? 1 : 0, (hipStream_t)stream);
+  return hip_status(e, "select_decode");
+}
+
 }  // namespace
 
 extern "C" {
+
+int ckv_select_decode(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
+                      float* out, const ckv_layer* next, void* ws, size_t ws_bytes, void* stream) {
+  return select_decode_impl(L, q, budget, sel_pos, sel_count, out, ws, ws_bytes, stream, nullptr, nullptr, false,
+                            next);
+}
+
+int ckv_append_select_decode(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                             int32_t budget, int32_t* sel_pos, int32_t* sel_count, float* out, const ckv_layer* next,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return fail(CKV_EINVAL, "k_new / v_new is NULL");
+  const int rc =
+      select_decode_impl(L, q, budget, sel_pos, sel_count, out, ws, ws_bytes, stream, k_new, v_new, false, next);
+  if (rc) return rc;
+  L->n_total += 1;
+  return CKV_OK;
+}
+
+int ckv_select_decode_per_head(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                               int32_t* sel_count, float* out, const ckv_layer* next, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return select_decode_impl(L, q, budget, sel_pos, sel_count, out, ws, ws_bytes, stream, nullptr, nullptr, true,
+                            next);
+}
 
 int ckv_select(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos, int32_t* sel_count,
                void* ws, size_t ws_bytes, void* stream) {

@@ -75,6 +75,24 @@ hipError_t launch_sparse_decode(const uint16_t* q, int group, const uint16_t* k_
                                 float* partials, uint32_t* counters, float* out, int units,
                                 int per_head, hipStream_t s);
 
+// Recall and sparse decode in one launch: every workgroup of a set recalls
+// the set itself, then streams its chunk of the attended rows (sinks, recent
+// rows, whole clusters, the cut's kept tokens) and the last chunk merges.
+// Writes sel_pos / sel_count as launch_select does and out as
+// launch_sparse_decode does.  counters[sets] must be zero on entry and are
+// zero again on exit; cut_ws [sets, clu_stride] u32 is scratch for cut
+// clusters above 4096 tokens.  With k_new non-null the launch also appends
+// k_new / v_new as row n_total - 1 (n_total counts it) and attends to it.
+// pf_cmean / pf_offsets (or null): centroids [units, K, 128] and offsets
+// [units, K + 1] of the next call's layer, read into the caches at the end.
+hipError_t launch_recall_decode(const uint16_t* q, int group, const float* cmean, const int32_t* offsets, int K,
+                                uint16_t* k_tok, uint16_t* v_tok, int capacity, const uint16_t* k_clu,
+                                const uint16_t* v_clu, int clu_stride, int budget, int n_sink, int n_clustered,
+                                int n_total, int32_t* sel_pos, int32_t* sel_count, float* partials,
+                                uint32_t* counters, uint32_t* cut_ws, float* out, const uint16_t* k_new,
+                                const uint16_t* v_new, const float* pf_cmean, const int32_t* pf_offsets, int units,
+                                int per_head, hipStream_t s);
+
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_tok,
                          uint16_t* v_tok, int capacity, int row, int units, hipStream_t s);
 

@@ -19,6 +19,10 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _struct(layer):
+    return layer.struct if layer is not None else None
+
+
 class Layer:
     def __init__(self, batch: int, n_kv_heads: int, group: int, n_clusters: int, capacity: int,
                  n_sink: int = 16, max_budget: int = 2048, incremental: bool = True, per_head: bool = False,
@@ -168,3 +172,37 @@ class Layer:
         assert out.numel() == self.units * self.group * HEAD_DIM
         ckv.ckv_sparse_decode_per_head(self.struct, q.data_ptr(), sel_pos.data_ptr(), sel_count.data_ptr(),
                                        budget, out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def select_decode(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor, sel_count: torch.Tensor,
+                      out: torch.Tensor, next_layer: "Layer | None" = None) -> None:
+        """Recall and decode in one launch (ckv_select_decode); next_layer is the
+        prefetch hint (the layer whose call follows on the stream)."""
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * budget and sel_count.numel() >= self.units
+        assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_select_decode(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
+                              out.data_ptr(), _struct(next_layer), self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def append_select_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, budget: int,
+                             sel_pos: torch.Tensor, sel_count: torch.Tensor, out: torch.Tensor,
+                             next_layer: "Layer | None" = None) -> None:
+        """Append the decoded token, recall and decode in one launch (ckv_append_select_decode)."""
+        assert k_new.shape == (self.units, HEAD_DIM) and v_new.shape == (self.units, HEAD_DIM)
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * budget and sel_count.numel() >= self.units
+        assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_append_select_decode(self.struct, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), budget,
+                                     sel_pos.data_ptr(), sel_count.data_ptr(), out.data_ptr(), _struct(next_layer),
+                                     self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def select_decode_per_head(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor, sel_count: torch.Tensor,
+                               out: torch.Tensor, next_layer: "Layer | None" = None) -> None:
+        """Per-query-head recall and decode in one launch (ckv_select_decode_per_head)."""
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * self.group * budget
+        assert sel_count.numel() >= self.units * self.group
+        assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_select_decode_per_head(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
+                                       out.data_ptr(), _struct(next_layer), self.ws.data_ptr(), self.ws_bytes,
+                                       _stream())

@@ -12,7 +12,7 @@ import sys
 import numpy as np
 import torch
 
-from oracle import bf16
+from oracle import bf16, pipeline
 
 DECODE_ATOL = 2e-3        # max |GPU f32 - oracle f64| of a decode output element
 ASSIGN_MARGIN = 1e-4      # relative top-2 margin below which an assignment may differ
@@ -90,3 +90,90 @@ def selection_boundary_gap(sel: dict, k_clu_vals: np.ndarray, offsets: np.ndarra
 
 def widen(bits):
     return bf16.widen(bits)
+
+
+# ------------------------------------------------------------------ GPU layers and comparisons
+
+
+def gpu_layer(k_bits, v_bits, group, K, n_sink=16, max_budget=4096):
+    """A Layer holding the given token rows (bf16 bits [U, capacity, 128]), one unit per row block."""
+    from semantic_cluster_sparse_amd.layer import Layer
+
+    U, cap, _ = k_bits.shape
+    L = Layer(batch=U, n_kv_heads=1, group=group, n_clusters=K, capacity=cap, n_sink=n_sink,
+              max_budget=max_budget)
+    L.k_tok.copy_(dev_bf16(k_bits))
+    L.v_tok.copy_(dev_bf16(v_bits))
+    return L
+
+
+def load_state(L, states, n_sink=16):
+    """Teacher forcing: copy oracle states (one per unit) into the GPU buffers."""
+    for u, st in enumerate(states):
+        m = st["n_clustered"] - n_sink
+        L.cdir[u].copy_(dev_bf16(st["cdir_bits"]))
+        L.csum[u].copy_(torch.from_numpy(st["csum"]))
+        L.msum[u].copy_(torch.from_numpy(st["msum"]))
+        L.cmean[u].copy_(torch.from_numpy(st["cmean"].astype(np.float32)))
+        L.csize[u].copy_(torch.from_numpy(st["csize"].astype(np.int32)))
+        L.offsets[u].copy_(torch.from_numpy(st["offsets"].astype(np.int32)))
+        L.assign[u, :m].copy_(torch.from_numpy(st["assign"].astype(np.int32)))
+        L.perm[u, :m].copy_(torch.from_numpy(st["perm"].astype(np.int32)))
+        L.k_clu[u, :m].copy_(dev_bf16(st["k_clu_bits"]))
+        L.v_clu[u, :m].copy_(dev_bf16(st["v_clu_bits"]))
+
+
+def check_state(L, u, ora, x, cdir_used, n_sink=16, full=True, tag=""):
+    """Compare one unit's GPU cluster state with the oracle's. Returns #label mismatches."""
+    m = len(ora["assign"])
+    a_g = L.assign[u, :m].cpu().numpy()
+    mism, unexc = compare_assign(a_g, ora["assign"], x, cdir_used)
+    say(f"  {tag} unit {u}: label mismatches {mism} (unexcused {unexc}) of {m}")
+    assert unexc == 0
+    if mism:
+        return mism
+    assert np.array_equal(host_bits(L.cdir[u]), ora["cdir_bits"]), "directions differ"
+    assert np.array_equal(L.csize[u].cpu().numpy(), ora["csize"])
+    assert np.array_equal(L.offsets[u].cpu().numpy(), ora["offsets"])
+    assert np.array_equal(L.perm[u, :m].cpu().numpy(), ora["perm"])
+    assert np.allclose(L.csum[u].cpu().numpy(), ora["csum"], rtol=0, atol=1e-9)
+    if full:
+        assert np.allclose(L.msum[u].cpu().numpy(), ora["msum"], rtol=0, atol=1e-7)
+        mu = L.cmean[u].cpu().numpy().astype(np.float64)
+        assert np.allclose(mu, ora["cmean"], rtol=1e-6, atol=1e-6)
+        assert np.array_equal(host_bits(L.k_clu[u, :m]), ora["k_clu_bits"])
+        assert np.array_equal(host_bits(L.v_clu[u, :m]), ora["v_clu_bits"])
+    return 0
+
+
+def compare_selection(L, u, sel_pos, cnt, ora_state, sel, budget):
+    """Token sets of GPU and oracle recall; returns the differing token count."""
+    m = len(ora_state["assign"])
+    c = int(cnt[u])
+    assert c == min(budget, m)
+    pos_g = sel_pos[u, :c]
+    assert np.all(np.diff(pos_g) > 0), "positions must ascend"
+    tok_g = set(L.perm[u, :m].cpu().numpy()[pos_g].tolist())
+    tok_o = set(ora_state["perm"][sel["positions"]].tolist())
+    diff = len(tok_g ^ tok_o)
+    if diff:
+        gap = selection_boundary_gap(sel, bf16.widen(ora_state["k_clu_bits"]), ora_state["offsets"])
+        say(f"  unit {u}: recall differs by {diff} tokens; boundary gap {gap:.3g}")
+        assert gap <= SELECT_GAP
+    return diff
+
+
+def check_decode(og_u, q_u, k_u, v_u, ora, sp_u, cnt_u, sel, diff, n_sink, n_clustered, n_total, tag=""):
+    """Decode of one unit against the oracle's attention.  When the recall sets
+    agree the attended rows are the oracle's own recall; when they differ (an
+    excused near-tie, already checked by compare_selection) the rows are the
+    GPU's recalled positions, which index the same cluster-ordered rows (the
+    state was checked bitwise equal), so decode is still checked on its own.
+    Returns 1 (one decode compared)."""
+    pos = sel["positions"] if diff == 0 else np.asarray(sp_u[:int(cnt_u)], np.int64)
+    ref = pipeline.decode_unit(q_u, k_u, v_u, ora["k_clu_bits"], ora["v_clu_bits"], pos, n_sink,
+                               n_clustered, n_total)
+    err = float(np.abs(og_u - ref).max())
+    say(f"  {tag} decode max abs err {err:.3g} ({'oracle' if diff == 0 else 'GPU'} recall)")
+    assert err <= DECODE_ATOL
+    return 1

@@ -229,6 +229,33 @@ def test_assign_host_rules():
     assert e.value.code == ckv.CKV_EINVAL and "cdir" in e.value.message
 
 
+def test_select_decode_host_rules():
+    L = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=100, n_clustered=100))
+    with pytest.raises(ckv.CkvError) as e:                      # full cache: nothing appended
+        ckv.ckv_append_select_decode(L, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_ENOSPACE and L.n_total == 100
+    for call in (ckv.ckv_select_decode, ckv.ckv_select_decode_per_head):
+        with pytest.raises(ckv.CkvError) as e:
+            call(L, FAKE, -1, FAKE, FAKE, FAKE, None, FAKE, 1 << 40)
+        assert e.value.code == ckv.CKV_EINVAL
+        with pytest.raises(ckv.CkvError) as e:                  # output not 16-byte aligned
+            call(L, FAKE, 8, FAKE, FAKE, FAKE + 4, None, FAKE, 1 << 40)
+        assert e.value.code == ckv.CKV_EINVAL
+        with pytest.raises(ckv.CkvError) as e:                  # workspace too small
+            call(L, FAKE, 8, FAKE, FAKE, FAKE, L, FAKE, 256)
+        assert e.value.code == ckv.CKV_ENOSPACE
+    L2 = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=20, n_clustered=20))
+    with pytest.raises(ckv.CkvError) as e:                      # 4 clustered tokens < K
+        ckv.ckv_select_decode(L2, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_append_select_decode(L2, None, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 40)
+    assert e.value.code == ckv.CKV_EINVAL and L2.n_total == 20
+    # the fused call needs the decode's partials and the recall's cut scores at once
+    L3 = _layer()
+    assert ckv.ckv_workspace_bytes_per_head(L3, 2048) >= ckv.ckv_workspace_bytes(L3, 2048)
+
+
 def test_missing_library_fails_loudly(tmp_path):
     # the binding has no fallback: without the built library every call path raises
     with pytest.raises(RuntimeError, match="libckv.so not found"):

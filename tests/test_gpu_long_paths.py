@@ -9,7 +9,10 @@ through the workspace above that.  These tests run exactly those launches:
   chunks of 8208 rows (nine segments);
 * per-query-head recall + decode at the same layer shape: 256 sets, one
   chunk of 2096 rows per set (three segments);
-* a recall whose cut cluster holds 6000 tokens.
+* a recall whose cut cluster holds 6000 tokens;
+* the fused recall + decode launch (ckv_select_decode) in the benchmark's own
+  configuration (64 units, 4 chunks per set), dense, per query head, and with
+  the 6000-token cut cluster.
 
 Bars as in test_gpu_parity: same recalled token sets unless the oracle's
 boundary has a near-tie, decode within 2e-3 of float64.
@@ -64,19 +67,24 @@ def stack_layer():
     return dict(cfg=cfg, L=L, k=k, v=v, q=q, oras=oras, n=n, n_total=n + RECENT)
 
 
-def test_dense_decode_full_layer(stack_layer):
+@pytest.mark.parametrize("fused", [False, True])
+def test_dense_decode_full_layer(stack_layer, fused):
     """budget >= m: recall takes every cluster and decode attends to every token,
-    in the launch the benchmark's dense baseline uses (4 chunks of 8208 rows per unit)."""
+    in the launch the benchmark's dense baseline uses (4 chunks of 8208 rows per
+    unit), separately or fused."""
     st = stack_layer
     cfg, L, q = st["cfg"], st["L"], st["q"]
     m, units, n_total = cfg.m, cfg.units, st["n_total"]
-    say(f"case: dense decode, {units} units, budget {m}, {n_total} attended rows per unit")
+    say(f"case: dense decode, {units} units, budget {m}, {n_total} attended rows per unit, fused={fused}")
     qd = dev_bf16(q)
     sel_pos = torch.full((units, m), -1, dtype=torch.int32, device="cuda")
     cnt = torch.zeros((units,), dtype=torch.int32, device="cuda")
     out = torch.zeros((units, cfg.group, D), dtype=torch.float32, device="cuda")
-    L.select(qd, m, sel_pos, cnt)
-    L.sparse_decode(qd, sel_pos, cnt, m, out)
+    if fused:
+        L.select_decode(qd, m, sel_pos, cnt, out)
+    else:
+        L.select(qd, m, sel_pos, cnt)
+        L.sparse_decode(qd, sel_pos, cnt, m, out)
     torch.cuda.synchronize()
     assert np.all(cnt.cpu().numpy() == m)
     assert torch.equal(sel_pos, torch.arange(m, dtype=torch.int32, device="cuda").expand(units, m))
@@ -88,19 +96,23 @@ def test_dense_decode_full_layer(stack_layer):
         assert err <= DECODE_ATOL
 
 
-def test_per_head_recall_decode_full_layer(stack_layer):
+@pytest.mark.parametrize("fused", [False, True])
+def test_per_head_recall_decode_full_layer(stack_layer, fused):
     """One recalled set per query head at the benchmark's layer shape: 256 sets,
-    one chunk of 2096 rows each."""
+    one chunk of 2096 rows each, separately or fused."""
     st = stack_layer
     cfg, L, q = st["cfg"], st["L"], st["q"]
     G, units, budget, n, n_total = cfg.group, cfg.units, cfg.budget, st["n"], st["n_total"]
-    say(f"case: per-head recall + decode, {units * G} sets, budget {budget}, {RECENT} recent rows")
+    say(f"case: per-head recall + decode, {units * G} sets, budget {budget}, {RECENT} recent rows, fused={fused}")
     qd = dev_bf16(q)
     sel_pos = torch.full((units * G, budget), -1, dtype=torch.int32, device="cuda")
     cnt = torch.zeros((units * G,), dtype=torch.int32, device="cuda")
     out = torch.zeros((units, G, D), dtype=torch.float32, device="cuda")
-    L.select_per_head(qd, budget, sel_pos, cnt)
-    L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
+    if fused:
+        L.select_decode_per_head(qd, budget, sel_pos, cnt, out)
+    else:
+        L.select_per_head(qd, budget, sel_pos, cnt)
+        L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
     torch.cuda.synchronize()
     assert np.all(cnt.cpu().numpy() == budget)
     sp, og = sel_pos.cpu().numpy(), out.cpu().numpy()
@@ -128,13 +140,13 @@ def test_per_head_recall_decode_full_layer(stack_layer):
     assert compared >= 1, "no sampled unit's state matched the oracle's"
 
 
-@pytest.mark.parametrize("per_head", [False, True])
-def test_recall_cut_cluster_above_lds(per_head):
+@pytest.mark.parametrize("per_head,fused", [(False, False), (True, False), (False, True), (True, True)])
+def test_recall_cut_cluster_above_lds(per_head, fused):
     """Three well separated groups of 1000, 6000 and 5000 keys, ranked in that
     order by the query; budget 3000 takes the first whole and cuts the 6000-key
     cluster, whose token scores go through the workspace (more than 4096)."""
     sizes, G, budget, n_sink, recent = [1000, 6000, 5000], 4, 3000, 16, 9
-    say(f"case: cut cluster of {sizes[1]} tokens, budget {budget}, per_head={per_head}")
+    say(f"case: cut cluster of {sizes[1]} tokens, budget {budget}, per_head={per_head}, fused={fused}")
     k0, v0, cen, labels = synth.make_planted_groups(61, sizes, n_sink=n_sink, extra_rows=recent)
     nc = n_sink + sum(sizes)
     n_total = nc + recent
@@ -167,7 +179,9 @@ def test_recall_cut_cluster_above_lds(per_head):
     sel_pos = torch.full((sets, budget), -1, dtype=torch.int32, device="cuda")
     cnt = torch.zeros((sets,), dtype=torch.int32, device="cuda")
     out = torch.zeros((1, G, D), dtype=torch.float32, device="cuda")
-    if per_head:
+    if fused:
+        (L.select_decode_per_head if per_head else L.select_decode)(qd, budget, sel_pos, cnt, out)
+    elif per_head:
         L.select_per_head(qd, budget, sel_pos, cnt)
         L.sparse_decode_per_head(qd, sel_pos, cnt, budget, out)
     else:
@@ -198,3 +212,50 @@ def test_recall_cut_cluster_above_lds(per_head):
     err = float(np.abs(og[0] - ref).max())
     say(f"  decode max abs err {err:.3g}")
     assert err <= DECODE_ATOL
+
+
+def test_fused_recall_decode_full_layer(stack_layer):
+    """The benchmark's step on one full layer: ckv_append_select_decode with
+    budget 2048 over 64 units (4 chunks per set), against the oracle on the
+    sampled units and against ckv_select's positions on every unit."""
+    st = stack_layer
+    cfg, L, q = st["cfg"], st["L"], st["q"]
+    G, units, budget, n, n_total = cfg.group, cfg.units, cfg.budget, st["n"], st["n_total"]
+    say(f"case: fused append + recall + decode, {units} units, budget {budget}, {RECENT} recent rows + 1 appended")
+    new = synth.make_unit_inputs(5151, 0, units, 16)
+    k_full, v_full = st["k"].copy(), st["v"].copy()
+    k_full[:, n_total] = new[0]
+    v_full[:, n_total] = new[1]
+    qd = dev_bf16(q)
+    sel_pos = torch.full((units, budget), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((units,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((units, G, D), dtype=torch.float32, device="cuda")
+    sp2 = torch.full((units, budget), -1, dtype=torch.int32, device="cuda")
+    cn2 = torch.zeros((units,), dtype=torch.int32, device="cuda")
+    L.select(qd, budget, sp2, cn2)
+    L.append_select_decode(dev_bf16(new[0]), dev_bf16(new[1]), qd, budget, sel_pos, cnt, out)
+    torch.cuda.synchronize()
+    try:
+        assert L.n_total == n_total + 1
+        assert torch.equal(sel_pos, sp2) and torch.equal(cnt, cn2), "fused recall differs from ckv_select"
+        assert np.array_equal(host_bits(L.k_tok[:, n_total]), new[0])
+        sp, og = sel_pos.cpu().numpy(), out.cpu().numpy()
+        compared = 0
+        for u, ora in st["oras"].items():
+            if not np.array_equal(L.assign[u, :cfg.m].cpu().numpy(), ora["assign"]):
+                continue
+            sel = pipeline.select_unit(q[u], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
+            pos = sp[u]
+            if not np.array_equal(pos, sel["positions"]):
+                gap = selection_boundary_gap(sel, bf16.widen(ora["k_clu_bits"]), ora["offsets"])
+                say(f"  unit {u}: recall differs; boundary gap {gap:.3g}")
+                assert gap <= SELECT_GAP
+            ref = pipeline.decode_unit(q[u], k_full[u], v_full[u], ora["k_clu_bits"], ora["v_clu_bits"], pos, 16, n,
+                                       n_total + 1)
+            err = float(np.abs(og[u] - ref).max())
+            say(f"  unit {u}: fused decode max abs err {err:.3g}")
+            assert err <= DECODE_ATOL
+            compared += 1
+        assert compared >= 1, "no sampled unit's state matched the oracle's"
+    finally:
+        L.set_counters(n_total, n)   # the other tests on this layer see RECENT recent rows
