@@ -354,6 +354,27 @@ int ckv_select_decode_per_head(const ckv_layer* L, const uint16_t* q, int32_t bu
                                int32_t* sel_count, float* out, const ckv_layer* next, void* ws, size_t ws_bytes,
                                void* stream);
 
+/*
+ * ckv_select_decode for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Computes
+ * exactly what ckv_select_decode computes (the same kernel, the same bits),
+ * with no workspace argument: its scratch (arrival counters, split-K
+ * partials, cut-cluster scores) is a file-scope device array of
+ * ckv_select_decode_noalloc_limit() bytes (16 MiB) that each GPU holds from
+ * the library's first such call on it until the process ends.  The call
+ * allocates and frees nothing.  The first call on a device zero-fills the
+ * counters with a kernel on `stream`; every call leaves them zero.  Needs
+ * 64 KiB + units * W * 4 * tier(group) * 130 + units * (capacity - n_sink) * 4
+ * bytes (W <= 64 chunks per unit, tier = group rounded up to a power of two);
+ * a larger layer returns CKV_ENOSPACE before anything is enqueued.  All calls
+ * on one GPU share the array: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results.
+ * Other errors as for ckv_select_decode.
+ */
+size_t ckv_select_decode_noalloc_limit(void);
+int ckv_select_decode_noalloc(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                              int32_t* sel_count, float* out, const ckv_layer* next, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

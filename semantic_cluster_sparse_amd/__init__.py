@@ -24,6 +24,8 @@ from .ckv import (  # noqa: F401
     ckv_last_error,
     ckv_select,
     ckv_select_decode,
+    ckv_select_decode_noalloc,
+    ckv_select_decode_noalloc_limit,
     ckv_select_decode_per_head,
     ckv_select_per_head,
     ckv_sparse_decode,

@@ -112,6 +112,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_select_decode_per_head.restype = c_int
     lib.ckv_select_decode_per_head.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, LP, c_void_p,
                                                c_size_t, c_void_p]
+    lib.ckv_select_decode_noalloc_limit.restype = c_size_t
+    lib.ckv_select_decode_noalloc_limit.argtypes = []
+    lib.ckv_select_decode_noalloc.restype = c_int
+    lib.ckv_select_decode_noalloc.argtypes = [LP, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, LP, c_void_p]
     if lib.ckv_abi_layer_bytes() != ctypes.sizeof(CkvLayerStruct):
         raise RuntimeError("ckv_layer layout mismatch between libckv.so and the binding")
     if path is None:
@@ -242,3 +246,14 @@ def ckv_select_decode_per_head(layer: CkvLayerStruct, q: int, budget: int, sel_p
     _check("ckv_select_decode_per_head",
            load_library().ckv_select_decode_per_head(_ref(layer), q, budget, sel_pos, sel_count, out,
                                                      _opt_ref(next_layer), ws, ws_bytes, stream))
+
+
+def ckv_select_decode_noalloc_limit() -> int:
+    return int(load_library().ckv_select_decode_noalloc_limit())
+
+
+def ckv_select_decode_noalloc(layer: CkvLayerStruct, q: int, budget: int, sel_pos: int, sel_count: int, out: int,
+                              next_layer=None, stream: int = 0) -> None:
+    _check("ckv_select_decode_noalloc",
+           load_library().ckv_select_decode_noalloc(_ref(layer), q, budget, sel_pos, sel_count, out,
+                                                    _opt_ref(next_layer), stream))

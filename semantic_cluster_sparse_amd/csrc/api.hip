@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ckv.h"
 #include "launch.hpp"
 
@@ -444,9 +446,9 @@ int decode_impl(const ckv_layer* L, const uint16_t* q, const int32_t* sel_pos, c
   return hip_status(e, "sparse_decode");
 }
 
-int select_decode_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
-                       int32_t* sel_count, float* out, void* ws, size_t ws_bytes, void* stream,
-                       const uint16_t* k_new, const uint16_t* v_new, bool per_head, const ckv_layer* next) {
+// Checks shared by the fused recall + decode calls (everything but the scratch).
+int select_decode_check(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                        int32_t* sel_count, float* out, const uint16_t* k_new, const uint16_t* v_new) {
   int rc = check_layer(L);
   if (rc) return rc;
   if (budget < 0) return fail(CKV_EINVAL, "budget %d < 0", budget);
@@ -462,9 +464,15 @@ int select_decode_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, in
     if (rc) return rc;
     if (L->n_total >= L->capacity) return fail(CKV_ENOSPACE, "cache full (capacity %d)", L->capacity);
   }
-  rc = check_ws(L, ws, ws_bytes, per_head);
-  if (rc) return rc;
-  const Layout w = layout_of(L, per_head);
+  return CKV_OK;
+}
+
+// The fused launch over caller-provided scratch: split-K partials, arrival
+// counters (zero on entry, left zero) and the cut-cluster score area.
+int select_decode_launch(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                         int32_t* sel_count, float* out, void* stream, const uint16_t* k_new, const uint16_t* v_new,
+                         bool per_head, const ckv_layer* next, float* partials, uint32_t* counters,
+                         uint32_t* cut_scores) {
   const int units = L->batch * L->n_kv_heads;
   const int n_total = L->n_total + (k_new != nullptr ? 1 : 0);
   // the prefetch hint is used only for a layer laid out like this one
@@ -477,10 +485,22 @@ int select_decode_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, in
   }
   hipError_t e = ckv::launch_recall_decode(
       q, L->group, L->cmean, L->offsets, L->n_clusters, L->k_tok, L->v_tok, L->capacity, L->k_clu, L->v_clu,
-      L->capacity - L->n_sink, budget, L->n_sink, L->n_clustered, n_total, sel_pos, sel_count,
-      (float*)((char*)ws + w.off_partials), (uint32_t*)ws, (uint32_t*)((char*)ws + w.off_rd_cut), out, k_new, v_new,
-      pf_cmean, pf_offsets, units, per_head ? 1 : 0, (hipStream_t)stream);
+      L->capacity - L->n_sink, budget, L->n_sink, L->n_clustered, n_total, sel_pos, sel_count, partials, counters,
+      cut_scores, out, k_new, v_new, pf_cmean, pf_offsets, units, per_head ? 1 : 0, (hipStream_t)stream);
   return hip_status(e, "select_decode");
+}
+
+int select_decode_impl(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                       int32_t* sel_count, float* out, void* ws, size_t ws_bytes, void* stream,
+                       const uint16_t* k_new, const uint16_t* v_new, bool per_head, const ckv_layer* next) {
+  int rc = select_decode_check(L, q, budget, sel_pos, sel_count, out, k_new, v_new);
+  if (rc) return rc;
+  rc = check_ws(L, ws, ws_bytes, per_head);
+  if (rc) return rc;
+  const Layout w = layout_of(L, per_head);
+  return select_decode_launch(L, q, budget, sel_pos, sel_count, out, stream, k_new, v_new, per_head, next,
+                              (float*)((char*)ws + w.off_partials), (uint32_t*)ws,
+                              (uint32_t*)((char*)ws + w.off_rd_cut));
 }
 
 }  // namespace
@@ -550,6 +570,94 @@ int ckv_sparse_decode_per_head(const ckv_layer* L, const uint16_t* q, const int3
                                const int32_t* sel_count, int32_t budget, float* out, void* ws, size_t ws_bytes,
                                void* stream) {
   return decode_impl(L, q, sel_pos, sel_count, budget, out, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free fused call: its scratch lives in a file-scope device
+// array instead of a caller workspace.  Each device holds its own copy of the
+// array until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr size_t kNoAllocCounterBytes = (size_t)64 << 10;  // arrival counters: up to 16384 sets
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+bool g_scratch_cleared[kMaxDevices];        // its counters zero-filled on that device
+
+// Bytes of scratch one ckv_select_decode_noalloc call needs: the counters,
+// then the split-K partials, then the cut-cluster score area.
+size_t noalloc_bytes(const ckv_layer* L, int32_t budget) {
+  const size_t units = (size_t)L->batch * L->n_kv_heads;
+  const int m = clustered_tokens(L);
+  const int beff = budget < m ? budget : m;
+  const int rows = L->n_sink + beff + (L->n_total - L->n_clustered);
+  const int W = ckv::recall_decode_chunks((int)units, rows);
+  const size_t partials = align256(units * W * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
+  const size_t cut = align256(units * (size_t)(L->capacity - L->n_sink) * sizeof(uint32_t));
+  return kNoAllocCounterBytes + partials + cut;
+}
+
+// The scratch of the current device; the first call on a device looks up its
+// address and zero-fills the counters on `s` (with a kernel, so a caller may
+// capture it in a graph).
+int noalloc_scratch(hipStream_t s, unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CKV_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(CKV_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = (unsigned char*)p;
+  }
+  if (!g_scratch_cleared[dev]) {
+    e = ckv::launch_zero(g_scratch_ptr[dev], kNoAllocCounterBytes, s);
+    if (e != hipSuccess) return hip_status(e, "zero-fill of the no-alloc counters");
+    g_scratch_cleared[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return CKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ckv_select_decode_noalloc_limit(void) { return kNoAllocScratchBytes; }
+
+int ckv_select_decode_noalloc(const ckv_layer* L, const uint16_t* q, int32_t budget, int32_t* sel_pos,
+                              int32_t* sel_count, float* out, const ckv_layer* next, void* stream) {
+  int rc = select_decode_check(L, q, budget, sel_pos, sel_count, out, nullptr, nullptr);
+  if (rc) return rc;
+  const size_t units = (size_t)L->batch * L->n_kv_heads;
+  if (units * sizeof(uint32_t) > kNoAllocCounterBytes)
+    return fail(CKV_ENOSPACE, "no-alloc call: %zu units exceed the %zu counters", units,
+                kNoAllocCounterBytes / sizeof(uint32_t));
+  const size_t need = noalloc_bytes(L, budget);
+  if (need > kNoAllocScratchBytes)
+    return fail(CKV_ENOSPACE, "no-alloc call needs %zu bytes of scratch > the %zu-byte limit", need,
+                kNoAllocScratchBytes);
+  const int m = clustered_tokens(L);
+  const int beff = budget < m ? budget : m;
+  const int W = ckv::recall_decode_chunks((int)units, L->n_sink + beff + (L->n_total - L->n_clustered));
+  const size_t partial_bytes = align256(units * W * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
+  unsigned char* base = nullptr;
+  rc = noalloc_scratch((hipStream_t)stream, &base);
+  if (rc) return rc;
+  return select_decode_launch(L, q, budget, sel_pos, sel_count, out, stream, nullptr, nullptr, false, next,
+                              (float*)(base + kNoAllocCounterBytes), (uint32_t*)base,
+                              (uint32_t*)(base + kNoAllocCounterBytes + partial_bytes));
 }
 
 }  // extern "C"

@@ -75,6 +75,11 @@ hipError_t launch_sparse_decode(const uint16_t* q, int group, const uint16_t* k_
                                 float* partials, uint32_t* counters, float* out, int units,
                                 int per_head, hipStream_t s);
 
+// Chunks (workgroups) per attended set of a fused recall + decode launch over
+// `sets` sets of `rows` attended rows each; its split-K partials take
+// sets * chunks * group_tier * kPartialStride floats.
+int recall_decode_chunks(int sets, int rows);
+
 // Recall and sparse decode in one launch: every workgroup of a set recalls
 // the set itself, then streams its chunk of the attended rows (sinks, recent
 // rows, whole clusters, the cut's kept tokens) and the last chunk merges.

@@ -467,6 +467,16 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   }
 }
 
+int recall_decode_chunks(int sets, int rows) {
+  // about 256 workgroups per launch (one per CU), chunks of at least 64 rows
+  int W = (256 + sets - 1) / sets;
+  if (W > kMaxChunks) W = kMaxChunks;
+  const int wmax = (rows + 63) / 64;
+  if (W > wmax) W = wmax;
+  if (W < 1) W = 1;
+  return W;
+}
+
 hipError_t launch_recall_decode(const uint16_t* q, int group, const float* cmean, const int32_t* offsets, int K,
                                 uint16_t* k_tok, uint16_t* v_tok, int capacity, const uint16_t* k_clu,
                                 const uint16_t* v_clu, int clu_stride, int budget, int n_sink, int n_clustered,
@@ -479,13 +489,7 @@ hipError_t launch_recall_decode(const uint16_t* q, int group, const float* cmean
   const int sets = units * hs;
   const int m = n_clustered - n_sink;
   const int beff = budget < m ? budget : m;
-  const int rows = n_sink + beff + (n_total - n_clustered);
-  // about 256 workgroups per launch (one per CU), chunks of at least 64 rows
-  int W = (256 + sets - 1) / sets;
-  if (W > kMaxChunks) W = kMaxChunks;
-  const int wmax = (rows + 63) / 64;
-  if (W > wmax) W = wmax;
-  if (W < 1) W = 1;
+  const int W = recall_decode_chunks(sets, n_sink + beff + (n_total - n_clustered));
   const dim3 grid((unsigned)(sets * W));
   int gt = 1;
   while (gt < Ge) gt <<= 1;

@@ -206,3 +206,12 @@ class Layer:
         ckv.ckv_select_decode_per_head(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
                                        out.data_ptr(), _struct(next_layer), self.ws.data_ptr(), self.ws_bytes,
                                        _stream())
+
+    def select_decode_noalloc(self, q: torch.Tensor, budget: int, sel_pos: torch.Tensor, sel_count: torch.Tensor,
+                              out: torch.Tensor, next_layer: "Layer | None" = None) -> None:
+        """ckv_select_decode without the workspace (the library's per-device scratch array)."""
+        assert q.is_contiguous() and q.numel() == self.units * self.group * HEAD_DIM
+        assert sel_pos.numel() >= self.units * budget and sel_count.numel() >= self.units
+        assert out.is_contiguous() and out.dtype == torch.float32 and out.numel() == self.units * self.group * HEAD_DIM
+        ckv.ckv_select_decode_noalloc(self.struct, q.data_ptr(), budget, sel_pos.data_ptr(), sel_count.data_ptr(),
+                                      out.data_ptr(), _struct(next_layer), _stream())

@@ -256,6 +256,19 @@ def test_select_decode_host_rules():
     assert ckv.ckv_workspace_bytes_per_head(L3, 2048) >= ckv.ckv_workspace_bytes(L3, 2048)
 
 
+def test_select_decode_noalloc_host_rules():
+    assert ckv.ckv_select_decode_noalloc_limit() == 16 << 20
+    # the cut-score area alone (64 units x 131056 rows x 4 B) is beyond the limit: refused before any launch
+    big = _fill_ptrs(_layer(batch=64, n_kv_heads=1, capacity=131072, n_total=131072, n_clustered=131072))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_select_decode_noalloc(big, FAKE, 2048, FAKE, FAKE, FAKE)
+    assert e.value.code == ckv.CKV_ENOSPACE and "limit" in e.value.message
+    L = _fill_ptrs(_layer(capacity=100, n_clusters=8, n_total=100, n_clustered=100))
+    with pytest.raises(ckv.CkvError) as e:
+        ckv.ckv_select_decode_noalloc(L, FAKE, -1, FAKE, FAKE, FAKE)
+    assert e.value.code == ckv.CKV_EINVAL
+
+
 def test_missing_library_fails_loudly(tmp_path):
     # the binding has no fallback: without the built library every call path raises
     with pytest.raises(RuntimeError, match="libckv.so not found"):
