@@ -34,6 +34,8 @@ bf16 mode, a fixed point, brute-force optimum on tiny inputs, a hand-worked
 golden example; ``kmeans.build_index`` -- bijection / scan / stability;
 ``kmeans.scoring_centroids`` -- Jensen's inequality, the tight-cluster limit
 and the Gaussian closed form of the centroid approximation (§3.1);
+``init.init_indices`` -- published SplitMix64 outputs, a hand-worked Floyd
+draw, distinctness, range, determinism and uniformity over subsets;
 ``select.select_unit`` -- a hand-worked golden example, an independent
 total-order formulation, exact count, prefix property, budget >= m;
 ``attention.attend`` -- torch's float64 SDPA, |S| = 1, q = 0, order and shift
@@ -47,4 +49,4 @@ invariants; reserved slots -- Lloyd with reserves equals Lloyd without them
 when no key is an outlier, and an outlier lands in the reserve.
 """
 
-from . import bf16, kmeans, select, attention, pipeline  # noqa: F401
+from . import bf16, kmeans, select, attention, pipeline, init  # noqa: F401

@@ -3,7 +3,9 @@
 Each case monkeypatches one plausible slip into the oracle (on the CPU) and
 checks that a pin from the other test files fails on it: a dropped
 normalisation, ties to the wrong index, a dropped 1/sqrt(d), a reversed
-cluster order, an unstable index, recent tokens left out of the attended set.
+cluster order, an unstable index, recent tokens left out of the attended set,
+and in the seeded init a wrong modulus, a duplicate insert and a wrong
+generator constant.
 """
 
 import json
@@ -14,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, bf16, kmeans, pipeline, select
+from oracle import attention, bf16, init, kmeans, pipeline, select
 
 
 def _kmeans_golden_ok(golden_dir):
@@ -103,3 +105,43 @@ def test_missing_recent_rows_is_caught(monkeypatch):
                         lambda kt, vt, kc, vc, p, s, nc, nt: orig(kt, vt, kc, vc, p, s, nc, nc))
     K, _ = attention.attended_rows(k_tok, k_tok, k_tok, k_tok, [1], 2, 7, 9)
     assert len(K) != 2 + 1 + 2
+
+
+def _init_golden_ok(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "init_floyd_tiny.json")))
+    st = init.splitmix64(g["splitmix64"]["state"])
+    if [next(st) for _ in range(3)] != [int(h, 16) for h in g["splitmix64"]["outputs_hex"]]:
+        return False
+    for case in ("floyd", "floyd_all"):
+        c = g[case]
+        if init.floyd_sample(c["m"], c["k"], iter(c["draws"])) != c["indices"]:
+            return False
+    return True
+
+
+def test_unplanted_init_passes(golden_dir):
+    assert _init_golden_ok(golden_dir)
+
+
+def test_init_modulus_off_by_one_is_caught(golden_dir, monkeypatch):
+    def bad(m, k, draws):
+        out, seen = [], set()
+        for j in range(m - k, m):
+            t = next(draws) % max(j, 1)          # j instead of j + 1
+            p = t if t not in seen else j
+            seen.add(p)
+            out.append(p)
+        return out
+    monkeypatch.setattr(init, "floyd_sample", bad)
+    assert not _init_golden_ok(golden_dir)
+
+
+def test_init_duplicate_insert_is_caught(golden_dir, monkeypatch):
+    monkeypatch.setattr(init, "floyd_sample",
+                        lambda m, k, draws: [next(draws) % (j + 1) for j in range(m - k, m)])
+    assert not _init_golden_ok(golden_dir)
+
+
+def test_init_generator_constant_is_caught(golden_dir, monkeypatch):
+    monkeypatch.setattr(init, "GOLDEN_GAMMA", 0x9E3779B97F4A7C13)
+    assert not _init_golden_ok(golden_dir)
