@@ -367,14 +367,14 @@ def run_stack(cfg, args) -> dict:
     log(f"[bench] generated inputs; {torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
     # ---------------------------------------------------------------- prefill (timed separately)
-    inits = [dgen.init_indices(units, cfg.m, cfg.n_clusters, seed=30_000 + so + li, device=dev)
-             for li in range(n_layers)]
+    # seeded prefill: the library draws each unit's initial indices (seed + unit); layers get disjoint seeds
+    seeds = [30_000 + so + li * units for li in range(n_layers)]
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for li, L in enumerate(layers):
-        L.prefill(cfg.n_tokens, cfg.iters, inits[li])
+        L.prefill(cfg.n_tokens, cfg.iters, seeds[li])
     ev1.record(stream)
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t0
@@ -382,7 +382,6 @@ def run_stack(cfg, args) -> dict:
     keys = n_layers * units * cfg.m
     log(f"[bench] prefill {prefill_s * 1e3:.1f} ms wall, {prefill_ev_s * 1e3:.1f} ms events; "
         f"{keys / prefill_ev_s / 1e6:.1f} M keys/s")
-    del inits
     assign = time_assign(layers, cfg, units, stream)
     # the recent tokens past the clustered prefix are already in the token-order rows
     for L in layers:

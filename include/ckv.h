@@ -113,12 +113,11 @@ int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream);
 /*
  * Prefill clustering (ClusterKV article §3.2 prefill; §3.1 centroid; §4.1 layout).
  * Clusters tokens [n_sink, n) of every unit into K clusters by cosine K-means:
- *   init     c_j = bf16(x_I(j) / |x_I(j)|) with I = init_idx[u, :] -- K distinct
- *            indices in [0, m) into the clustered tokens, drawn by the caller
- *            (device int32 [units, K]); an index outside [0, m) gives a zero
- *            direction: -1 holds slot j in reserve for ckv_cluster_split (a
- *            zero direction scores 0 against every key, so the slot stays
- *            empty unless a key scores below 0 against every other direction);
+ *   init     c_j = bf16(x_I(j) / |x_I(j)|) where I are K distinct indices in
+ *            [0, m), m = n - n_sink, into the clustered tokens: the draw
+ *            ckv_init_indices makes from `seed` (the article does not say how
+ *            K-means is initialised; the reading taken is a uniform draw
+ *            without replacement);
  *   iters rounds of: a_i = argmax_j x_i . c_j (ties -> smallest j);
  *            S_j = sum of unit keys of members; c_j = bf16_rne(S_j / |S_j|)
  *            (empty or zero-sum clusters keep c_j);
@@ -129,8 +128,32 @@ int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * n <= capacity, iters >= 1, and no pending ckv_cluster_incremental_async
  * result.  Sets n_total = n_clustered = n on success.
  */
-int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
-                        void* ws, size_t ws_bytes, void* stream);
+int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, uint64_t seed, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * The seeded initial indices of ckv_cluster_prefill (its initialisation
+ * step, exposed so that callers can inspect or reuse the draw): for every
+ * unit u, K distinct indices in [0, m), m = n - n_sink, drawn by Floyd's
+ * sampling algorithm (Bentley and Floyd, CACM 1987) from the outputs of
+ * SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) started from state
+ * seed + u: for j = m - K .. m - 1, t = r mod (j + 1) for the next output r;
+ * t is taken unless already taken, else j.  init_idx[u, j] is the j-th index
+ * taken (device int32 [units, K], written).  Requirements as for the prefill's
+ * n; no workspace.
+ */
+int ckv_init_indices(const ckv_layer* L, int32_t n, uint64_t seed, int32_t* init_idx, void* stream);
+
+/*
+ * ckv_cluster_prefill from caller-given initial indices instead of a seed:
+ * init_idx is device int32 [units, K], K distinct indices in [0, m) per unit;
+ * an index outside [0, m) gives a zero direction: -1 holds slot j in reserve
+ * for ckv_cluster_split (a zero direction scores 0 against every key, so the
+ * slot stays empty unless a key scores below 0 against every other
+ * direction).  Everything else as for ckv_cluster_prefill.
+ */
+int ckv_cluster_prefill_indices(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /*
  * Append one decoded token per unit (ClusterKV article §3.2, decoding-stage

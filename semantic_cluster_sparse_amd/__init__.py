@@ -20,6 +20,8 @@ from .ckv import (  # noqa: F401
     ckv_cluster_incremental,
     ckv_cluster_incremental_async,
     ckv_cluster_prefill,
+    ckv_cluster_prefill_indices,
+    ckv_init_indices,
     ckv_cluster_split,
     ckv_last_error,
     ckv_select,

@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_double, c_int, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_double, c_int, c_int32, c_size_t, c_uint64, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_lib", "libckv.so")
@@ -75,7 +75,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.ckv_workspace_init.restype = c_int
     lib.ckv_workspace_init.argtypes = [c_void_p, c_size_t, c_void_p]
     lib.ckv_cluster_prefill.restype = c_int
-    lib.ckv_cluster_prefill.argtypes = [LP, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ckv_cluster_prefill.argtypes = [LP, c_int32, c_int32, c_uint64, c_void_p, c_size_t, c_void_p]
+    lib.ckv_cluster_prefill_indices.restype = c_int
+    lib.ckv_cluster_prefill_indices.argtypes = [LP, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.ckv_init_indices.restype = c_int
+    lib.ckv_init_indices.argtypes = [LP, c_int32, c_uint64, c_void_p, c_void_p]
     lib.ckv_append.restype = c_int
     lib.ckv_append.argtypes = [LP, c_void_p, c_void_p, c_void_p]
     lib.ckv_cluster_incremental.restype = c_int
@@ -151,10 +155,21 @@ def ckv_workspace_init(ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check("ckv_workspace_init", load_library().ckv_workspace_init(ws, ws_bytes, stream))
 
 
-def ckv_cluster_prefill(layer: CkvLayerStruct, n: int, iters: int, init_idx: int, ws: int,
+def ckv_cluster_prefill(layer: CkvLayerStruct, n: int, iters: int, seed: int, ws: int,
                         ws_bytes: int, stream: int = 0) -> None:
     _check("ckv_cluster_prefill",
-           load_library().ckv_cluster_prefill(_ref(layer), n, iters, init_idx, ws, ws_bytes, stream))
+           load_library().ckv_cluster_prefill(_ref(layer), n, iters, seed & (2 ** 64 - 1), ws, ws_bytes, stream))
+
+
+def ckv_cluster_prefill_indices(layer: CkvLayerStruct, n: int, iters: int, init_idx: int, ws: int,
+                                ws_bytes: int, stream: int = 0) -> None:
+    _check("ckv_cluster_prefill_indices",
+           load_library().ckv_cluster_prefill_indices(_ref(layer), n, iters, init_idx, ws, ws_bytes, stream))
+
+
+def ckv_init_indices(layer: CkvLayerStruct, n: int, seed: int, init_idx: int, stream: int = 0) -> None:
+    _check("ckv_init_indices",
+           load_library().ckv_init_indices(_ref(layer), n, seed & (2 ** 64 - 1), init_idx, stream))
 
 
 def ckv_append(layer: CkvLayerStruct, k_new: int, v_new: int, stream: int = 0) -> None:

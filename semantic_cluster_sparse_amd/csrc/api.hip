@@ -191,8 +191,12 @@ int ckv_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hip_status(ckv::launch_zero(ws, ws_bytes, (hipStream_t)stream), "workspace init");
 }
 
-int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx, void* ws,
-                        size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a prefill call (everything but the initial indices).
+int prefill_check(ckv_layer* L, int32_t n, int32_t iters, void* ws, size_t ws_bytes) {
   int rc = check_layer(L);
   if (rc) return rc;
   if (iters < 1) return fail(CKV_EINVAL, "iters %d < 1", iters);
@@ -202,21 +206,21 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
                 L->n_pending);
   const int m = n - L->n_sink;
   if (m < L->n_clusters) return fail(CKV_EINVAL, "need n_clusters %d <= m = n - n_sink = %d", L->n_clusters, m);
-  rc = check_ptrs("k_tok,v_tok,k_clu,v_clu,cdir,csum,msum,cmean,csize,offsets,assign,perm,init_idx", 13,
-                  L->k_tok, L->v_tok, L->k_clu, L->v_clu, L->cdir, L->csum, L->msum, L->cmean, L->csize,
-                  L->offsets, L->assign, L->perm, init_idx);
+  rc = check_ptrs("k_tok,v_tok,k_clu,v_clu,cdir,csum,msum,cmean,csize,offsets,assign,perm", 12, L->k_tok, L->v_tok,
+                  L->k_clu, L->v_clu, L->cdir, L->csum, L->msum, L->cmean, L->csize, L->offsets, L->assign, L->perm);
   if (rc) return rc;
-  rc = check_ws(L, ws, ws_bytes);
-  if (rc) return rc;
+  return check_ws(L, ws, ws_bytes);
+}
 
-  const hipStream_t s = (hipStream_t)stream;
+// The prefill's kernels from the initial indices init_idx [units, K] on.
+int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx, void* ws, hipStream_t s) {
+  const int m = n - L->n_sink;
   const int units = L->batch * L->n_kv_heads;
   const int K = L->n_clusters;
   const int clu_stride = L->capacity - L->n_sink;
   const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
   const Layout w = layout_of(L);
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
-
   double* invn = (double*)((char*)ws + w.off_invn);
 
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
@@ -238,6 +242,45 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, const int32_t* i
   L->n_total = n;
   L->n_clustered = n;
   return CKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ckv_init_indices(const ckv_layer* L, int32_t n, uint64_t seed, int32_t* init_idx, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (n > L->capacity) return fail(CKV_EINVAL, "n %d > capacity %d", n, L->capacity);
+  const int m = n - L->n_sink;
+  if (m < L->n_clusters) return fail(CKV_EINVAL, "need n_clusters %d <= m = n - n_sink = %d", L->n_clusters, m);
+  rc = check_ptrs("init_idx", 1, init_idx);
+  if (rc) return rc;
+  const hipError_t e =
+      ckv::launch_init_draw(seed, m, L->n_clusters, init_idx, L->batch * L->n_kv_heads, (hipStream_t)stream);
+  return hip_status(e, "init draw");
+}
+
+int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, uint64_t seed, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = prefill_check(L, n, iters, ws, ws_bytes);
+  if (rc) return rc;
+  // the drawn indices live in the histogram region until the first round's histogram overwrites them
+  const Layout w = layout_of(L);
+  int32_t* idx = (int32_t*)((char*)ws + w.off_hist);
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = ckv::launch_init_draw(seed, n - L->n_sink, L->n_clusters, idx, L->batch * L->n_kv_heads, s);
+  if (e != hipSuccess) return hip_status(e, "init draw");
+  return prefill_run(L, n, iters, idx, ws, s);
+}
+
+int ckv_cluster_prefill_indices(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx, void* ws,
+                                size_t ws_bytes, void* stream) {
+  int rc = prefill_check(L, n, iters, ws, ws_bytes);
+  if (rc) return rc;
+  rc = check_ptrs("init_idx", 1, init_idx);
+  if (rc) return rc;
+  return prefill_run(L, n, iters, init_idx, ws, (hipStream_t)stream);
 }
 
 int ckv_append(ckv_layer* L, const uint16_t* k_new, const uint16_t* v_new, void* stream) {

@@ -16,6 +16,84 @@
 namespace ckv {
 
 // ---------------------------------------------------------------------------
+// Seeded initial indices (the prefill's initialisation, which the ClusterKV
+// article leaves open): K distinct clustered-token indices per unit drawn by
+// Floyd's sampling algorithm (Bentley and Floyd, CACM 1987) from SplitMix64
+// outputs (Steele, Lea and Flood, OOPSLA 2014), state seed + unit.  For
+// j = m - K .. m - 1 a draw r gives t = r mod (j + 1); t is inserted unless it
+// is already in the sample, in which case j is.  The draws are sequential, so
+// one workgroup per unit makes them.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t splitmix64_next(uint64_t& x) {
+  x += 0x9E3779B97F4A7C15ull;
+  uint64_t z = x;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Membership of the indices drawn so far: a bitmap over [0, m) in LDS when it
+// fits (one lane then makes the draws, with no barrier between them), else the
+// list of draws scanned by all 64 lanes.
+constexpr int kDrawBitmapWords = 16384;  // 64 KiB of LDS: m up to 524288
+
+__global__ __launch_bounds__(64) void init_draw_bitmap_kernel(uint64_t seed, int m, int K,
+                                                              int32_t* __restrict__ init_idx) {
+  extern __shared__ uint32_t bitmap[];
+  const int u = blockIdx.x;
+  const int words = (m + 31) >> 5;
+  for (int i = threadIdx.x; i < words; i += kWave) bitmap[i] = 0u;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint64_t x = seed + (uint64_t)u;
+  int32_t* out = init_idx + (size_t)u * K;
+  for (int i = 0; i < K; ++i) {
+    const int j = m - K + i;
+    const int t = (int)(splitmix64_next(x) % (uint64_t)(j + 1));
+    const bool taken = (bitmap[t >> 5] >> (t & 31)) & 1u;
+    const int pick = taken ? j : t;  // j itself is never taken yet: every earlier pick is below it
+    bitmap[pick >> 5] |= 1u << (pick & 31);
+    out[i] = pick;
+  }
+}
+
+__global__ __launch_bounds__(64) void init_draw_kernel(uint64_t seed, int m, int K, int32_t* __restrict__ init_idx) {
+  __shared__ int chosen[kMaxClusters];
+  const int u = blockIdx.x;
+  const int lane = lane_id();
+  uint64_t x = seed + (uint64_t)u;
+  for (int i = 0; i < K; ++i) {
+    const int j = m - K + i;
+    const uint64_t r = splitmix64_next(x);  // the same draw in every lane
+    const int t = (int)(r % (uint64_t)(j + 1));
+    bool hit = false;
+    for (int c = lane; c < i; c += kWave) hit |= chosen[c] == t;
+    const int pick = __ballot(hit) ? j : t;
+    if (lane == 0) chosen[i] = pick;
+    __syncthreads();  // the insert is seen by every lane's next membership test
+  }
+  for (int i = lane; i < K; i += kWave) init_idx[(size_t)u * K + i] = chosen[i];
+}
+
+hipError_t launch_init_draw(uint64_t seed, int m, int K, int32_t* init_idx, int units, hipStream_t s) {
+  const int words = (m + 31) / 32;
+  if (words <= kDrawBitmapWords) {
+    static std::once_flag lds_attr;  // the bitmap may exceed the default dynamic LDS limit
+    static hipError_t lds_err = hipSuccess;
+    std::call_once(lds_attr, [] {
+      lds_err = hipFuncSetAttribute((const void*)init_draw_bitmap_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kDrawBitmapWords * 4);
+    });
+    if (lds_err != hipSuccess) return lds_err;
+    hipLaunchKernelGGL(init_draw_bitmap_kernel, dim3((unsigned)units), dim3(kWave), (size_t)words * 4, s, seed, m, K,
+                       init_idx);
+  } else {
+    hipLaunchKernelGGL(init_draw_kernel, dim3((unsigned)units), dim3(kWave), 0, s, seed, m, K, init_idx);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Initial directions: one wave per (unit, cluster); lane l holds dims 2l, 2l+1.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void init_dirs_kernel(const uint16_t* __restrict__ k_tok,

@@ -16,6 +16,10 @@ constexpr int kPartialStride = 130; // floats per (chunk, head) partial: o[128],
 
 enum UpdateMode { kUpdIter = 0, kUpdFinal = 1, kUpdIncr = 2 };
 
+// init_idx[u, 0:K] = Floyd's sample of K distinct indices in [0, m) driven
+// by SplitMix64 from state seed + u (K <= kMaxClusters, K <= m).
+hipError_t launch_init_draw(uint64_t seed, int m, int K, int32_t* init_idx, int units, hipStream_t s);
+
 // c_j = bf16(x_idx / |x_idx|) for idx = init_idx[u, j] (zero if idx outside [0, m)).
 hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int m,
                             const int32_t* init_idx, int K, uint16_t* cdir, int units,

@@ -88,11 +88,23 @@ class Layer:
         self.struct.n_clustered = n_clustered
 
     # ----------------------------------------------------------------- calls
-    def prefill(self, n: int, iters: int, init_idx: torch.Tensor) -> None:
-        assert init_idx.dtype == torch.int32 and init_idx.is_contiguous()
-        assert tuple(init_idx.shape) == (self.units, self.n_clusters)
-        ckv.ckv_cluster_prefill(self.struct, n, iters, init_idx.data_ptr(), self.ws.data_ptr(),
-                                self.ws_bytes, _stream())
+    def prefill(self, n: int, iters: int, init) -> None:
+        """Prefill clustering of tokens [n_sink, n): `init` is a seed (int; the
+        library draws the initial indices, ckv_cluster_prefill) or the initial
+        indices themselves (int32 [units, K] tensor, ckv_cluster_prefill_indices)."""
+        if isinstance(init, int):
+            ckv.ckv_cluster_prefill(self.struct, n, iters, init, self.ws.data_ptr(), self.ws_bytes, _stream())
+            return
+        assert init.dtype == torch.int32 and init.is_contiguous()
+        assert tuple(init.shape) == (self.units, self.n_clusters)
+        ckv.ckv_cluster_prefill_indices(self.struct, n, iters, init.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                                        _stream())
+
+    def init_indices(self, n: int, seed: int) -> torch.Tensor:
+        """The initial indices the seeded prefill of tokens [n_sink, n) draws (ckv_init_indices)."""
+        out = torch.empty((self.units, self.n_clusters), dtype=torch.int32, device=self.device)
+        ckv.ckv_init_indices(self.struct, n, seed, out.data_ptr(), _stream())
+        return out
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         assert k_new.shape == (self.units, HEAD_DIM) and v_new.shape == (self.units, HEAD_DIM)

@@ -79,7 +79,7 @@ def test_workspace_bytes_and_errors():
 def test_layer_validation(field, value, code):
     L = _fill_ptrs(_layer(**{field: value}))
     with pytest.raises(ckv.CkvError) as e:
-        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1 << 40)
+        ckv.ckv_cluster_prefill(L, 32768, 10, 1234, FAKE, 1 << 40)
     assert e.value.code == code
     assert ckv.ckv_last_error()
 
@@ -93,17 +93,26 @@ def test_prefill_argument_errors():
     ]
     for kw, code in cases:
         with pytest.raises(ckv.CkvError) as e:
-            ckv.ckv_cluster_prefill(L, kw["n"], kw["iters"], FAKE, FAKE, 1 << 40)
+            ckv.ckv_cluster_prefill(L, kw["n"], kw["iters"], 1234, FAKE, 1 << 40)
+        with pytest.raises(ckv.CkvError) as e:
+            ckv.ckv_cluster_prefill_indices(L, kw["n"], kw["iters"], FAKE, FAKE, 1 << 40)
+        assert e.value.code == code, kw
         assert e.value.code == code, kw
     with pytest.raises(ckv.CkvError) as e:                      # misaligned init_idx
-        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE + 4, FAKE, 1 << 40)
+        ckv.ckv_cluster_prefill_indices(L, 32768, 10, FAKE + 4, FAKE, 1 << 40)
     assert e.value.code == ckv.CKV_EINVAL
     with pytest.raises(ckv.CkvError) as e:                      # workspace too small
-        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1024)
+        ckv.ckv_cluster_prefill(L, 32768, 10, 1234, FAKE, 1024)
     assert e.value.code == ckv.CKV_ENOSPACE
+    with pytest.raises(ckv.CkvError) as e:                      # no output for the drawn indices
+        ckv.ckv_init_indices(L, 32768, 1234, None)
+    assert e.value.code == ckv.CKV_EINVAL
+    with pytest.raises(ckv.CkvError) as e:                      # K > m
+        ckv.ckv_init_indices(L, 100, 1234, FAKE)
+    assert e.value.code == ckv.CKV_EINVAL
     L.k_tok = None
     with pytest.raises(ckv.CkvError) as e:
-        ckv.ckv_cluster_prefill(L, 32768, 10, FAKE, FAKE, 1 << 40)
+        ckv.ckv_cluster_prefill(L, 32768, 10, 1234, FAKE, 1 << 40)
     assert e.value.code == ckv.CKV_EINVAL
     assert L.n_total == 0 and L.n_clustered == 0               # nothing advanced
 
@@ -163,7 +172,8 @@ def test_async_incremental_and_commit_host_rules():
     P = _fill_ptrs(_layer(capacity=200, n_clusters=8, n_total=130, n_clustered=100, n_pending=120))
     for call in (lambda: ckv.ckv_cluster_incremental_async(P, FAKE, 1 << 40),
                  lambda: ckv.ckv_cluster_incremental(P, FAKE, 1 << 40),
-                 lambda: ckv.ckv_cluster_prefill(P, 130, 2, FAKE, FAKE, 1 << 40)):
+                 lambda: ckv.ckv_cluster_prefill(P, 130, 2, 1234, FAKE, 1 << 40),
+                 lambda: ckv.ckv_cluster_prefill_indices(P, 130, 2, FAKE, FAKE, 1 << 40)):
         with pytest.raises(ckv.CkvError) as e:
             call()
         assert e.value.code == ckv.CKV_EINVAL and "pending" in e.value.message
