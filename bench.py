@@ -44,6 +44,14 @@ decode kernel attends to all cached tokens; and the assignment step alone
 (``assign_roofline``: ckv_assign over every layer after the prefill, against
 the bf16 MFMA peak).
 
+``--workload single-head-2k`` and ``--workload llama8b-layer-32k``: one
+layer (1 unit with one query head, K = 24, budget 256; or 8 KV heads x 4
+query heads, K = 400, budget 1024) through the same prefill and 200 fused
+decode steps; their ``cpu_baseline`` times the oracle on every unit.
+
+Every line reports the measured 1 GiB device-copy rate beside the HBM peak
+(``roofline.copy_gbs``, ``roofline.frac_of_copy``).
+
 Inputs are synthetic (seeded Gaussian-mixture keys on the GPU) and resident
 in HBM before the timed region.  Decode steps are captured once each as a HIP
 graph (the per-step host counters differ, so every step has its own graph)
@@ -139,8 +147,32 @@ def measured_traffic(kernel: str):
     return t["fetch_kib"] * 1024 * 2.0 + t["write_kib"] * 1024 * 1.0
 
 
+def copy_bandwidth(dev) -> float:
+    """Measured device-to-device copy rate of 1 GiB (bytes read + written per second, GB/s):
+    the practical HBM rate a streaming kernel can reach, reported beside the 8 TB/s peak."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 3 * 2 * src.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"[bench] device copy of 1 GiB: {gbs:.0f} GB/s (read + write)")
+    return gbs
+
+
 def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
-    """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
+    """The oracle, untuned, on the host cores: on every unit of the workload when
+    it has at most 8 (timed in full), else on a bounded sample extrapolated to
+    the workload's units."""
     import numpy as np
 
     import synth
@@ -153,9 +185,11 @@ def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
         threads = 1
     t_pre = t_dec = 0.0
     n_units = n_unit_steps = 0
-    deadline = time.perf_counter() + seconds
+    units_total = cfg.layers * cfg.units
+    full = units_total <= 8
+    deadline = time.perf_counter() + (float("inf") if full else seconds)
     u = 0
-    while time.perf_counter() < deadline and u < 64:
+    while time.perf_counter() < deadline and u < min(64, units_total):
         kb, vb, cen = synth.make_unit_inputs(cfg.data_seed, u, cfg.n_tokens, cfg.components)
         init = synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters, unit_ids=[u])[0]
         t0 = time.perf_counter()
@@ -171,16 +205,18 @@ def run_cpu_baseline(cfg, steps: int, seconds: float = 20.0) -> dict:
             t_dec += time.perf_counter() - t0
             n_unit_steps += 1
         u += 1
-    units_total = cfg.layers * cfg.units
     step_s = t_dec / n_unit_steps * units_total
+    sample = (f"every unit ({n_units}) of the workload, {steps} decode steps each (select + decode, float64 "
+              f"NumPy), and its whole prefill: timed in full" if full else
+              f"{n_units} units x {steps} decode steps (select + decode, float64 NumPy) of the same "
+              f"workload, extrapolated to {units_total} units per step; prefill of the same "
+              f"{n_units} units timed for K-means keys/s")
     return {
         "value": cfg.batch / step_s,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{n_units} units x {steps} decode steps (select + decode, float64 NumPy) of the same "
-                   f"workload, extrapolated to {units_total} units per step; prefill of the same "
-                   f"{n_units} units timed for K-means keys/s"),
+        "sample": sample,
         "kmeans_keys_per_s": n_units * cfg.m / t_pre,
         "seconds": t_pre + t_dec,
     }
@@ -594,6 +630,7 @@ def run_stack(cfg, args) -> dict:
         full["step_speedup"] = n_layers * full["decode_us"] * 1e-3 / ms_per_step
     traffic = (measured_traffic("recall_decode" if fused else "sparse_decode")
                if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph else None)
+    copy_gbs = copy_bandwidth(dev)
 
     result = {
         "metric": METRIC,
@@ -619,7 +656,8 @@ def run_stack(cfg, args) -> dict:
                                f"<{1 if ph else _group_tier(G)}>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes},
+                     "launch_us": dec_ms * 1e3, "bytes_per_launch": dbytes,
+                     "copy_gbs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "step_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kmeans_keys_per_s": keys / prefill_ev_s,
         "prefill_ms": prefill_ev_s * 1e3,
@@ -733,6 +771,7 @@ def run_incremental(cfg, args) -> dict:
         return sorted(x)[len(x) // 2]
 
     inc_ms = med(t_inc)
+    copy_gbs = copy_bandwidth(dev)
     ibytes = incremental_bytes(units, cfg.n_clusters, cfg.m, n_new)
     achieved = ibytes / (inc_ms * 1e-3) / 1e9
     log(f"[bench] ckv_cluster_incremental {inc_ms * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic; "
@@ -767,12 +806,51 @@ def run_incremental(cfg, args) -> dict:
         "roofline": {"bound": "hbm", "kernel": "ckv_cluster_incremental (whole call)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "launch_us": inc_ms * 1e3, "bytes_per_launch": ibytes},
+                     "launch_us": inc_ms * 1e3, "bytes_per_launch": ibytes,
+                     "copy_gbs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "select_us": med(t_sel) * 1e3,
         "select_before_incremental_us": med(t_sel0) * 1e3,
         "sparse_decode_us": med(t_dec) * 1e3,
         **extra,
     }
+
+
+def run_cpu_baseline_incremental(cfg, seconds: float = 20.0) -> dict:
+    """The oracle's incremental pass (the same 320 new keys per unit, 10% from 8
+    new components) on a bounded sample of units, each after its own oracle
+    prefill (untimed), extrapolated to the workload's units."""
+    import numpy as np
+
+    import synth
+    from oracle import pipeline
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t_inc = 0.0
+    n_units = 0
+    deadline = time.perf_counter() + seconds
+    n_new = cfg.n_tokens + cfg.new_tokens
+    while time.perf_counter() < deadline and n_units < cfg.units:
+        u = n_units
+        k, v, cen = synth.make_layer_inputs(cfg, units=[u], capacity=n_new)
+        kn, vn, _ = synth.make_new_tokens(cfg.data_seed, cen, cfg.new_tokens, cfg.new_components, cfg.new_fraction,
+                                          unit_ids=[u])
+        k[:, cfg.n_tokens:n_new] = kn
+        v[:, cfg.n_tokens:n_new] = vn
+        init = synth.make_init_indices(cfg.init_seed, 1, cfg.m, cfg.n_clusters, unit_ids=[u])[0]
+        st = pipeline.prefill_unit(k[0], cfg.n_tokens, init, cfg.n_clusters, cfg.iters, v_bits=v[0])
+        t0 = time.perf_counter()
+        pipeline.incremental_unit(st, k[0], n_new, v_bits=v[0])
+        t_inc += time.perf_counter() - t0
+        n_units += 1
+    us = t_inc / n_units * cfg.units * 1e6
+    return {"value": us, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": (f"the incremental pass of {n_units} units (each after its own untimed oracle prefill), "
+                       f"float64 NumPy, extrapolated to {cfg.units} units"),
+            "seconds": t_inc}
 
 
 def seed_offset(cfg) -> int:
@@ -788,7 +866,10 @@ def _group_tier(G: int) -> int:
 
 
 DEFAULT_WORKLOAD = "llama8b-stack-32k-b8"
-WORKLOADS = (DEFAULT_WORKLOAD, "glm4-stack-32k-b16", "llama8b-incremental-b16")
+WORKLOADS = (DEFAULT_WORKLOAD, "glm4-stack-32k-b16", "llama8b-incremental-b16", "single-head-2k",
+             "llama8b-layer-32k")
+# decode steps timed on the single-layer workloads when --steps is not given
+SINGLE_LAYER_STEPS = 200
 
 
 def main() -> int:
@@ -841,13 +922,18 @@ def main() -> int:
     cfg = synth.CONFIGS[args.workload]
     if args.workload == DEFAULT_WORKLOAD and args.steps is None:
         args.steps = 20
+    if cfg.layers == 1 and not cfg.new_tokens and args.steps is None:
+        args.steps = SINGLE_LAYER_STEPS
     if cfg.new_tokens and cfg.layers == 1:
         result = run_incremental(cfg, args)
     else:
         result = run_stack(cfg, args)
-    if args.workload == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
-        log("[bench] timing the oracle on the host (bounded sample)")
-        result["cpu_baseline"] = run_cpu_baseline(cfg, steps=3, seconds=args.cpu_seconds)
+    if not args.no_cpu_baseline and not args.per_head_recall and args.workload != "glm4-stack-32k-b16":
+        log("[bench] timing the oracle on the host")
+        if cfg.new_tokens and cfg.layers == 1:
+            result["cpu_baseline"] = run_cpu_baseline_incremental(cfg, seconds=args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = run_cpu_baseline(cfg, steps=3, seconds=args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 
