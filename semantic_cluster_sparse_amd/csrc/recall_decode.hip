@@ -96,15 +96,6 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   const int li = tid & 15;
   const int grp = tid >> 4;
 
-  // the appended token's row (its K/V are streamed from k_new / v_new, not
-  // read back from the row written here)
-  if (k_new != nullptr && w == 0 && v % hs == 0 && tid < 32) {
-    const int c8 = (tid & 15) * 8;
-    const uint16_t* src = (tid < 16 ? k_new : v_new) + (size_t)u * kHeadDim + c8;
-    uint16_t* dst = (tid < 16 ? k_tok : v_tok) + ((size_t)u * capacity + n_total - 1) * kHeadDim + c8;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-  }
-
   // the stream's query operand, loaded while the recall's loads are in flight
   StreamState sst;
   stream_init(sst, q, v, G);
@@ -117,7 +108,11 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   const int m = off[K];
   const int beff = budget < m ? budget : m;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
+  // The query sum first: its loads leave before the centroid rows', which
+  // complete in order after them (1.4 us less per launch than summing after
+  // the rows' loads are issued).
   float qb[8];
+  qbar8(q, v, G, li, qb);
   for (int j0 = 0; j0 < K; j0 += kRdGroups * kRdRowsInFlight) {
     float4 a[kRdRowsInFlight][2];
 #pragma unroll
@@ -130,7 +125,6 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
         a[t][0] = a[t][1] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    if (j0 == 0) qbar8(q, v, G, li, qb);  // the query sum while the first rows are in flight
 #pragma unroll
     for (int t = 0; t < kRdRowsInFlight; ++t) {
       const int j = j0 + grp + t * kRdGroups;
@@ -439,6 +433,16 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
     stream_rows(sst, rb, lds_addr(rowsrc), lds_addr(smem), nrows, G);
   }
   const int rank = finish_chunk<GT>(sst, reinterpret_cast<float*>(smem), &sh[7], partials, counters, out, v, w, W, G);
+
+  // The appended token's row into the token-order cache (this launch streamed
+  // it from k_new / v_new).  Done last: the copy's load would otherwise hold
+  // up the wave's first recall loads.
+  if (k_new != nullptr && w == 0 && v % hs == 0 && tid < 32) {
+    const int c8 = (tid & 15) * 8;
+    const uint16_t* src = (tid < 16 ? k_new : v_new) + (size_t)u * kHeadDim + c8;
+    uint16_t* dst = (tid < 16 ? k_tok : v_tok) + ((size_t)u * capacity + n_total - 1) * kHeadDim + c8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
 
   // The chunks that did not merge are done while the last one merges: they
   // bring the next call's centroids and offsets of this unit (the next layer,
