@@ -21,37 +21,48 @@ namespace ckv {
 // Floyd's sampling algorithm (Bentley and Floyd, CACM 1987) from SplitMix64
 // outputs (Steele, Lea and Flood, OOPSLA 2014), state seed + unit.  For
 // j = m - K .. m - 1 a draw r gives t = r mod (j + 1); t is inserted unless it
-// is already in the sample, in which case j is.  The draws are sequential, so
-// one workgroup per unit makes them.
+// is already in the sample, in which case j is.  One workgroup per unit.  The
+// generator's state after i + 1 steps is its initial state plus (i + 1) times
+// its increment, so the lanes compute every draw's t at once; only the
+// membership tests and inserts run in order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t splitmix64_next(uint64_t& x) {
-  x += 0x9E3779B97F4A7C15ull;
-  uint64_t z = x;
+constexpr uint64_t kSplitMixGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
 }
 
+// t of every draw of unit u into t_out[0, K)
+__device__ __forceinline__ void floyd_targets(uint64_t seed, int u, int m, int K, int* t_out) {
+  const uint64_t s0 = seed + (uint64_t)u;
+  for (int i = lane_id(); i < K; i += kWave) {
+    const uint64_t r = splitmix64_mix(s0 + (uint64_t)(i + 1) * kSplitMixGamma);
+    t_out[i] = (int)(r % (uint64_t)(m - K + i + 1));
+  }
+}
+
 // Membership of the indices drawn so far: a bitmap over [0, m) in LDS when it
-// fits (one lane then makes the draws, with no barrier between them), else the
-// list of draws scanned by all 64 lanes.
+// fits (one lane then makes the inserts, with no barrier between them), else
+// the list of draws scanned by all 64 lanes.
 constexpr int kDrawBitmapWords = 16384;  // 64 KiB of LDS: m up to 524288
 
 __global__ __launch_bounds__(64) void init_draw_bitmap_kernel(uint64_t seed, int m, int K,
                                                               int32_t* __restrict__ init_idx) {
   extern __shared__ uint32_t bitmap[];
+  __shared__ int tdraw[kMaxClusters];
   const int u = blockIdx.x;
   const int words = (m + 31) >> 5;
   for (int i = threadIdx.x; i < words; i += kWave) bitmap[i] = 0u;
+  floyd_targets(seed, u, m, K, tdraw);
   __syncthreads();
   if (threadIdx.x != 0) return;
-  uint64_t x = seed + (uint64_t)u;
   int32_t* out = init_idx + (size_t)u * K;
   for (int i = 0; i < K; ++i) {
-    const int j = m - K + i;
-    const int t = (int)(splitmix64_next(x) % (uint64_t)(j + 1));
+    const int t = tdraw[i];
     const bool taken = (bitmap[t >> 5] >> (t & 31)) & 1u;
-    const int pick = taken ? j : t;  // j itself is never taken yet: every earlier pick is below it
+    const int pick = taken ? m - K + i : t;  // m - K + i itself is never taken yet: every earlier pick is below it
     bitmap[pick >> 5] |= 1u << (pick & 31);
     out[i] = pick;
   }
@@ -59,16 +70,16 @@ __global__ __launch_bounds__(64) void init_draw_bitmap_kernel(uint64_t seed, int
 
 __global__ __launch_bounds__(64) void init_draw_kernel(uint64_t seed, int m, int K, int32_t* __restrict__ init_idx) {
   __shared__ int chosen[kMaxClusters];
+  __shared__ int tdraw[kMaxClusters];
   const int u = blockIdx.x;
   const int lane = lane_id();
-  uint64_t x = seed + (uint64_t)u;
+  floyd_targets(seed, u, m, K, tdraw);
+  __syncthreads();
   for (int i = 0; i < K; ++i) {
-    const int j = m - K + i;
-    const uint64_t r = splitmix64_next(x);  // the same draw in every lane
-    const int t = (int)(r % (uint64_t)(j + 1));
+    const int t = tdraw[i];
     bool hit = false;
     for (int c = lane; c < i; c += kWave) hit |= chosen[c] == t;
-    const int pick = __ballot(hit) ? j : t;
+    const int pick = __ballot(hit) ? m - K + i : t;
     if (lane == 0) chosen[i] = pick;
     __syncthreads();  // the insert is seen by every lane's next membership test
   }
