@@ -124,9 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": None, "fetch_kib": None, "write_kib": None},
+                      "sha256": "6de1c480912449792115ab8b20c2b054ef6e75d9fad96fbb8fa092b3449e9571",
+                      "fetch_kib": 47176.4, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": None, "fetch_kib": None, "write_kib": None},
+                      "sha256": "4222189810fd49ac38a4fce49011429ebc93b6cb140668ee404dcdcdef0b931e",
+                      "fetch_kib": 34287.2, "write_kib": 762.0},
 }
 
 
@@ -628,8 +630,11 @@ def run_stack(cfg, args) -> dict:
         full = full_attention_baseline(layers, qs, qlast, outs, units, G, r_now, dec_ms, cs if graphs else None,
                                        stream, dev)
         full["step_speedup"] = n_layers * full["decode_us"] * 1e-3 / ms_per_step
+    # counters taken on the default workload (the fused form with the next layer's
+    # centroids read at the end of each launch, which they include)
     traffic = (measured_traffic("recall_decode" if fused else "sparse_decode")
-               if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph else None)
+               if cfg.name == DEFAULT_WORKLOAD and n_layers == cfg.layers and not ph
+               and not (fused and args.no_prefetch) else None)
     copy_gbs = copy_bandwidth(dev)
 
     result = {
