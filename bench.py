@@ -820,10 +820,11 @@ def run_incremental(cfg, args) -> dict:
     }
 
 
-def run_cpu_baseline_incremental(cfg, seconds: float = 20.0) -> dict:
+def run_cpu_baseline_incremental(cfg, seconds: float = None) -> dict:
     """The oracle's incremental pass (the same 320 new keys per unit, 10% from 8
-    new components) on a bounded sample of units, each after its own oracle
-    prefill (untimed), extrapolated to the workload's units."""
+    new components) on every unit of the workload (seconds=None), each after its
+    own oracle prefill (untimed; about 2 s per unit), or on the units that fit in
+    `seconds`, extrapolated to the workload's units."""
     import numpy as np
 
     import synth
@@ -836,7 +837,7 @@ def run_cpu_baseline_incremental(cfg, seconds: float = 20.0) -> dict:
         threads = 1
     t_inc = 0.0
     n_units = 0
-    deadline = time.perf_counter() + seconds
+    deadline = time.perf_counter() + seconds if seconds is not None else float("inf")
     n_new = cfg.n_tokens + cfg.new_tokens
     while time.perf_counter() < deadline and n_units < cfg.units:
         u = n_units
@@ -853,7 +854,9 @@ def run_cpu_baseline_incremental(cfg, seconds: float = 20.0) -> dict:
         n_units += 1
     us = t_inc / n_units * cfg.units * 1e6
     return {"value": us, "unit": "us", "cores": int(threads), "kind": "oracle",
-            "sample": (f"the incremental pass of {n_units} units (each after its own untimed oracle prefill), "
+            "sample": (f"the incremental pass of every unit ({n_units}), each after its own untimed oracle prefill, "
+                       f"float64 NumPy: timed in full" if n_units == cfg.units else
+                       f"the incremental pass of {n_units} units (each after its own untimed oracle prefill), "
                        f"float64 NumPy, extrapolated to {cfg.units} units"),
             "seconds": t_inc}
 
@@ -901,7 +904,9 @@ def main() -> int:
     ap.add_argument("--split-reserve", type=int, default=0,
                     help="llama8b-incremental-b16 only: hold this many cluster slots empty at prefill and "
                          "time ckv_cluster_split after the incremental call")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=None,
+                    help="bound on the oracle's timed work (default: 20 s on the stacks; every unit of the "
+                         "one-layer and incremental workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 device copies of 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -938,7 +943,7 @@ def main() -> int:
         if cfg.new_tokens and cfg.layers == 1:
             result["cpu_baseline"] = run_cpu_baseline_incremental(cfg, seconds=args.cpu_seconds)
         else:
-            result["cpu_baseline"] = run_cpu_baseline(cfg, steps=3, seconds=args.cpu_seconds)
+            result["cpu_baseline"] = run_cpu_baseline(cfg, steps=3, seconds=args.cpu_seconds or 20.0)
     print(json.dumps(result), flush=True)
     return 0
 
