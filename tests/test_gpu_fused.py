@@ -144,6 +144,78 @@ def test_fused_random_shapes_end_to_end(case):
     assert compared >= 1
 
 
+def _fused_exact(L, st, q, k, v, budget, n_sink, nc, n_total, tag):
+    """Fused call on unit 0 against the oracle where ties decide the recall:
+    the token sets must be equal (the tie rules fix them), and the output too."""
+    G = q.shape[1]
+    sp, cn, out = _bufs(1, budget, 1, G)
+    L.select_decode(dev_bf16(q), budget, sp, cn, out)
+    sp2, cn2, _ = _bufs(1, budget, 1, G)
+    L.select(dev_bf16(q), budget, sp2, cn2)
+    torch.cuda.synchronize()
+    m = nc - n_sink
+    c = min(budget, m)
+    assert int(cn[0]) == c and torch.equal(sp[:, :c], sp2[:, :c]), "fused recall differs from ckv_select"
+    spn, cnn, og = sp.cpu().numpy(), cn.cpu().numpy(), out.cpu().numpy()
+    sel = pipeline.select_unit(q[0], st["cmean"], st["csize"], st["offsets"], st["k_clu_bits"], budget)
+    diff = compare_selection(L, 0, spn, cnn, st, sel, budget)
+    assert diff == 0, f"{tag}: recall differs by {diff} tokens where only ties decide"
+    check_decode(og[0], q[0], k[0], v[0], st, spn[0], cnn[0], sel, 0, n_sink, nc, n_total, tag=tag)
+
+
+def test_fused_degenerate_scores():
+    """q = 0: every cluster and cut-token score is 0, so the score range is
+    degenerate and both selections take their radix fallback; ties go to the
+    smaller cluster index and the smaller position (earlier token)."""
+    say("case: fused recall + decode with a zero query (all scores tie)")
+    n_sink, K, recent = 16, 40, 9
+    nc = n_sink + 3000
+    n_total = nc + recent
+    kb, vb, cen = synth.make_unit_inputs(81, 0, n_total, 24, capacity=n_total + 8)
+    init = synth.make_init_indices(82, 1, nc - n_sink, K)[0]
+    st = pipeline.prefill_unit(kb, nc, init, K, 2, n_sink=n_sink, v_bits=vb)
+    L = gpu_layer(kb[None], vb[None], 2, K, n_sink=n_sink, max_budget=3100)
+    load_state(L, [st], n_sink=n_sink)
+    L.set_counters(n_total, nc)
+    q = np.zeros((1, 2, D), np.uint16)
+    for budget in (1, 77, 1500, 2999, 3100):
+        _fused_exact(L, st, q, kb[None], vb[None], budget, n_sink, nc, n_total, tag=f"zero query, budget {budget}")
+
+
+def test_fused_crowded_crossing_bucket():
+    """100 clusters with one shared scoring centroid (so one shared score, in
+    the middle of the range): the bucket where the budget is crossed holds more
+    candidates than the exact in-bucket rank takes, and the selection falls
+    back to the radix select; ties among the 100 go to the smaller index."""
+    say("case: fused recall + decode with 100 equal cluster scores at the cut")
+    n_sink, K, recent, G = 16, 200, 3, 4
+    nc = n_sink + 8000
+    n_total = nc + recent
+    kb, vb, cen = synth.make_unit_inputs(83, 0, n_total, 96, capacity=n_total + 8)
+    init = synth.make_init_indices(84, 1, nc - n_sink, K)[0]
+    st = pipeline.prefill_unit(kb, nc, init, K, 2, n_sink=n_sink, v_bits=vb)
+    q = synth.make_queries(85, cen[None], G)
+    qbar = bf16.widen(q[0]).sum(axis=0)
+    mu = st["cmean"].astype(np.float32).astype(np.float64)  # the GPU holds f32 centroids
+    scores = mu @ qbar
+    group = np.argsort(scores)[50:150]              # 100 clusters from the middle of the order
+    common = mu[group].mean(axis=0).astype(np.float32).astype(np.float64)
+    mu[group] = common
+    st = dict(st, cmean=mu)
+    scores = np.where(st["csize"] > 0, mu @ qbar, -np.inf)
+    order = sorted(range(K), key=lambda j: (-scores[j], j))
+    pos = [order.index(j) for j in group]
+    first = min(pos)
+    before = int(sum(st["csize"][order[i]] for i in range(first)))
+    inside = int(sum(st["csize"][j] for j in group))
+    L = gpu_layer(kb[None], vb[None], G, K, n_sink=n_sink, max_budget=8000)
+    load_state(L, [st], n_sink=n_sink)
+    L.set_counters(n_total, nc)
+    for budget in (before + inside // 2, before + inside // 3 + 1, before + 1):
+        _fused_exact(L, st, q, kb[None], vb[None], budget, n_sink, nc, n_total,
+                     tag=f"crowded bucket, budget {budget}")
+
+
 def test_fused_glm4_layer_full_size():
     """One full GLM4-shaped layer (32 units, G = 16, K = 410, 300 recent rows,
     budget 2048): 8 chunks per set in the fused launch."""
