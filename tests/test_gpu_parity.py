@@ -664,9 +664,17 @@ def test_edge_zero_and_duplicate_keys(K, T):
         sel_pos = torch.zeros((1, max(budget, 1)), dtype=torch.int32, device="cuda")
         cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
         L.select(dev_bf16(q), budget, sel_pos, cnt)
+        # the fused launch recalls the same positions and attends to them
+        sp2, cn2 = torch.full_like(sel_pos, -1), torch.zeros_like(cnt)
+        out2 = torch.zeros((1, 1, D), dtype=torch.float32, device="cuda")
+        L.select_decode(dev_bf16(q), budget, sp2, cn2, out2)
         torch.cuda.synchronize()
+        c = int(cnt[0])
+        assert torch.equal(cn2, cnt) and torch.equal(sp2[:, :c], sel_pos[:, :c]), "fused recall differs"
         sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
-        compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
+        diff = compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
+        check_decode(out2.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff, 16, n, n,
+                     tag=f"edge fused, budget {budget}")
 
 
 @pytest.mark.parametrize("n_sink", [0, 16])
@@ -691,14 +699,16 @@ def test_edge_every_key_its_own_cluster(n_sink):
         out = torch.zeros((1, G, D), dtype=torch.float32, device="cuda")
         L.select(dev_bf16(q), budget, sel_pos, cnt)
         L.sparse_decode(dev_bf16(q), sel_pos, cnt, budget, out)
+        sp2, cn2, out2 = torch.full_like(sel_pos, -1), torch.zeros_like(cnt), torch.zeros_like(out)
+        L.select_decode(dev_bf16(q), budget, sp2, cn2, out2)
         torch.cuda.synchronize()
+        c = int(cnt[0])
+        assert torch.equal(cn2, cnt) and torch.equal(sp2[:, :c], sel_pos[:, :c]), "fused recall differs"
         sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
-        if compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget) == 0:
-            ref = pipeline.decode_unit(q[0], kb, vb, ora["k_clu_bits"], ora["v_clu_bits"], sel["positions"],
-                                       n_sink, n, n)
-            err = np.abs(out.cpu().numpy()[0] - ref).max()
-            say(f"  budget {budget}: decode max abs err {err:.3g}")
-            assert err <= DECODE_ATOL
+        diff = compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
+        for o, form in ((out, "two launches"), (out2, "fused")):
+            check_decode(o.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff, n_sink, n, n,
+                         tag=f"K=m {form}, budget {budget}")
 
 
 def test_determinism():
