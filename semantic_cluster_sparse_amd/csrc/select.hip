@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t tkey[kCutLds];
   __shared__ __attribute__((aligned(16))) float tsc[kCutLds];
   __shared__ __attribute__((aligned(16))) SelScratch<kSelThreads> ws;
-  __shared__ int sh_cut, sh_need, sh_last;
+  __shared__ int sh_last;
 
   // selection v of physical unit u: hs = 1 (one recall per KV head, q_bar over
   // its G query heads) or hs = G (one recall per query head, G passed as 1)
