@@ -74,12 +74,14 @@ def test_fused_teacher_forced(G, n_sink, recent, budget, K, units):
     c = min(budget, m)
     assert torch.equal(sp[:, :c], sp2[:, :c]), "fused recall differs from ckv_select"
     spn, cnn, og = sp.cpu().numpy(), cn.cpu().numpy(), out.cpu().numpy()
+    compared = 0
     for u in checked:
         st = states[u]
         sel = pipeline.select_unit(q[u], st["cmean"], st["csize"], st["offsets"], st["k_clu_bits"], budget)
         diff = compare_selection(L, u, spn, cnn, st, sel, budget)
-        check_decode(og[u], q[u], k[u], v[u], st, spn[u], cnn[u], sel, diff, n_sink, nc, n_total,
-                     tag=f"unit {u}: fused")
+        compared += check_decode(og[u], q[u], k[u], v[u], st, spn[u], cnn[u], sel, diff, n_sink, nc, n_total,
+                                 tag=f"unit {u}: fused")
+    assert compared >= 1, "no checked unit's decode was compared"
 
 
 def _random_case(rng):
@@ -160,7 +162,7 @@ def _fused_exact(L, st, q, k, v, budget, n_sink, nc, n_total, tag):
     sel = pipeline.select_unit(q[0], st["cmean"], st["csize"], st["offsets"], st["k_clu_bits"], budget)
     diff = compare_selection(L, 0, spn, cnn, st, sel, budget)
     assert diff == 0, f"{tag}: recall differs by {diff} tokens where only ties decide"
-    check_decode(og[0], q[0], k[0], v[0], st, spn[0], cnn[0], sel, 0, n_sink, nc, n_total, tag=tag)
+    assert check_decode(og[0], q[0], k[0], v[0], st, spn[0], cnn[0], sel, 0, n_sink, nc, n_total, tag=tag) == 1
 
 
 def test_fused_degenerate_scores():

@@ -660,6 +660,7 @@ def test_edge_zero_and_duplicate_keys(K, T):
     if K > 3:
         assert np.count_nonzero(ora["csize"] == 0) >= 1
     q = synth.make_queries(92, cen[None], 1)
+    compared = 0
     for budget in (0, 50, 723, 800):
         sel_pos = torch.zeros((1, max(budget, 1)), dtype=torch.int32, device="cuda")
         cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
@@ -673,8 +674,9 @@ def test_edge_zero_and_duplicate_keys(K, T):
         assert torch.equal(cn2, cnt) and torch.equal(sp2[:, :c], sel_pos[:, :c]), "fused recall differs"
         sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
         diff = compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
-        check_decode(out2.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff, 16, n, n,
-                     tag=f"edge fused, budget {budget}")
+        compared += check_decode(out2.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff,
+                                 16, n, n, tag=f"edge fused, budget {budget}")
+    assert compared >= 1
 
 
 @pytest.mark.parametrize("n_sink", [0, 16])
@@ -693,6 +695,7 @@ def test_edge_every_key_its_own_cluster(n_sink):
     x = bf16.widen(kb[n_sink:n])
     assert check_state(L, 0, ora, x, ora["history"][-2][1], n_sink=n_sink, tag="K=m") == 0
     q = synth.make_queries(142, cen[None], G)
+    compared = 0
     for budget in (1, 37, m):
         sel_pos = torch.zeros((1, budget), dtype=torch.int32, device="cuda")
         cnt = torch.zeros((1,), dtype=torch.int32, device="cuda")
@@ -707,8 +710,9 @@ def test_edge_every_key_its_own_cluster(n_sink):
         sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], budget)
         diff = compare_selection(L, 0, sel_pos.cpu().numpy(), cnt.cpu().numpy(), ora, sel, budget)
         for o, form in ((out, "two launches"), (out2, "fused")):
-            check_decode(o.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff, n_sink, n, n,
-                         tag=f"K=m {form}, budget {budget}")
+            compared += check_decode(o.cpu().numpy()[0], q[0], kb, vb, ora, sel_pos.cpu().numpy()[0], c, sel, diff,
+                                     n_sink, n, n, tag=f"K=m {form}, budget {budget}")
+    assert compared >= 2
 
 
 def test_determinism():

@@ -64,8 +64,8 @@ def test_seeded_prefill_single_head_end_to_end():
     sel = pipeline.select_unit(q[0], ora["cmean"], ora["csize"], ora["offsets"], ora["k_clu_bits"], cfg.budget)
     spn, cnn = sp.cpu().numpy(), cn.cpu().numpy()
     diff = compare_selection(L, 0, spn, cnn, ora, sel, cfg.budget)
-    check_decode(out.cpu().numpy()[0], q[0], k[0], v[0], ora, spn[0], cnn[0], sel, diff, 16, cfg.n_tokens,
-                 cfg.n_tokens, tag="unit 0:")
+    assert check_decode(out.cpu().numpy()[0], q[0], k[0], v[0], ora, spn[0], cnn[0], sel, diff, 16, cfg.n_tokens,
+                        cfg.n_tokens, tag="unit 0:") == 1
 
 
 def test_seeded_prefill_llama_layer():

@@ -44,11 +44,13 @@ def _compare(L, q_bits, budget, G, states, k, v, nc, n_total, n_sink, tag):
         f"outputs equal {torch.equal(a[2], b[2])}")
     assert torch.equal(a[1], b[1]) and torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
     spn, cnn, og = b[0].cpu().numpy(), b[1].cpu().numpy(), b[2].cpu().numpy()
+    compared = 0
     for u, st in states.items():
         sel = pipeline.select_unit(q_bits[u], st["cmean"], st["csize"], st["offsets"], st["k_clu_bits"], budget)
         diff = compare_selection(L, u, spn, cnn, st, sel, budget)
-        check_decode(og[u], q_bits[u], k[u], v[u], st, spn[u], cnn[u], sel, diff, n_sink, nc, n_total,
-                     tag=f"{tag} unit {u}:")
+        compared += check_decode(og[u], q_bits[u], k[u], v[u], st, spn[u], cnn[u], sel, diff, n_sink, nc, n_total,
+                                 tag=f"{tag} unit {u}:")
+    assert compared >= 1
 
 
 def _teacher_forced(units, K, m, G, recent, seed):
