@@ -152,11 +152,10 @@ int incremental_impl(const ckv_layer* L, void* ws, size_t ws_bytes, hipStream_t 
   int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
   double* invn = (double*)((char*)ws + w.off_invn);
 
+  // the new keys' labels and inverse norms
   hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
-                                    clu_stride, m_old, units, s);
+                                    clu_stride, m_old, units, s, invn);
   if (e != hipSuccess) return hip_status(e, "assign");
-  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, m_old, m_new, invn, clu_stride, units, s);
-  if (e != hipSuccess) return hip_status(e, "norms");
   e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
   if (e != hipSuccess) return hip_status(e, "hist");
   e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, offsets_out, units, s);
@@ -225,10 +224,10 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
 
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
   if (e != hipSuccess) return hip_status(e, "init");
-  e = ckv::launch_inv_norm(L->k_tok, L->capacity, L->n_sink, 0, m, invn, clu_stride, units, s);
-  if (e != hipSuccess) return hip_status(e, "norms");
   for (int it = 0; it < iters; ++it) {
-    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s);
+    // the first round's assignment also writes the keys' inverse norms
+    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s,
+                           it == 0 ? invn : nullptr);
     if (e != hipSuccess) return hip_status(e, "assign");
     e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
     if (e != hipSuccess) return hip_status(e, "hist");

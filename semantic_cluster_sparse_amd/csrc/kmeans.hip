@@ -133,6 +133,20 @@ __global__ __launch_bounds__(256) void init_dirs_kernel(const uint16_t* __restri
   *reinterpret_cast<uint32_t*>(cdir + ((size_t)u * K + j) * kHeadDim + 2 * lane) = out;
 }
 
+// Sum of squares, in f64 and in element order, of the 8 bf16 values of one
+// 16-byte chunk of a key row: the per-chunk part of every key norm computed
+// here.  A row's 16 chunk sums are then added by a butterfly over the chunk
+// index (xor 1, 2, 4, 8), so wherever the norm is computed it is the same f64.
+__device__ __forceinline__ double chunk_sq_sum(uint4 w) {
+  double x[8];
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  double n2 = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
+  return n2;
+}
+
 // ---------------------------------------------------------------------------
 // Assignment: scores = X C^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16), fp32
 // accumulate, argmax fused in registers.  A workgroup owns 256 keys (4 waves x
@@ -286,10 +300,15 @@ constexpr int kAsResMt = 2;                  // 16-key M-tiles per wave tile (re
 constexpr int kAsResTile = 16 * kAsResMt;     // keys per wave tile
 constexpr int kAsResMaxK = 512;
 
+// NORMS: the kernel also writes 1/|x| (f64) of every key it assigns into
+// invn[u, first + i], from the key registers it already holds (the chunk sums
+// and butterfly of inv_norm_kernel, so the values are the same bits); the
+// prefill's first round uses it instead of a separate pass over the keys.
+template <bool NORMS>
 __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
     const uint16_t* __restrict__ k_tok, int capacity, int row0, int count,
     const uint16_t* __restrict__ cdir, int K, int32_t* __restrict__ assign, int clu_stride, int first,
-    int wg_per_unit, int tiles_per_wg) {
+    int wg_per_unit, int tiles_per_wg, double* __restrict__ invn) {
   extern __shared__ __attribute__((aligned(16))) uint16_t csr[];
   const int u = blockIdx.x / wg_per_unit;
   const int part = blockIdx.x % wg_per_unit;
@@ -436,6 +455,25 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
       }
       const int r = t * kAsResTile + mt * 16 + r16;
       if (kg == 0 && r < count) out[r] = bi;
+    }
+    if constexpr (NORMS) {
+      // lane (r16, kg) holds chunks c = 4 s + kg of key r16: the butterfly's
+      // xor 1 and 2 on c are lanes 16 and 32 apart, xor 4 and 8 are s ^ 1, s ^ 2
+      double* inv_out = invn + (size_t)u * clu_stride + first;
+#pragma unroll
+      for (int mt = 0; mt < kAsResMt; ++mt) {
+        double v[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v[s] = chunk_sq_sum(__builtin_bit_cast(uint4, a[mt][s]));
+          v[s] += __shfl_xor(v[s], 16);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] += __shfl_xor(v[s], 32);
+        const double n2 = (v[0] + v[1]) + (v[2] + v[3]);
+        const int r = t * kAsResTile + mt * 16 + r16;
+        if (kg == 0 && r < count) inv_out[r] = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+      }
     }
   };
 
@@ -615,13 +653,7 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restric
 #pragma unroll
   for (int k = 0; k < kNormRows; ++k) {
     const int i = i0 + 16 * k;
-    double x[8];
-    x[0] = bf16_lo(w[k].x); x[1] = bf16_hi(w[k].x); x[2] = bf16_lo(w[k].y); x[3] = bf16_hi(w[k].y);
-    x[4] = bf16_lo(w[k].z); x[5] = bf16_hi(w[k].z); x[6] = bf16_lo(w[k].w); x[7] = bf16_hi(w[k].w);
-    double n2 = 0.0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) n2 += x[t] * x[t];
-    n2 = xor_sum16(n2);
+    const double n2 = xor_sum16(chunk_sq_sum(w[k]));
     if (i < count && li == 0) invn[(size_t)u * clu_stride + first + i] = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
   }
 }
@@ -1027,7 +1059,7 @@ hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int
 
 hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
-                         int first, int units, hipStream_t s) {
+                         int first, int units, hipStream_t s, double* invn) {
   if (count <= 0) return hipSuccess;
   if (K <= kAsResMaxK) {
     // about one 8-wave workgroup per CU, each on one unit's range of key tiles
@@ -1043,14 +1075,25 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
     static std::once_flag lds_once;
     static hipError_t lds_status = hipSuccess;
     std::call_once(lds_once, [] {
-      lds_status = hipFuncSetAttribute((const void*)assign_resident_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kAsResMaxK * kAsLds * sizeof(uint16_t)));
+      const int bytes = (int)(kAsResMaxK * kAsLds * sizeof(uint16_t));
+      lds_status = hipFuncSetAttribute((const void*)assign_resident_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (lds_status == hipSuccess)
+        lds_status = hipFuncSetAttribute((const void*)assign_resident_kernel<true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     });
     if (lds_status != hipSuccess) return lds_status;
-    hipLaunchKernelGGL(assign_resident_kernel, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds, s,
-                       k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw);
+    if (invn != nullptr)
+      hipLaunchKernelGGL(assign_resident_kernel<true>, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds,
+                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn);
+    else
+      hipLaunchKernelGGL(assign_resident_kernel<false>, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds,
+                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn);
     return hipGetLastError();
+  }
+  if (invn != nullptr) {  // the chunked kernel does not hold whole rows: a separate pass
+    const hipError_t e = launch_inv_norm(k_tok, capacity, row0 - first, first, count, invn, clu_stride, units, s);
+    if (e != hipSuccess) return e;
   }
   const int tiles = (count + kAsRows - 1) / kAsRows;
   hipLaunchKernelGGL(assign_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, k_tok,

@@ -26,9 +26,11 @@ hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int
                             hipStream_t s);
 
 // assign[u, first + i] = argmax_j k_tok[u, row0 + i] . cdir[u, j] for i < count.
+// With invn non-null also invn[u, first + i] = 1/|k_tok[u, row0 + i]| (f64),
+// the same values launch_inv_norm writes.
 hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
-                         int first, int units, hipStream_t s);
+                         int first, int units, hipStream_t s, double* invn = nullptr);
 
 // Per-tile histograms of assign[u, 0:count): hist[u, tile, K].
 hipError_t launch_hist(const int32_t* assign, int clu_stride, int count, int K,
