@@ -124,10 +124,10 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "6de1c480912449792115ab8b20c2b054ef6e75d9fad96fbb8fa092b3449e9571",
+                      "sha256": "9d8df3636dc3dacdaf6d7257aad18ac871aa04996afa16fd3db9a90754520e02",
                       "fetch_kib": 47176.4, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "4222189810fd49ac38a4fce49011429ebc93b6cb140668ee404dcdcdef0b931e",
+                      "sha256": "502181985b451b9b234b26cecce7fab07b8e867e848d5ee1ef9924102366e80f",
                       "fetch_kib": 34287.2, "write_kib": 762.0},
 }
 
