@@ -705,7 +705,8 @@ def run_stack(cfg, args) -> dict:
 
 def run_incremental(cfg, args) -> dict:
     """One layer: prefill, append cfg.new_tokens keys per unit, then time
-    ckv_cluster_incremental, ckv_select and ckv_sparse_decode (median over repetitions)."""
+    ckv_cluster_incremental, ckv_select and ckv_sparse_decode, and the fused
+    ckv_select_decode (median over repetitions)."""
     import torch
 
     from synth import device as dgen
@@ -738,13 +739,13 @@ def run_incremental(cfg, args) -> dict:
     log(f"[bench] {cfg.name}: {units} units, {n0} clustered + {n_new} new tokens; "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
-    t_inc, t_sel, t_dec, t_sel0, t_split, split_rows = [], [], [], [], [], []
+    t_inc, t_sel, t_dec, t_sel0, t_split, split_rows, t_fused = [], [], [], [], [], [], []
     for r in range(W + reps):
         L.prefill(n0, cfg.iters, init)
         L.k_tok[:, n0:cap].copy_(k_add)
         L.v_tok[:, n0:cap].copy_(v_add)
         L.set_counters(cap, n0)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         torch.cuda.synchronize()
         e[0].record(stream)
         L.select(q, budget, sel_pos, cnt)        # recall with the 320 tokens still recent
@@ -755,6 +756,8 @@ def run_incremental(cfg, args) -> dict:
         e[3].record(stream)
         L.sparse_decode(q, sel_pos, cnt, budget, out)
         e[4].record(stream)
+        L.select_decode(q, budget, sel_pos, cnt, out)  # the same recall and attention in one launch
+        e[5].record(stream)
         torch.cuda.synchronize()
         if R:
             tau, rows = split_plan(L, R)
@@ -771,6 +774,7 @@ def run_incremental(cfg, args) -> dict:
             t_inc.append(e[1].elapsed_time(e[2]))
             t_sel.append(e[2].elapsed_time(e[3]))
             t_dec.append(e[3].elapsed_time(e[4]))
+            t_fused.append(e[4].elapsed_time(e[5]))
 
     def med(x):
         return sorted(x)[len(x) // 2]
@@ -780,7 +784,8 @@ def run_incremental(cfg, args) -> dict:
     ibytes = incremental_bytes(units, cfg.n_clusters, cfg.m, n_new)
     achieved = ibytes / (inc_ms * 1e-3) / 1e9
     log(f"[bench] ckv_cluster_incremental {inc_ms * 1e3:.1f} us, {achieved:.0f} GB/s algorithmic; "
-        f"select {med(t_sel) * 1e3:.1f} us; decode {med(t_dec) * 1e3:.1f} us")
+        f"select {med(t_sel) * 1e3:.1f} us; decode {med(t_dec) * 1e3:.1f} us; fused recall + decode "
+        f"{med(t_fused) * 1e3:.1f} us")
     extra = {}
     if R:
         sp_ms = med(t_split)
@@ -816,6 +821,7 @@ def run_incremental(cfg, args) -> dict:
         "select_us": med(t_sel) * 1e3,
         "select_before_incremental_us": med(t_sel0) * 1e3,
         "sparse_decode_us": med(t_dec) * 1e3,
+        "select_decode_us": med(t_fused) * 1e3,
         **extra,
     }
 
