@@ -124,11 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "9d8df3636dc3dacdaf6d7257aad18ac871aa04996afa16fd3db9a90754520e02",
-                      "fetch_kib": 47176.4, "write_kib": 1274.4},
+                      "sha256": "82f1da9d406bc88868b006f05f7bdf1d2ef44f40818689ccad6f7b6a00d9df9c",
+                      "fetch_kib": 47176.3, "write_kib": 1274.3},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "502181985b451b9b234b26cecce7fab07b8e867e848d5ee1ef9924102366e80f",
-                      "fetch_kib": 34287.2, "write_kib": 762.0},
+                      "sha256": "1ee911bcd2c9dc4b9f3b6611d1ce56fafc1fdecf52801385a751f1cf79e4cb77",
+                      "fetch_kib": 34286.8, "write_kib": 762.0},
 }
 
 

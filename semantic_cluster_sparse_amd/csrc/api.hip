@@ -35,13 +35,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t counters;  // [2 units] u32 arrival counters: decode, then select; zero between calls
-  size_t hist;      // prefill / incremental: [units, tiles, K] int32
+  size_t aux;       // prefill: [units, K] int32 drawn indices; split: [units, 2K + 1] int32 pair plan
   size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
   size_t scores;    // select: [units, K] f32
   size_t cut;       // select: [units, clu_cap] u32 keys of the cut cluster
   size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
   size_t total;
-  size_t off_hist, off_invn, off_scores, off_cut, off_partials;
+  size_t off_aux, off_invn, off_scores, off_cut, off_partials;
   size_t off_rd_cut;  // fused recall + decode: cut scores after the partials
 };
 
@@ -57,25 +57,24 @@ Layout layout_of(const ckv_layer* L, bool per_head = false) {
   const size_t units = (size_t)L->batch * L->n_kv_heads;
   const size_t sets = units * (per_head ? (size_t)L->group : 1);
   const size_t clu_cap = (size_t)(L->capacity - L->n_sink);
-  const size_t tiles = (clu_cap + ckv::kSortTile - 1) / ckv::kSortTile;
   Layout w;
   // Arrival counters of both recall modes (decode at [0, sets), recall at
   // [sets, 2 sets)), sized for the per-query-head count whatever the mode, so
   // that the bodies below never overlap the counters of either mode when calls
   // of both modes share one workspace.
   w.counters = align256(units * (size_t)L->group * 2 * sizeof(uint32_t));
-  w.hist = align256(units * tiles * L->n_clusters * sizeof(int32_t));
+  w.aux = align256(units * (2 * (size_t)L->n_clusters + 1) * sizeof(int32_t));
   w.invn = align256(units * clu_cap * sizeof(double));
   w.scores = align256(sets * L->n_clusters * sizeof(float));
   w.cut = align256(sets * clu_cap * sizeof(uint32_t));
   w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
-  w.off_hist = w.counters;
-  w.off_invn = w.counters + w.hist;
+  w.off_aux = w.counters;
+  w.off_invn = w.counters + w.aux;
   w.off_scores = w.counters;
   w.off_cut = w.counters + w.scores;
   w.off_partials = w.counters;
   w.off_rd_cut = w.counters + w.partials;
-  size_t body = w.hist + w.invn;
+  size_t body = w.aux + w.invn;
   if (w.scores + w.cut > body) body = w.scores + w.cut;
   if (w.partials + w.cut > body) body = w.partials + w.cut;
   w.total = w.counters + body;
@@ -147,19 +146,15 @@ int incremental_impl(const ckv_layer* L, void* ws, size_t ws_bytes, hipStream_t 
   const int m_old = L->n_clustered - L->n_sink;
   const int m_new = L->n_total - L->n_clustered;
   const int m = m_old + m_new;
-  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
   const Layout w = layout_of(L);
-  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
   double* invn = (double*)((char*)ws + w.off_invn);
 
   // the new keys' labels and inverse norms
   hipError_t e = ckv::launch_assign(L->k_tok, L->capacity, L->n_clustered, m_new, L->cdir, K, L->assign,
                                     clu_stride, m_old, units, s, invn);
   if (e != hipSuccess) return hip_status(e, "assign");
-  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
-  if (e != hipSuccess) return hip_status(e, "hist");
-  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, offsets_out, units, s);
-  if (e != hipSuccess) return hip_status(e, "scatter");
+  e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, offsets_out, units, s);
+  if (e != hipSuccess) return hip_status(e, "index");
   e = ckv::launch_update(ckv::kUpdIncr, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride,
                          offsets_out, K, invn, L->csum, L->msum, cmean_out, L->csize, L->cdir, L->k_clu_alt,
                          L->v_clu_alt, units, s);
@@ -217,9 +212,7 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
   const int units = L->batch * L->n_kv_heads;
   const int K = L->n_clusters;
   const int clu_stride = L->capacity - L->n_sink;
-  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
   const Layout w = layout_of(L);
-  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
   double* invn = (double*)((char*)ws + w.off_invn);
 
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
@@ -229,10 +222,8 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
     e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s,
                            it == 0 ? invn : nullptr);
     if (e != hipSuccess) return hip_status(e, "assign");
-    e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
-    if (e != hipSuccess) return hip_status(e, "hist");
-    e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
-    if (e != hipSuccess) return hip_status(e, "scatter");
+    e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
+    if (e != hipSuccess) return hip_status(e, "index");
     const int mode = (it == iters - 1) ? ckv::kUpdFinal : ckv::kUpdIter;
     e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K,
                            invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s);
@@ -264,9 +255,9 @@ int ckv_cluster_prefill(ckv_layer* L, int32_t n, int32_t iters, uint64_t seed, v
                         void* stream) {
   int rc = prefill_check(L, n, iters, ws, ws_bytes);
   if (rc) return rc;
-  // the drawn indices live in the histogram region until the first round's histogram overwrites them
+  // the drawn indices live in the auxiliary region, read once by the centre initialisation
   const Layout w = layout_of(L);
-  int32_t* idx = (int32_t*)((char*)ws + w.off_hist);
+  int32_t* idx = (int32_t*)((char*)ws + w.off_aux);
   const hipStream_t s = (hipStream_t)stream;
   const hipError_t e = ckv::launch_init_draw(seed, n - L->n_sink, L->n_clusters, idx, L->batch * L->n_kv_heads, s);
   if (e != hipSuccess) return hip_status(e, "init draw");
@@ -390,22 +381,17 @@ int ckv_cluster_split(ckv_layer* L, double threshold, void* ws, size_t ws_bytes,
   const int units = L->batch * L->n_kv_heads;
   const int K = L->n_clusters;
   const int clu_stride = L->capacity - L->n_sink;
-  const int tiles = (m + ckv::kSortTile - 1) / ckv::kSortTile;
   const Layout w = layout_of(L);
-  int32_t* hist = (int32_t*)((char*)ws + w.off_hist);
 
-  // The pair plan, units x (2K + 1) int32, sits at the start of the histogram
-  // and norm regions (at least 12 K bytes per unit between them); the
-  // histogram kernel below overwrites it only after the split has used it.
-  int32_t* plan = hist;
+  // The pair plan, units x (2K + 1) int32, fills the auxiliary region, which
+  // the rebuild below does not use.
+  int32_t* plan = (int32_t*)((char*)ws + w.off_aux);
   hipError_t e = ckv::launch_split(L->k_clu, L->n_sink, L->perm, clu_stride, L->offsets, K, L->csum,
                                    L->csize, L->cdir, threshold, plan, L->assign, units, s);
   if (e != hipSuccess) return hip_status(e, "split");
   // one pass over the keys follows: the update takes each key's norm from the row itself
-  e = ckv::launch_hist(L->assign, clu_stride, m, K, hist, tiles, units, s);
-  if (e != hipSuccess) return hip_status(e, "hist");
-  e = ckv::launch_scatter(L->assign, clu_stride, m, K, hist, tiles, L->n_sink, L->perm, L->offsets, units, s);
-  if (e != hipSuccess) return hip_status(e, "scatter");
+  e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
+  if (e != hipSuccess) return hip_status(e, "index");
   e = ckv::launch_update(ckv::kUpdFinal, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride,
                          L->offsets, K, nullptr, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu,
                          units, s);

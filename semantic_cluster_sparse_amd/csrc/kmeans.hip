@@ -1,5 +1,5 @@
 // Cosine K-means kernels: initial directions, MFMA assignment with a fused
-// row argmax, per-tile histograms, stable counting-sort scatter, and the
+// row argmax, a one-launch stable counting sort by label, and the
 // per-cluster segmented reduction that updates the centroid state and writes
 // the cluster-contiguous copy of the K/V rows.
 //
@@ -492,37 +492,6 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Counting sort by cluster label, stable in token order.
-// hist: per (unit, tile of kSortTile tokens) label counts.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ assign,
-                                                   int clu_stride, int count, int K,
-                                                   int32_t* __restrict__ hist, int tiles) {
-  __shared__ int h[kMaxClusters];
-  const int u = blockIdx.x / tiles;
-  const int t = blockIdx.x % tiles;
-  for (int c = threadIdx.x; c < K; c += blockDim.x) h[c] = 0;
-  __syncthreads();
-  const int lo = t * kSortTile, hi = min(count, lo + kSortTile);
-  const int32_t* a = assign + (size_t)u * clu_stride;
-  constexpr int kPer = kSortTile / 256;  // labels per thread, all loads in flight at once
-  int lab[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = lo + threadIdx.x + k * 256;
-    lab[k] = i < hi ? a[i] : 0;
-  }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    if (lo + (int)threadIdx.x + k * 256 >= hi) continue;
-    const int c = lab[k] < 0 ? 0 : (lab[k] >= K ? K - 1 : lab[k]);
-    atomicAdd(&h[c], 1);
-  }
-  __syncthreads();
-  int32_t* out = hist + ((size_t)u * tiles + t) * K;
-  for (int c = threadIdx.x; c < K; c += blockDim.x) out[c] = h[c];
-}
-
 // Lanes of the wave holding the same label as this lane (among `valid` lanes).
 __device__ __forceinline__ unsigned long long match_label(int c, bool valid, int nbits) {
   unsigned long long peers = __ballot(valid);
@@ -534,96 +503,187 @@ __device__ __forceinline__ unsigned long long match_label(int c, bool valid, int
   return peers;
 }
 
-// scatter: each workgroup places the tokens of one tile.  Start of cluster c
-// for this tile = offsets[c] + (tokens of c in earlier tiles); inside the tile
-// each wave owns 512 consecutive tokens, and inside a wave batches of 64 are
-// placed in lane order via the peers mask.  Writes offsets from tile 0.
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ assign,
-                                                      int clu_stride, int count, int K,
-                                                      const int32_t* __restrict__ hist, int tiles,
-                                                      int n_sink, int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ offsets) {
-  __shared__ int base[kMaxClusters];
-  __shared__ int hw[4][kMaxClusters];
-  __shared__ int scan_scratch[8];
-  const int u = blockIdx.x / tiles;
-  const int t = blockIdx.x % tiles;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int32_t* hu = hist + (size_t)u * tiles * K;
+// ---------------------------------------------------------------------------
+// Index build in one launch: the same stable counting sort by label (perm in
+// cluster order, token order inside a cluster; offsets the exclusive scan of
+// the cluster sizes), with the permutation written in whole lines.  A
+// workgroup owns one (unit, range of clusters [c_lo, c_hi)); its 16 waves
+// each own a contiguous segment of the unit's tokens.
+//  1. Every wave walks its segment: a ballot counts its tokens below the
+//     range, and LDS atomics count its in-range tokens per cluster (both
+//     order-free).
+//  2. The waves' below-counts give the range's first position; a scan over
+//     the waves gives each wave's first position inside every cluster, and a
+//     scan over the range's clusters their starts (written to offsets).
+//  3. Every wave walks its segment again.  Per group of 8 batches of 64 it
+//     compacts its in-range tokens, in token order, into an LDS list, then
+//     places the list 64 at a time: rank among equal labels in lane order
+//     plus the wave's running position of that cluster.  Token order inside
+//     each cluster follows, as the sort is stable.
+// Only in-range tokens reach the peer search, so the work per token that is
+// repeated by every range's workgroup is a load, a ballot and a compare.
+// The range's positions are staged in LDS and copied to perm contiguously; a
+// range larger than the staging area writes its positions directly.
+// ---------------------------------------------------------------------------
+constexpr int kIdxThreads = 1024;
+constexpr int kIdxWaves = kIdxThreads / kWave;
+constexpr int kIdxPer = 32;                     // labels per lane loaded together
+constexpr int kIdxFlush = 8;                    // batches compacted before placement
+constexpr int kIdxBuf = kIdxFlush * kWave;      // compacted entries per wave
+constexpr int kIdxLdsMax = 160 * 1024;          // LDS of one CU
+constexpr int kIdxLabelBits = 10;               // range-relative label < kMaxClusters
 
-  int running = 0;
-  for (int c0 = 0; c0 < K; c0 += blockDim.x) {
-    const int c = c0 + threadIdx.x;
-    int total = 0, before = 0;
-    if (c < K) {
-      for (int tt0 = 0; tt0 < tiles; tt0 += 8) {  // 8 tiles' counts in flight at once
-        int v[8];
+static_assert(kMaxClusters <= (1 << kIdxLabelBits), "label field of a compacted entry");
+static_assert(kMaxClusters <= kIdxThreads, "one thread per cluster of a range");
+
+int index_ranges(int units, int K) {
+  int p = (256 + units - 1) / units;  // about one workgroup per CU
+  if (p > 32) p = 32;
+  if (p > K) p = K;
+  return p < 1 ? 1 : p;
+}
+
+int index_fixed_ints(int K, int ranges) {
+  const int R = (K + ranges - 1) / ranges;
+  return kIdxWaves * R + kIdxWaves * kIdxBuf + kIdxWaves + kIdxWaves + 1;
+}
+
+// staging room: twice a range's mean size, within what LDS leaves
+int index_stage_ints(int K, int ranges, int count) {
+  const int cap = kIdxLdsMax / (int)sizeof(int) - index_fixed_ints(K, ranges);
+  const long per = ((long)count + ranges - 1) / ranges;
+  long want = ((2 * per + 255) / 256) * 256;
+  if (want < 1024) want = 1024;
+  return (int)(want < cap ? want : cap);
+}
+
+__global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __restrict__ assign, int clu_stride,
+                                                            int count, int K, int ranges, int stage_cap,
+                                                            int xcd_map, int n_sink,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ offsets) {
+  extern __shared__ int ilds[];
+  const int R = (K + ranges - 1) / ranges;
+  int* cnt = ilds;                       // [waves][R] per-wave counts, then first positions
+  int* buf = cnt + kIdxWaves * R;        // [waves][kIdxBuf] compacted (offset, label) entries
+  int* below = buf + kIdxWaves * kIdxBuf;  // [waves] tokens below the range
+  int* scr = below + kIdxWaves;          // [waves + 1] scan scratch
+  int* stage = scr + kIdxWaves + 1;      // [stage_cap] the range's positions
+  // Workgroups are dealt to the 8 XCDs round-robin; with xcd_map (units a
+  // multiple of 8) all ranges of a unit share one XCD, so its labels are
+  // fetched into that XCD's L2 once.
+  const int b = blockIdx.x;
+  const int u = xcd_map ? (b & 7) + 8 * ((b >> 3) / ranges) : b / ranges;
+  const int p = xcd_map ? (b >> 3) % ranges : b % ranges;
+  const int c_lo = (int)((long)K * p / ranges);
+  const int c_hi = (int)((long)K * (p + 1) / ranges);
+  const int nr = c_hi - c_lo;  // 1 <= nr <= R
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  for (int e = tid; e < kIdxWaves * R; e += kIdxThreads) cnt[e] = 0;
+  __syncthreads();
+
+  int rbits = 0;
+  while ((1 << rbits) < nr) ++rbits;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int32_t* a = assign + (size_t)u * clu_stride;
+  const int seg = ((count + kIdxWaves - 1) / kIdxWaves + kWave - 1) & ~(kWave - 1);
+  const int s_lo = min(count, wave * seg), s_hi = min(count, s_lo + seg);
+  int* wc = cnt + wave * R;
+  // A segment of one chunk keeps its labels in registers for both walks.
+  const bool one_chunk = seg <= kIdxPer * kWave;  // uniform over the workgroup
+  int cv[kIdxPer];
+  auto load_chunk = [&](int b0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = tt0 + k < tiles ? hu[(size_t)(tt0 + k) * K + c] : 0;
+    for (int j = 0; j < kIdxPer; ++j) {
+      const int i = b0 + j * kWave + lane;
+      cv[j] = i < s_hi ? a[i] : 0;
+    }
+  };
+
+  // 1. the segment's tokens below the range, and its in-range counts
+  int nbelow = 0;
+  for (int b0 = s_lo; b0 < s_hi; b0 += kIdxPer * kWave) {
+    load_chunk(b0);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          total += v[k];
-          if (tt0 + k < t) before += v[k];
+    for (int j = 0; j < kIdxPer; ++j) {
+      if (b0 + j * kWave >= s_hi) break;  // uniform over the wave
+      const bool valid = b0 + j * kWave + lane < s_hi;
+      const int c = cv[j] < 0 ? 0 : (cv[j] >= K ? K - 1 : cv[j]);
+      nbelow += __popcll(__ballot(valid && c < c_lo));
+      if (valid && c >= c_lo && c < c_hi) atomicAdd(&wc[c - c_lo], 1);
+    }
+  }
+  if (lane == 0) below[wave] = nbelow;
+  __syncthreads();
+
+  // 2. first positions, relative to the range's first position r_lo
+  int r_lo = 0;
+  for (int w = 0; w < kIdxWaves; ++w) r_lo += below[w];
+  int size = 0;
+  if (tid < nr) {
+    for (int w = 0; w < kIdxWaves; ++w) {
+      const int v = cnt[w * R + tid];
+      cnt[w * R + tid] = size;
+      size += v;
+    }
+  }
+  int rtot;
+  const int cs = block_exclusive_scan(size, scr, &rtot);  // size is 0 beyond the range
+  if (tid < nr) {
+    for (int w = 0; w < kIdxWaves; ++w) cnt[w * R + tid] += cs;
+    offsets[(size_t)u * (K + 1) + c_lo + tid] = r_lo + cs;
+  }
+  if (p == ranges - 1 && tid == 0) offsets[(size_t)u * (K + 1) + K] = r_lo + rtot;
+  __syncthreads();
+  const bool staged = rtot <= stage_cap;  // uniform over the workgroup
+
+  // 3. placement in token order
+  int32_t* pu = perm + (size_t)u * clu_stride + r_lo;
+  int* wb = buf + wave * kIdxBuf;
+  for (int b0 = s_lo; b0 < s_hi; b0 += kIdxPer * kWave) {
+    if (!one_chunk) load_chunk(b0);
+#pragma unroll
+    for (int g = 0; g < kIdxPer; g += kIdxFlush) {
+      if (b0 + g * kWave >= s_hi) break;
+      int nb = 0;  // compacted entries (uniform over the wave)
+#pragma unroll
+      for (int jj = 0; jj < kIdxFlush; ++jj) {
+        const int j = g + jj;
+        if (b0 + j * kWave >= s_hi) break;
+        const int off = j * kWave + lane;
+        const bool valid = b0 + off < s_hi;
+        const int c = cv[j] < 0 ? 0 : (cv[j] >= K ? K - 1 : cv[j]);
+        const bool mine = valid && c >= c_lo && c < c_hi;
+        const unsigned long long m = __ballot(mine);
+        if (mine) wb[nb + __popcll(m & lt)] = (off << kIdxLabelBits) | (c - c_lo);
+        nb += __popcll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      for (int k0 = 0; k0 < nb; k0 += kWave) {
+        const bool has = k0 + lane < nb;
+        const int e = has ? wb[k0 + lane] : 0;
+        const int cl = e & ((1 << kIdxLabelBits) - 1);
+        const unsigned long long peers = match_label(cl, has, rbits);
+        int pos = 0;
+        if (has) pos = wc[cl] + __popcll(peers & lt);
+        // every lane has read its base before the leader moves it
+        if (has && (peers & lt) == 0ull) wc[cl] += __popcll(peers);
+        if (has) {
+          const int32_t tok = n_sink + b0 + (e >> kIdxLabelBits);
+          if (staged)
+            stage[pos] = tok;
+          else
+            pu[pos] = tok;
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // the list is read before the next group overwrites it
     }
-    int chunk_total;
-    const int excl = block_exclusive_scan(total, scan_scratch, &chunk_total);
-    if (c < K) {
-      base[c] = running + excl + before;
-      if (t == 0) offsets[(size_t)u * (K + 1) + c] = running + excl;
-    }
-    running += chunk_total;
   }
-  if (t == 0 && threadIdx.x == 0) offsets[(size_t)u * (K + 1) + K] = running;
-
-  // this wave's labels, all loads in flight at once (reused for the placement)
-  constexpr int kBatches = kSortTile / 4 / kWave;
-  const int32_t* a = assign + (size_t)u * clu_stride;
-  const int wlo = t * kSortTile + wave * (kSortTile / 4);
-  int lab[kBatches];
-#pragma unroll
-  for (int b = 0; b < kBatches; ++b) {
-    const int i = wlo + b * kWave + lane;
-    int c = i < count ? a[i] : 0;
-    lab[b] = c < 0 ? 0 : (c >= K ? K - 1 : c);
-  }
-  for (int e = threadIdx.x; e < 4 * kMaxClusters; e += blockDim.x) (&hw[0][0])[e] = 0;
+  if (!staged) return;
   __syncthreads();
-#pragma unroll
-  for (int b = 0; b < kBatches; ++b)
-    if (wlo + b * kWave + lane < count) atomicAdd(&hw[wave][lab[b]], 1);
-  __syncthreads();
-  for (int c = threadIdx.x; c < K; c += blockDim.x) {
-    int run = base[c];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int v = hw[w][c];
-      hw[w][c] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-
-  int nbits = 0;
-  while ((1 << nbits) < K) ++nbits;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t* pu = perm + (size_t)u * clu_stride;
-#pragma unroll
-  for (int b = 0; b < kBatches; ++b) {
-    const int i = wlo + b * kWave + lane;
-    const bool valid = i < count;
-    const int c = lab[b];
-    const unsigned long long peers = match_label(c, valid, nbits);
-    int bs = 0;
-    if (valid) bs = hw[wave][c];
-    if (valid) {
-      const int rank = __popcll(peers & lt);
-      pu[bs + rank] = n_sink + i;
-      if ((peers >> lane) == 1ull) hw[wave][c] = bs + __popcll(peers);
-    }
-  }
+  for (int j = tid; j < rtot; j += kIdxThreads) pu[j] = stage[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -1101,18 +1161,22 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
   return hipGetLastError();
 }
 
-hipError_t launch_hist(const int32_t* assign, int clu_stride, int count, int K,
-                       int32_t* hist, int tiles, int units, hipStream_t s) {
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, assign,
-                     clu_stride, count, K, hist, tiles);
-  return hipGetLastError();
-}
-
-hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int K,
-                          const int32_t* hist, int tiles, int n_sink, int32_t* perm,
-                          int32_t* offsets, int units, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)(units * tiles)), dim3(256), 0, s, assign,
-                     clu_stride, count, K, hist, tiles, n_sink, perm, offsets);
+hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K, int n_sink, int32_t* perm,
+                        int32_t* offsets, int units, hipStream_t s) {
+  if (K < 1 || K > kMaxClusters || count < 0) return hipErrorInvalidValue;
+  const int ranges = index_ranges(units, K);
+  const int stage = index_stage_ints(K, ranges, count);
+  const size_t lds = ((size_t)index_fixed_ints(K, ranges) + stage) * sizeof(int);
+  static std::once_flag lds_once;  // above the default dynamic LDS limit
+  static hipError_t lds_status = hipSuccess;
+  std::call_once(lds_once, [] {
+    lds_status =
+        hipFuncSetAttribute((const void*)index_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kIdxLdsMax);
+  });
+  if (lds_status != hipSuccess) return lds_status;
+  const int xcd_map = (units % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(index_kernel, dim3((unsigned)(units * ranges)), dim3(kIdxThreads), lds, s, assign, clu_stride,
+                     count, K, ranges, stage, xcd_map, n_sink, perm, offsets);
   return hipGetLastError();
 }
 

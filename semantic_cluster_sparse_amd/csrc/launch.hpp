@@ -8,7 +8,6 @@
 
 namespace ckv {
 
-constexpr int kSortTile = 4096;     // clustered tokens per histogram / scatter tile
 constexpr int kMaxClusters = 1024;  // K limit of the LDS-resident per-cluster arrays
 constexpr int kMaxGroup = 16;
 constexpr int kMaxChunks = 64;      // split-K chunks per unit in sparse decode
@@ -32,18 +31,14 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
                          int first, int units, hipStream_t s, double* invn = nullptr);
 
-// Per-tile histograms of assign[u, 0:count): hist[u, tile, K].
-hipError_t launch_hist(const int32_t* assign, int clu_stride, int count, int K,
-                       int32_t* hist, int tiles, int units, hipStream_t s);
-
-// Stable counting sort by label: perm[u, pos] = n_sink + i, offsets[u, 0..K].
-hipError_t launch_scatter(const int32_t* assign, int clu_stride, int count, int K,
-                          const int32_t* hist, int tiles, int n_sink, int32_t* perm,
-                          int32_t* offsets, int units, hipStream_t s);
-
 // 1/|x| (f64) of clustered tokens [first, first + count) into invn[u, first + i].
 hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int first, int count,
                            double* invn, int clu_stride, int units, hipStream_t s);
+
+// Stable counting sort by label in one launch: perm[u, pos] = n_sink + i in
+// cluster order (token order inside a cluster), offsets[u, 0..K].
+hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K, int n_sink, int32_t* perm,
+                        int32_t* offsets, int units, hipStream_t s);
 
 // Per-cluster segmented reduction over the members listed by perm/offsets.
 hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity,
