@@ -37,11 +37,12 @@ struct Layout {
   size_t counters;  // [2 units] u32 arrival counters: decode, then select; zero between calls
   size_t aux;       // prefill: [units, K] int32 drawn indices; split: [units, 2K + 1] int32 pair plan
   size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
+  size_t labs;      // prefill: [units, clu_cap] int32 labels of alternate Lloyd rounds
   size_t scores;    // select: [units, K] f32
   size_t cut;       // select: [units, clu_cap] u32 keys of the cut cluster
   size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
   size_t total;
-  size_t off_aux, off_invn, off_scores, off_cut, off_partials;
+  size_t off_aux, off_invn, off_labs, off_scores, off_cut, off_partials;
   size_t off_rd_cut;  // fused recall + decode: cut scores after the partials
 };
 
@@ -65,16 +66,18 @@ Layout layout_of(const ckv_layer* L, bool per_head = false) {
   w.counters = align256(units * (size_t)L->group * 2 * sizeof(uint32_t));
   w.aux = align256(units * (2 * (size_t)L->n_clusters + 1) * sizeof(int32_t));
   w.invn = align256(units * clu_cap * sizeof(double));
+  w.labs = align256(units * clu_cap * sizeof(int32_t));
   w.scores = align256(sets * L->n_clusters * sizeof(float));
   w.cut = align256(sets * clu_cap * sizeof(uint32_t));
   w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
   w.off_aux = w.counters;
   w.off_invn = w.counters + w.aux;
+  w.off_labs = w.off_invn + w.invn;
   w.off_scores = w.counters;
   w.off_cut = w.counters + w.scores;
   w.off_partials = w.counters;
   w.off_rd_cut = w.counters + w.partials;
-  size_t body = w.aux + w.invn;
+  size_t body = w.aux + w.invn + w.labs;
   if (w.scores + w.cut > body) body = w.scores + w.cut;
   if (w.partials + w.cut > body) body = w.partials + w.cut;
   w.total = w.counters + body;
@@ -217,16 +220,34 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
 
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
   if (e != hipSuccess) return hip_status(e, "init");
+  int32_t* labs = (int32_t*)((char*)ws + w.off_labs);
+  // Rounds before the last move the sums by the keys that changed cluster
+  // where the shape allows it; otherwise every round rebuilds from the index.
+  const bool by_changes = ckv::delta_supported(K, m, units);
   for (int it = 0; it < iters; ++it) {
+    const bool last = it == iters - 1;
+    // Labels alternate between the layer's assign and the workspace, so that
+    // a round by changes sees the previous round's; the last round writes
+    // assign.
+    int32_t* cur = (!by_changes || (iters - 1 - it) % 2 == 0) ? L->assign : labs;
+    int32_t* prev = (cur == L->assign) ? labs : L->assign;
     // the first round's assignment also writes the keys' inverse norms
-    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, L->assign, clu_stride, 0, units, s,
+    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, cur, clu_stride, 0, units, s,
                            it == 0 ? invn : nullptr);
     if (e != hipSuccess) return hip_status(e, "assign");
+    if (by_changes && !last) {
+      e = ckv::launch_delta(cur, it == 0 ? nullptr : prev, clu_stride, m, K, L->k_tok, L->capacity, L->n_sink, invn,
+                            L->csum, L->csize, L->cdir, units, s);
+      if (e != hipSuccess) return hip_status(e, "delta update");
+      continue;
+    }
+    // index, then the sums and directions from scratch; the last round also
+    // writes the means and the cluster-ordered rows
     e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
     if (e != hipSuccess) return hip_status(e, "index");
-    const int mode = (it == iters - 1) ? ckv::kUpdFinal : ckv::kUpdIter;
-    e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K,
-                           invn, L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s);
+    e = ckv::launch_update(last ? ckv::kUpdFinal : ckv::kUpdIter, L->k_tok, L->v_tok, L->capacity, L->n_sink,
+                           L->perm, clu_stride, L->offsets, K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir,
+                           L->k_clu, L->v_clu, units, s);
     if (e != hipSuccess) return hip_status(e, "update");
   }
   L->n_total = n;

@@ -687,6 +687,315 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Lloyd rounds before the last: the sums move with the keys that changed
+// cluster.  Round t's S_j = sum of x/|x| over the members of j is S_j of
+// round t-1 plus the keys that joined j minus those that left; n_j likewise.
+// S is held as exact integers, sum over members of rint(x_d / |x| * 2^F)
+// (F = min(50, 62 - bitlen(m)), so no sum leaves int64), so the update by
+// changes equals the sum from scratch bit for bit and does not depend on
+// the order of the additions.  The rounding to 2^-F (at most 2^-48 per
+// term at m < 2^15) is far below what f64 summation in any order already
+// leaves.  Directions are then c_j = bf16(S_j / |S_j|) from S_j in f64, as
+// in the update kernel; the last round rebuilds everything from the index.
+//
+// A workgroup of 1024 threads owns one (unit, slice of D dims, range of
+// clusters); with units >= 64 the range is all K clusters, so a key that
+// changed cluster is read once per slice and leaves and joins in the same
+// workgroup.  The range's additions sit in LDS as int64, one row of D + D/8
+// slots per cluster (dim d of the slice at slot (D/8)(d % 8) + d / 8; the
+// extra D/8 slots shift consecutive rows across the banks).  The 16 waves
+// walk their token segments, compact the keys whose label changed (and whose
+// old or new cluster is in the range), then add them D/8 lanes per key, 8
+// dims (one 16-byte load) per lane, the next keys' loads in flight while the
+// current ones are added.  A term is added as the bits of
+// fma(x, 2^F/|x|, 1.5 * 2^52), whose integer value is the rounded term plus
+// the bits of 1.5 * 2^52; the row's net member change times those bits is
+// taken off at the end.  Each workgroup then adds its touched rows into S
+// (slice 0 also moves n), and delta_dirs_kernel recomputes the directions
+// from the whole rows.  The first round starts from zero sums and adds every
+// key.
+// ---------------------------------------------------------------------------
+constexpr int kDelThreads = 1024;
+constexpr int kDelWaves = kDelThreads / kWave;
+constexpr int kDelPer = 12;                   // labels per lane loaded together
+constexpr int kDelBuf = 8 * kWave;            // listed keys per wave
+constexpr int kDelMaxRanges = 32;            // cluster ranges per unit
+
+
+// dims per slice: the widest whose LDS rows for all K clusters fit beside the lists
+int delta_dims(int K) { return K <= 440 ? 32 : 16; }
+
+// bits of a range-relative label in a listed key (with one value for "none")
+constexpr int delta_label_bits(int D) { return D == 32 ? 9 : 10; }
+
+__host__ __device__ inline int delta_seg(int count) { return ((count + kDelWaves - 1) / kDelWaves + kWave - 1) & ~(kWave - 1); }
+
+
+
+int delta_ranges(int units, int K) {
+  const int slices = kHeadDim / delta_dims(K);
+  int p = (256 + units * slices - 1) / (units * slices);  // about one workgroup per CU
+  if (p > kDelMaxRanges) p = kDelMaxRanges;
+  if (p > K) p = K;
+  return p < 1 ? 1 : p;
+}
+
+size_t delta_lds_bytes(int K, int ranges) {
+  const int D = delta_dims(K);
+  const size_t R = (size_t)((K + ranges - 1) / ranges);
+  return R * (D + D / 8) * sizeof(unsigned long long) + 2 * R * sizeof(int) +
+         (size_t)kDelWaves * kDelBuf * sizeof(uint32_t);
+}
+
+// whether the delta rounds take this shape: the LDS rows fit and a wave's
+// segment offsets fit their field of a listed key
+bool delta_supported(int K, int count, int units) {
+  if (K < 1 || K > kMaxClusters || count < 1) return false;
+  const int D = delta_dims(K);
+  if (delta_lds_bytes(K, delta_ranges(units, K)) > (size_t)kIdxLdsMax) return false;
+  return delta_seg(count) <= (1 << (32 - 2 * delta_label_bits(D)));
+}
+
+int delta_fbits(int m) {
+  int b = 0;
+  while (b < 31 && (1 << b) <= m) ++b;  // bitlen(m)
+  const int f = 62 - b;
+  return f < 50 ? f : 50;
+}
+
+template <int D, bool FIRST>
+__global__ __launch_bounds__(kDelThreads) void delta_kernel(
+    const int32_t* __restrict__ cur_lab, const int32_t* __restrict__ prev_lab, int clu_stride, int count, int K,
+    int ranges, int xcd_map, const uint16_t* __restrict__ k_tok, int capacity, int n_sink,
+    const double* __restrict__ invn, int fbits, long long* __restrict__ sfix, int32_t* __restrict__ csize) {
+  constexpr int kSlices = kHeadDim / D;
+  constexpr int LK = D / 8;       // lanes per key
+  constexpr int KW = kWave / LK;  // keys per wave batch
+  constexpr int ROW = D + LK;     // LDS slots per cluster row
+  constexpr int kDelGroup = 2;   // key batches whose row loads are issued together
+  // a listed key: token offset in the wave's segment, then the new and old
+  // cluster relative to the range (kNone: outside it)
+  constexpr int LB = delta_label_bits(D), OB = 32 - 2 * LB;
+  constexpr uint32_t kNone = (1u << LB) - 1;
+  extern __shared__ __align__(16) unsigned char dlds[];
+  const int R = (K + ranges - 1) / ranges;
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(dlds);  // [R][ROW]
+  int* dn = reinterpret_cast<int*>(acc + (size_t)R * ROW);                // [R] member count changes
+  int* touched = dn + R;                                                   // [R]
+  uint32_t* buf = reinterpret_cast<uint32_t*>(touched + R);                // [waves][kDelBuf] listed keys
+  // Workgroups are dealt to the 8 XCDs round-robin; with xcd_map (units a
+  // multiple of 8) all workgroups of a unit share one XCD.
+  const int P = kSlices * ranges;
+  const int b = blockIdx.x;
+  const int u = xcd_map ? (b & 7) + 8 * ((b >> 3) / P) : b / P;
+  const int q = xcd_map ? (b >> 3) % P : b % P;
+  const int slice = q % kSlices, p = q / kSlices;
+  const int c_lo = (int)((long)K * p / ranges);
+  const int c_hi = (int)((long)K * (p + 1) / ranges);
+  const int nr = c_hi - c_lo;  // 1 <= nr <= R
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  for (int e = tid; e < nr * ROW; e += kDelThreads) acc[e] = 0ull;
+  for (int e = tid; e < nr; e += kDelThreads) dn[e] = touched[e] = 0;
+  __syncthreads();
+
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int32_t* cu = cur_lab + (size_t)u * clu_stride;
+  const int32_t* pu = FIRST ? nullptr : prev_lab + (size_t)u * clu_stride;
+  const int seg = delta_seg(count);
+  const int s_lo = min(count, wave * seg), s_hi = min(count, s_lo + seg);
+  uint32_t* wb = buf + wave * kDelBuf;
+  const int kk = lane / LK, lk = lane % LK;
+  const uint16_t* ku = k_tok + ((size_t)u * capacity + n_sink) * kHeadDim + slice * D + 8 * lk;
+  const double* iu = invn + (size_t)u * clu_stride;
+  const double scale = __builtin_ldexp(1.0, fbits);
+  const double magic = 6755399441055744.0;  // 1.5 * 2^52: adding it rounds to an integer
+  const long long magic_bits = __double_as_longlong(magic);
+
+  // KW keys per batch, kDelGroup batches per load group, two groups in flight
+  auto load_group = [&](int k0, int nb, uint4(&x)[kDelGroup], double(&iv)[kDelGroup],
+                        uint32_t(&ent)[kDelGroup]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kDelGroup; ++s) {
+      const int k = k0 + s * KW + kk;
+      ent[s] = k < nb ? wb[k] : 0xffffffffu;
+      if (k < nb) {
+        const int i = s_lo + (int)(ent[s] & ((1u << OB) - 1));
+        x[s] = *reinterpret_cast<const uint4*>(ku + (size_t)i * kHeadDim);
+        iv[s] = iu[i];
+      }
+    }
+  };
+  auto add_group = [&](const uint4(&x)[kDelGroup], const double(&iv)[kDelGroup],
+                       const uint32_t(&ent)[kDelGroup]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < kDelGroup; ++s) {
+      if (ent[s] == 0xffffffffu) continue;
+      const uint32_t cr = (ent[s] >> OB) & kNone, pr = ent[s] >> (OB + LB);
+      const uint32_t w[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+      const double ivf = iv[s] * scale;
+      unsigned long long* rc = acc + (size_t)cr * ROW + lk;
+      unsigned long long* rp = acc + (size_t)pr * ROW + lk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+        const unsigned long long v =
+            (unsigned long long)__double_as_longlong(fma((double)__uint_as_float(h), ivf, magic));
+        if (cr != kNone) atomicAdd(rc + LK * e, v);
+        if (pr != kNone) atomicSub(rp + LK * e, v);
+      }
+    }
+  };
+  // add the wave's listed keys, then empty the list
+  auto drain = [&](int nb) __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    constexpr int kStep = kDelGroup * KW;
+    uint4 xa[kDelGroup], xb[kDelGroup];
+    double ia[kDelGroup], ib[kDelGroup];
+    uint32_t ea[kDelGroup], eb[kDelGroup];
+    if (nb > 0) load_group(0, nb, xa, ia, ea);
+    for (int k0 = 0; k0 < nb; k0 += 2 * kStep) {
+      if (k0 + kStep < nb) load_group(k0 + kStep, nb, xb, ib, eb);
+      add_group(xa, ia, ea);
+      if (k0 + kStep >= nb) break;
+      if (k0 + 2 * kStep < nb) load_group(k0 + 2 * kStep, nb, xa, ia, ea);
+      add_group(xb, ib, eb);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the list is read before it is refilled
+  };
+
+  // Each wave walks its token segment in chunks of kDelPer batches, with all
+  // of a chunk's labels (this round's and the previous one's, packed as
+  // new | old << 16) loaded together.  It lists the keys that changed
+  // cluster (in the first round every key) whose new or old cluster is in the
+  // range, and adds them when the list could not take 4 more batches, so a
+  // round with few changes pays few row loads.
+  int nb = 0;  // listed keys (uniform over the wave)
+  for (int b0 = s_lo; b0 < s_hi; b0 += kDelPer * kWave) {
+    uint32_t lv[kDelPer];
+    {
+      int cv[kDelPer], ov[kDelPer];
+#pragma unroll
+      for (int j = 0; j < kDelPer; ++j) {
+        const int i = b0 + j * kWave + lane;
+        cv[j] = i < s_hi ? cu[i] : 0;
+        ov[j] = (!FIRST && i < s_hi) ? pu[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kDelPer; ++j) {
+        const int c = cv[j] < 0 ? 0 : (cv[j] >= K ? K - 1 : cv[j]);
+        const int o = ov[j] < 0 ? 0 : (ov[j] >= K ? K - 1 : ov[j]);
+        lv[j] = (uint32_t)c | ((uint32_t)o << 16);
+      }
+    }
+    // batch j of the chunk into the list
+    auto list_batch = [&](int j, uint32_t l) __attribute__((always_inline)) {
+      const int i = b0 + j * kWave + lane;
+      const int c = (int)(l & 0xffffu), o = (int)(l >> 16);
+      const bool moved = FIRST || c != o;
+      const bool cin = i < s_hi && moved && c >= c_lo && c < c_hi;
+      const bool pin = !FIRST && i < s_hi && moved && o >= c_lo && o < c_hi;
+      if (cin) {
+        atomicAdd(&dn[c - c_lo], 1);
+        touched[c - c_lo] = 1;
+      }
+      if (pin) {
+        atomicAdd(&dn[o - c_lo], -1);
+        touched[o - c_lo] = 1;
+      }
+      const bool mine = cin || pin;
+      const unsigned long long m = __ballot(mine);
+      if (mine)
+        wb[nb + __popcll(m & lt)] = (uint32_t)(i - s_lo) | ((cin ? (uint32_t)(c - c_lo) : kNone) << OB) |
+                                    ((pin ? (uint32_t)(o - c_lo) : kNone) << (OB + LB));
+      nb += __popcll(m);
+    };
+    // four batches at a time, the list drained first when it could not take
+    // them (one drain site in a loop that is not unrolled)
+#pragma unroll 1
+    for (int j0 = 0; j0 < kDelPer; j0 += 4) {
+      if (b0 + j0 * kWave >= s_hi) break;  // uniform over the wave
+      if (nb > kDelBuf - 4 * kWave) {
+        drain(nb);
+        nb = 0;
+      }
+      static_assert(kDelPer % 4 == 0 && kDelPer <= 32, "one case per 4 batches of the chunk");
+      switch (j0) {  // static register indices for the labels
+#define CKV_LIST4(J)                                      \
+  case J:                                                 \
+    if (J < kDelPer) {                                    \
+      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {  \
+        if (b0 + (J + jj) * kWave >= s_hi) break;         \
+        list_batch(J + jj, lv[(J + jj) % kDelPer]);       \
+      }                                                   \
+    }                                                     \
+    break;
+        CKV_LIST4(0)
+        CKV_LIST4(4)
+        CKV_LIST4(8)
+        CKV_LIST4(12)
+        CKV_LIST4(16)
+        CKV_LIST4(20)
+        CKV_LIST4(24)
+        CKV_LIST4(28)
+#undef CKV_LIST4
+      }
+    }
+  }
+  drain(nb);
+  __syncthreads();
+
+  // This slice of the touched rows into S (LK lanes per row, 8 dims each);
+  // slice 0 also moves n.
+  for (int r = wave * KW + kk; r < nr; r += kDelWaves * KW) {
+    if (!FIRST && touched[r] == 0) continue;
+    const size_t j = (size_t)u * K + c_lo + r;
+    const size_t sidx = j * kHeadDim + slice * D + 8 * lk;
+    // net members added times the bits of 1.5 * 2^52 come off every slot
+    const unsigned long long bias = (unsigned long long)(long long)dn[r] * (unsigned long long)magic_bits;
+    long long sf[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const long long add = (long long)(acc[(size_t)r * ROW + LK * t + lk] - bias);
+      sf[t] = (FIRST ? 0ll : sfix[sidx + t]) + add;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sfix[sidx + t] = sf[t];
+    if (slice == 0 && lk == 0) csize[j] = (FIRST ? 0 : csize[j]) + dn[r];
+  }
+}
+
+
+// c_j = bf16(S_j / |S_j|) from the fixed-point sums where n_j > 0 and
+// S_j != 0 (otherwise c_j stays): 16 lanes per cluster row, 8 dims each.
+__global__ __launch_bounds__(1024) void delta_dirs_kernel(const long long* __restrict__ sfix,
+                                                          const int32_t* __restrict__ csize,
+                                                          uint16_t* __restrict__ cdir, long rows, int fbits) {
+  const long row = (long)blockIdx.x * 64 + (threadIdx.x >> 4);
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const int li = threadIdx.x & 15;
+  const size_t sidx = (size_t)row * kHeadDim + li * 8;
+  const double unscale = __builtin_ldexp(1.0, -fbits);
+  double sv[8];
+  double ns2 = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    sv[t] = (double)sfix[sidx + t] * unscale;
+    ns2 += sv[t] * sv[t];
+  }
+  ns2 = xor_sum16(ns2);
+  if (csize[row] > 0 && ns2 > 0.0) {
+    const double nrm = sqrt(ns2);
+    uint32_t wv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      wv[t] = (uint32_t)f64_to_bf16_rne(sv[2 * t] / nrm) | ((uint32_t)f64_to_bf16_rne(sv[2 * t + 1] / nrm) << 16);
+    *reinterpret_cast<uint4*>(cdir + sidx) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Inverse key norms 1/|x| (f64) of clustered tokens [first, first + count):
 // 16 lanes per row, kNormRows rows per 16-lane group with all their loads in
 // flight (a workgroup covers 16 * kNormRows consecutive rows, each load
@@ -1177,6 +1486,45 @@ hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K,
   const int xcd_map = (units % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(index_kernel, dim3((unsigned)(units * ranges)), dim3(kIdxThreads), lds, s, assign, clu_stride,
                      count, K, ranges, stage, xcd_map, n_sink, perm, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu_stride, int count, int K,
+                        const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
+                        int32_t* csize, uint16_t* cdir, int units, hipStream_t s) {
+  if (!delta_supported(K, count, units)) return hipErrorInvalidValue;
+  const int D = delta_dims(K);
+  const int ranges = delta_ranges(units, K);
+  const size_t lds = delta_lds_bytes(K, ranges);
+  static std::once_flag lds_once;  // above the default dynamic LDS limit
+  static hipError_t lds_status = hipSuccess;
+  std::call_once(lds_once, [] {
+    const void* fns[] = {(const void*)delta_kernel<32, true>, (const void*)delta_kernel<32, false>,
+                         (const void*)delta_kernel<16, true>, (const void*)delta_kernel<16, false>};
+    for (const void* f : fns)
+      if (lds_status == hipSuccess)
+        lds_status = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kIdxLdsMax);
+  });
+  if (lds_status != hipSuccess) return lds_status;
+  const int xcd_map = (units % 8 == 0) ? 1 : 0;
+  const int fbits = delta_fbits(count);
+  long long* sfix = reinterpret_cast<long long*>(csum);
+  const dim3 grid((unsigned)(units * (kHeadDim / D) * ranges));
+#define CKV_DELTA(DD, F)                                                                                     \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<DD, F>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab, \
+                     clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize)
+  const bool first = prev_lab == nullptr;
+  if (D == 32) {
+    if (first) CKV_DELTA(32, true); else CKV_DELTA(32, false);
+  } else {
+    if (first) CKV_DELTA(16, true); else CKV_DELTA(16, false);
+  }
+#undef CKV_DELTA
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = (long)units * K;
+  hipLaunchKernelGGL(delta_dirs_kernel, dim3((unsigned)((rows + 63) / 64)), dim3(1024), 0, s, sfix, csize, cdir, rows,
+                     fbits);
   return hipGetLastError();
 }
 
