@@ -235,19 +235,20 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
     e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, cur, clu_stride, 0, units, s,
                            it == 0 ? invn : nullptr);
     if (e != hipSuccess) return hip_status(e, "assign");
-    if (by_changes && !last) {
-      e = ckv::launch_delta(cur, it == 0 ? nullptr : prev, clu_stride, m, K, L->k_tok, L->capacity, L->n_sink, invn,
-                            L->csum, L->csize, L->cdir, units, s);
+    if (by_changes && !last && it > 0) {
+      e = ckv::launch_delta(cur, prev, clu_stride, m, K, L->k_tok, L->capacity, L->n_sink, invn, L->csum, L->csize,
+                            L->cdir, units, s);
       if (e != hipSuccess) return hip_status(e, "delta update");
       continue;
     }
-    // index, then the sums and directions from scratch; the last round also
-    // writes the means and the cluster-ordered rows
-    e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
+    // index, then the sums and directions from scratch (the first of rounds by
+    // changes keeps them as fixed-point sums); the last round also writes the
+    // means and the cluster-ordered rows
+    e = ckv::launch_index(cur, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
     if (e != hipSuccess) return hip_status(e, "index");
-    e = ckv::launch_update(last ? ckv::kUpdFinal : ckv::kUpdIter, L->k_tok, L->v_tok, L->capacity, L->n_sink,
-                           L->perm, clu_stride, L->offsets, K, invn, L->csum, L->msum, L->cmean, L->csize, L->cdir,
-                           L->k_clu, L->v_clu, units, s);
+    const int mode = last ? ckv::kUpdFinal : (by_changes ? ckv::kUpdFixed : ckv::kUpdIter);
+    e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K, invn,
+                           L->csum, L->msum, L->cmean, L->csize, L->cdir, L->k_clu, L->v_clu, units, s, m);
     if (e != hipSuccess) return hip_status(e, "update");
   }
   L->n_total = n;

@@ -696,7 +696,9 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __res
 // the order of the additions.  The rounding to 2^-F (at most 2^-48 per
 // term at m < 2^15) is far below what f64 summation in any order already
 // leaves.  Directions are then c_j = bf16(S_j / |S_j|) from S_j in f64, as
-// in the update kernel; the last round rebuilds everything from the index.
+// in the update kernel.  The first round sums from scratch (index, then the
+// update kernel's fixed mode) and the last rebuilds everything from the index;
+// the rounds between move by the changes.
 //
 // A workgroup of 1024 threads owns one (unit, slice of D dims, range of
 // clusters); with units >= 64 the range is all K clusters, so a key that
@@ -712,8 +714,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __res
 // the bits of 1.5 * 2^52; the row's net member change times those bits is
 // taken off at the end.  Each workgroup then adds its touched rows into S
 // (slice 0 also moves n), and delta_dirs_kernel recomputes the directions
-// from the whole rows.  The first round starts from zero sums and adds every
-// key.
+// from the whole rows.
 // ---------------------------------------------------------------------------
 constexpr int kDelThreads = 1024;
 constexpr int kDelWaves = kDelThreads / kWave;
@@ -763,7 +764,7 @@ int delta_fbits(int m) {
   return f < 50 ? f : 50;
 }
 
-template <int D, bool FIRST>
+template <int D>
 __global__ __launch_bounds__(kDelThreads) void delta_kernel(
     const int32_t* __restrict__ cur_lab, const int32_t* __restrict__ prev_lab, int clu_stride, int count, int K,
     int ranges, int xcd_map, const uint16_t* __restrict__ k_tok, int capacity, int n_sink,
@@ -800,7 +801,7 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
 
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int32_t* cu = cur_lab + (size_t)u * clu_stride;
-  const int32_t* pu = FIRST ? nullptr : prev_lab + (size_t)u * clu_stride;
+  const int32_t* pu = prev_lab + (size_t)u * clu_stride;
   const int seg = delta_seg(count);
   const int s_lo = min(count, wave * seg), s_hi = min(count, s_lo + seg);
   uint32_t* wb = buf + wave * kDelBuf;
@@ -868,9 +869,9 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
   // Each wave walks its token segment in chunks of kDelPer batches, with all
   // of a chunk's labels (this round's and the previous one's, packed as
   // new | old << 16) loaded together.  It lists the keys that changed
-  // cluster (in the first round every key) whose new or old cluster is in the
-  // range, and adds them when the list could not take 4 more batches, so a
-  // round with few changes pays few row loads.
+  // cluster whose new or old cluster is in the range, and adds them when the
+  // list could not take 4 more batches, so a round with few changes pays few
+  // row loads.
   int nb = 0;  // listed keys (uniform over the wave)
   for (int b0 = s_lo; b0 < s_hi; b0 += kDelPer * kWave) {
     uint32_t lv[kDelPer];
@@ -880,7 +881,7 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
       for (int j = 0; j < kDelPer; ++j) {
         const int i = b0 + j * kWave + lane;
         cv[j] = i < s_hi ? cu[i] : 0;
-        ov[j] = (!FIRST && i < s_hi) ? pu[i] : 0;
+        ov[j] = i < s_hi ? pu[i] : 0;
       }
 #pragma unroll
       for (int j = 0; j < kDelPer; ++j) {
@@ -893,9 +894,9 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
     auto list_batch = [&](int j, uint32_t l) __attribute__((always_inline)) {
       const int i = b0 + j * kWave + lane;
       const int c = (int)(l & 0xffffu), o = (int)(l >> 16);
-      const bool moved = FIRST || c != o;
+      const bool moved = c != o;
       const bool cin = i < s_hi && moved && c >= c_lo && c < c_hi;
-      const bool pin = !FIRST && i < s_hi && moved && o >= c_lo && o < c_hi;
+      const bool pin = i < s_hi && moved && o >= c_lo && o < c_hi;
       if (cin) {
         atomicAdd(&dn[c - c_lo], 1);
         touched[c - c_lo] = 1;
@@ -949,7 +950,7 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
   // This slice of the touched rows into S (LK lanes per row, 8 dims each);
   // slice 0 also moves n.
   for (int r = wave * KW + kk; r < nr; r += kDelWaves * KW) {
-    if (!FIRST && touched[r] == 0) continue;
+    if (touched[r] == 0) continue;
     const size_t j = (size_t)u * K + c_lo + r;
     const size_t sidx = j * kHeadDim + slice * D + 8 * lk;
     // net members added times the bits of 1.5 * 2^52 come off every slot
@@ -958,11 +959,11 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const long long add = (long long)(acc[(size_t)r * ROW + LK * t + lk] - bias);
-      sf[t] = (FIRST ? 0ll : sfix[sidx + t]) + add;
+      sf[t] = sfix[sidx + t] + add;
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) sfix[sidx + t] = sf[t];
-    if (slice == 0 && lk == 0) csize[j] = (FIRST ? 0 : csize[j]) + dn[r];
+    if (slice == 0 && lk == 0) csize[j] += dn[r];
   }
 }
 
@@ -1041,13 +1042,20 @@ __global__ __launch_bounds__(256) void inv_norm_kernel(const uint16_t* __restric
 // that hold it, in the same order as inv_norm_kernel, so the value is the
 // same) instead of being read from invn; for a single pass over the keys this
 // saves the separate norm pass.
+//
+// Fixed mode (a Lloyd round followed by rounds by changes): as the iteration
+// mode, but S is summed as the exact fixed-point integers of the rounds by
+// changes (rint(x_d / |x| * 2^fbits) as int64, written over csum) and the
+// direction is computed from them as delta_dirs_kernel does.
 template <int MODE, bool OWN_NORMS>
 __global__ __launch_bounds__(256) void update_kernel(
     const uint16_t* __restrict__ k_tok, const uint16_t* __restrict__ v_tok, int capacity, int n_sink,
     const int32_t* __restrict__ perm, int clu_stride, const int32_t* __restrict__ offsets, int K,
     const double* __restrict__ invn, double* __restrict__ csum, double* __restrict__ msum,
     float* __restrict__ cmean, int32_t* __restrict__ csize, uint16_t* __restrict__ cdir,
-    uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, int units) {
+    uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, int units, int fbits) {
+  constexpr bool FX = MODE == kUpdFixed;
+  constexpr bool ITER = MODE == kUpdIter || FX;  // sums and directions only
   const int lane = lane_id();
   const long gw = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= (long)units * K) return;
@@ -1063,8 +1071,15 @@ __global__ __launch_bounds__(256) void update_kernel(
   const int acc_from = lo + n_old;
 
   double s[8], mm[8];
+  long long sf[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) s[t] = mm[t] = 0.0;
+  for (int t = 0; t < 8; ++t) {
+    s[t] = mm[t] = 0.0;
+    sf[t] = 0ll;
+  }
+  const double fx_scale = __builtin_ldexp(1.0, fbits);
+  const double fx_magic = 6755399441055744.0;  // 1.5 * 2^52, as in the rounds by changes
+  const long long fx_magic_bits = __double_as_longlong(fx_magic);
 
   const int32_t* pu = perm + (size_t)u * clu_stride;
   const double* iu = OWN_NORMS ? nullptr : invn + (size_t)u * clu_stride;
@@ -1092,14 +1107,14 @@ __global__ __launch_bounds__(256) void update_kernel(
       const int p = p0 + 4 * k + g;
       if (p < hi) {
         kx[k] = *reinterpret_cast<const uint4*>(ku + (size_t)tks[k] * kHeadDim);
-        if (MODE != kUpdIter) vx[k] = *reinterpret_cast<const uint4*>(vu + (size_t)tks[k] * kHeadDim);
+        if (!ITER) vx[k] = *reinterpret_cast<const uint4*>(vu + (size_t)tks[k] * kHeadDim);
       }
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int p = p0 + 4 * k + g;
       if (p >= hi) continue;
-      if (MODE != kUpdIter) {
+      if (!ITER) {
         *reinterpret_cast<uint4*>(k_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = kx[k];
         *reinterpret_cast<uint4*>(v_dst + ((size_t)u * clu_stride + p) * kHeadDim + li * 8) = vx[k];
       }
@@ -1117,20 +1132,35 @@ __global__ __launch_bounds__(256) void update_kernel(
         n2 = xor_sum16(n2);
         ivk = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
       }
+      if constexpr (FX) {
+        const double ivf = ivk * fx_scale;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        s[t] = fma(x[t], ivk, s[t]);
-        if (MODE != kUpdIter) mm[t] += x[t];
+        for (int t = 0; t < 8; ++t) sf[t] += __double_as_longlong(fma(x[t], ivf, fx_magic)) - fx_magic_bits;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          s[t] = fma(x[t], ivk, s[t]);
+          if (!ITER) mm[t] += x[t];
+        }
       }
     }
   }
+  if constexpr (FX) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    s[t] += __shfl_xor(s[t], 16);
-    s[t] += __shfl_xor(s[t], 32);
-    if (MODE != kUpdIter) {
-      mm[t] += __shfl_xor(mm[t], 16);
-      mm[t] += __shfl_xor(mm[t], 32);
+    for (int t = 0; t < 8; ++t) {
+      sf[t] += __shfl_xor(sf[t], 16);
+      sf[t] += __shfl_xor(sf[t], 32);
+      s[t] = (double)sf[t] * __builtin_ldexp(1.0, -fbits);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      s[t] += __shfl_xor(s[t], 16);
+      s[t] += __shfl_xor(s[t], 32);
+      if (!ITER) {
+        mm[t] += __shfl_xor(mm[t], 16);
+        mm[t] += __shfl_xor(mm[t], 32);
+      }
     }
   }
   if (MODE == kUpdIncr) {
@@ -1146,8 +1176,13 @@ __global__ __launch_bounds__(256) void update_kernel(
   ns2 = xor_sum16(ns2);
   if (g != 0) return;
 
+  if constexpr (FX) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) csum[sidx + t] = s[t];
+    for (int t = 0; t < 8; ++t) reinterpret_cast<long long*>(csum)[sidx + t] = sf[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) csum[sidx + t] = s[t];
+  }
   const bool touched = (MODE == kUpdIncr) ? (n > n_old) : (n > 0);
   if (touched && ns2 > 0.0) {
     const double nrm = sqrt(ns2);
@@ -1157,7 +1192,7 @@ __global__ __launch_bounds__(256) void update_kernel(
       w[t] = (uint32_t)f64_to_bf16_rne(s[2 * t] / nrm) | ((uint32_t)f64_to_bf16_rne(s[2 * t + 1] / nrm) << 16);
     *reinterpret_cast<uint4*>(cdir + sidx) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (MODE != kUpdIter) {
+  if (!ITER) {
     float mu[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -1492,15 +1527,14 @@ hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K,
 hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu_stride, int count, int K,
                         const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
                         int32_t* csize, uint16_t* cdir, int units, hipStream_t s) {
-  if (!delta_supported(K, count, units)) return hipErrorInvalidValue;
+  if (!delta_supported(K, count, units) || prev_lab == nullptr) return hipErrorInvalidValue;
   const int D = delta_dims(K);
   const int ranges = delta_ranges(units, K);
   const size_t lds = delta_lds_bytes(K, ranges);
   static std::once_flag lds_once;  // above the default dynamic LDS limit
   static hipError_t lds_status = hipSuccess;
   std::call_once(lds_once, [] {
-    const void* fns[] = {(const void*)delta_kernel<32, true>, (const void*)delta_kernel<32, false>,
-                         (const void*)delta_kernel<16, true>, (const void*)delta_kernel<16, false>};
+    const void* fns[] = {(const void*)delta_kernel<32>, (const void*)delta_kernel<16>};
     for (const void* f : fns)
       if (lds_status == hipSuccess)
         lds_status = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kIdxLdsMax);
@@ -1510,16 +1544,12 @@ hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu
   const int fbits = delta_fbits(count);
   long long* sfix = reinterpret_cast<long long*>(csum);
   const dim3 grid((unsigned)(units * (kHeadDim / D) * ranges));
-#define CKV_DELTA(DD, F)                                                                                     \
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<DD, F>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab, \
-                     clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize)
-  const bool first = prev_lab == nullptr;
-  if (D == 32) {
-    if (first) CKV_DELTA(32, true); else CKV_DELTA(32, false);
-  } else {
-    if (first) CKV_DELTA(16, true); else CKV_DELTA(16, false);
-  }
-#undef CKV_DELTA
+  if (D == 32)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<32>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab,
+                       clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<16>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab,
+                       clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)units * K;
@@ -1540,18 +1570,21 @@ hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int 
 hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity, int n_sink,
                          const int32_t* perm, int clu_stride, const int32_t* offsets, int K,
                          const double* invn, double* csum, double* msum, float* cmean, int32_t* csize,
-                         uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units, hipStream_t s) {
+                         uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst, int units, hipStream_t s, int count) {
   const long waves = (long)units * K;
+  const int fbits = mode == kUpdFixed ? delta_fbits(count) : 0;
   const dim3 grid((unsigned)((waves + 3) / 4));
 #define CKV_UPD(M, O)                                                                                     \
   hipLaunchKernelGGL(HIP_KERNEL_NAME(update_kernel<M, O>), grid, dim3(256), 0, s, k_tok, v_tok, capacity, \
                      n_sink, perm, clu_stride, offsets, K, invn, csum, msum, cmean, csize, cdir, k_dst, v_dst, \
-                     units)
+                     units, fbits)
   if (invn == nullptr) {  // norms from the rows themselves: the final mode only
     if (mode != kUpdFinal) return hipErrorInvalidValue;
     CKV_UPD(kUpdFinal, true);
   } else if (mode == kUpdIter) {
     CKV_UPD(kUpdIter, false);
+  } else if (mode == kUpdFixed) {
+    CKV_UPD(kUpdFixed, false);
   } else if (mode == kUpdFinal) {
     CKV_UPD(kUpdFinal, false);
   } else {

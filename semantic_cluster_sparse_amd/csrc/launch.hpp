@@ -13,7 +13,7 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxChunks = 64;      // split-K chunks per unit in sparse decode
 constexpr int kPartialStride = 130; // floats per (chunk, head) partial: o[128], m, l
 
-enum UpdateMode { kUpdIter = 0, kUpdFinal = 1, kUpdIncr = 2 };
+enum UpdateMode { kUpdIter = 0, kUpdFinal = 1, kUpdIncr = 2, kUpdFixed = 3 };
 
 // init_idx[u, 0:K] = Floyd's sample of K distinct indices in [0, m) driven
 // by SplitMix64 from state seed + u (K <= kMaxClusters, K <= m).
@@ -40,24 +40,26 @@ hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int 
 hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K, int n_sink, int32_t* perm,
                         int32_t* offsets, int units, hipStream_t s);
 
-// A Lloyd round before the last from the keys that changed cluster between
-// prev_lab and cur_lab [u, 0:count) (prev_lab NULL in the first round, which
-// adds every key to zeroed sums).  While the rounds run, csum holds the
-// unit-key sums as int64 fixed point (the last round's update writes them in
-// f64 again); csize and cdir are kept current.  invn[u, i] = 1/|x_i| of every
+// A Lloyd round between the first and the last from the keys that changed
+// cluster between prev_lab and cur_lab [u, 0:count).  While the rounds run,
+// csum holds the unit-key sums as int64 fixed point (the first round's
+// kUpdFixed update writes them, the last round's update writes them in f64
+// again); csize and cdir are kept current.  invn[u, i] = 1/|x_i| of every
 // clustered token.  delta_supported says whether a shape takes this form
-// (else the rounds rebuild from the index).
+// (else every round rebuilds from the index).
 bool delta_supported(int K, int count, int units);
 hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu_stride, int count, int K,
                         const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
                         int32_t* csize, uint16_t* cdir, int units, hipStream_t s);
 
 // Per-cluster segmented reduction over the members listed by perm/offsets.
+// kUpdFixed writes csum as the int64 fixed-point sums of launch_delta (count =
+// the clustered keys per unit, which fixes the scale).
 hipError_t launch_update(int mode, const uint16_t* k_tok, const uint16_t* v_tok, int capacity,
                          int n_sink, const int32_t* perm, int clu_stride, const int32_t* offsets,
                          int K, const double* invn, double* csum, double* msum, float* cmean,
                          int32_t* csize, uint16_t* cdir, uint16_t* k_dst, uint16_t* v_dst,
-                         int units, hipStream_t s);
+                         int units, hipStream_t s, int count = 0);
 
 // Drift split: the pairs go to plan [units, 2K + 1] int32 (workspace), then
 // the labels of the split clusters' members are rewritten.
