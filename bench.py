@@ -124,11 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "82f1da9d406bc88868b006f05f7bdf1d2ef44f40818689ccad6f7b6a00d9df9c",
-                      "fetch_kib": 47176.3, "write_kib": 1274.3},
+                      "sha256": "5af90ca1745a9b59aa68c25e7d7bf0fd593daea21386301b7937b22c4c8f2a98",
+                      "fetch_kib": 47176.1, "write_kib": 1274.3},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "1ee911bcd2c9dc4b9f3b6611d1ce56fafc1fdecf52801385a751f1cf79e4cb77",
-                      "fetch_kib": 34286.8, "write_kib": 762.0},
+                      "sha256": "3a47c2f286c48994e806d56d51569a6015a015093a480f532bda51fd9964f8ea",
+                      "fetch_kib": 34287.0, "write_kib": 762.0},
 }
 
 
