@@ -288,6 +288,35 @@ def test_select_teacher_forced():
         say(f"  budget {budget}: ok")
 
 
+@pytest.mark.parametrize("U,iters", [(64, 2), (64, 7), (5, 4)])
+def test_rounds_by_changes(U, iters):
+    # The prefill's rounds between the first and the last move the cluster sums by the keys
+    # that changed cluster.  64 units: one workgroup per (unit, 32-dim slice), a unit's
+    # workgroups on one XCD; 5 units: ranges of clusters, no XCD mapping.  The oracle sums
+    # every round from scratch, so the final state checks every round's update.
+    K, n = 96, 16 + 6000
+    say(f"case: rounds by changes, {U} units, K={K}, n={n}, {iters} rounds")
+    ks, vs = [], []
+    for u in range(U):
+        kb, vb, _ = synth.make_unit_inputs(171, u, n, 128)
+        ks.append(kb), vs.append(vb)
+    k, v = np.stack(ks), np.stack(vs)
+    init = synth.make_init_indices(172, U, n - 16, K)
+    L = gpu_layer(k, v, 4, K, max_budget=256)
+    L.prefill(n, iters, to_dev(init, torch.int32))
+    torch.cuda.synchronize()
+    moved = 0
+    for u in sorted({0, U // 2, U - 1}):
+        ora = pipeline.prefill_unit(k[u], n, init[u], K, iters, v_bits=v[u], history=True)
+        hist = ora["history"]
+        # keys that changed cluster in the rounds by changes (rounds 2 .. iters - 1)
+        moved += sum(int((hist[t][0] != hist[t - 1][0]).sum()) for t in range(2, iters))
+        x = bf16.widen(k[u][16:n])
+        assert check_state(L, u, ora, x, hist[-2][1], tag=f"U={U} T={iters}") == 0
+    if iters > 2:
+        assert moved > 0, "no key changed cluster in the rounds by changes"
+
+
 @pytest.mark.parametrize("shape", ["llama8b-layer-32k", "glm4-stack-32k-b16"])
 def test_per_head_recall_and_decode(shape):
     """Per-query-head recall + decode, teacher-forced: the Llama layer (G = 4, units 0-3,
