@@ -37,7 +37,7 @@ struct Layout {
   size_t counters;  // [2 units] u32 arrival counters: decode, then select; zero between calls
   size_t aux;       // prefill: [units, K] int32 drawn indices; split: [units, 2K + 1] int32 pair plan
   size_t invn;      // prefill / incremental: [units, clu_cap] f64 inverse key norms
-  size_t labs;      // prefill: [units, clu_cap] int32 labels of alternate Lloyd rounds
+  size_t labs;      // prefill: [2, units, stride16] uint16 labels of alternate Lloyd rounds
   size_t scores;    // select: [units, K] f32
   size_t cut;       // select: [units, clu_cap] u32 keys of the cut cluster
   size_t partials;  // decode: [units, kMaxChunks, GT, 130] f32
@@ -51,6 +51,10 @@ int group_tier(int g) {
   while (t < g) t <<= 1;
   return t;
 }
+
+// Row stride of the prefill's 16-bit label buffers: the clustered capacity
+// rounded up to even, so rows and their dword loads stay aligned.
+int label16_stride(const ckv_layer* L) { return (L->capacity - L->n_sink + 1) & ~1; }
 
 // per_head: one recall / attention set per query head (units * group of them)
 // instead of one per KV head.
@@ -66,7 +70,7 @@ Layout layout_of(const ckv_layer* L, bool per_head = false) {
   w.counters = align256(units * (size_t)L->group * 2 * sizeof(uint32_t));
   w.aux = align256(units * (2 * (size_t)L->n_clusters + 1) * sizeof(int32_t));
   w.invn = align256(units * clu_cap * sizeof(double));
-  w.labs = align256(units * clu_cap * sizeof(int32_t));
+  w.labs = align256(2 * units * label16_stride(L) * sizeof(uint16_t));
   w.scores = align256(sets * L->n_clusters * sizeof(float));
   w.cut = align256(sets * clu_cap * sizeof(uint32_t));
   w.partials = align256(units * ckv::kMaxChunks * group_tier(L->group) * ckv::kPartialStride * sizeof(float));
@@ -220,31 +224,34 @@ int prefill_run(ckv_layer* L, int32_t n, int32_t iters, const int32_t* init_idx,
 
   hipError_t e = ckv::launch_init_dirs(L->k_tok, L->capacity, L->n_sink, m, init_idx, K, L->cdir, units, s);
   if (e != hipSuccess) return hip_status(e, "init");
-  int32_t* labs = (int32_t*)((char*)ws + w.off_labs);
-  // Rounds before the last move the sums by the keys that changed cluster
-  // where the shape allows it; otherwise every round rebuilds from the index.
+  // Rounds between the first and the last move the sums by the keys that
+  // changed cluster where the shape allows it; otherwise every round rebuilds
+  // from the index.  Those rounds' labels alternate between two 16-bit
+  // buffers in the workspace (the first round writes one of them beside
+  // assign); the first and the last round write assign, which the index reads.
+  const int stride16 = label16_stride(L);
+  uint16_t* lab16 = (uint16_t*)((char*)ws + w.off_labs);
   const bool by_changes = ckv::delta_supported(K, m, units);
   for (int it = 0; it < iters; ++it) {
     const bool last = it == iters - 1;
-    // Labels alternate between the layer's assign and the workspace, so that
-    // a round by changes sees the previous round's; the last round writes
-    // assign.
-    int32_t* cur = (!by_changes || (iters - 1 - it) % 2 == 0) ? L->assign : labs;
-    int32_t* prev = (cur == L->assign) ? labs : L->assign;
+    const bool middle = by_changes && !last && it > 0;
+    uint16_t* cur16 = lab16 + (size_t)(it % 2) * units * stride16;
+    uint16_t* prev16 = lab16 + (size_t)((it + 1) % 2) * units * stride16;
     // the first round's assignment also writes the keys' inverse norms
-    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, cur, clu_stride, 0, units, s,
-                           it == 0 ? invn : nullptr);
+    e = ckv::launch_assign(L->k_tok, L->capacity, L->n_sink, m, L->cdir, K, middle ? nullptr : L->assign,
+                           clu_stride, 0, units, s, it == 0 ? invn : nullptr,
+                           (by_changes && !last) ? cur16 : nullptr, stride16);
     if (e != hipSuccess) return hip_status(e, "assign");
-    if (by_changes && !last && it > 0) {
-      e = ckv::launch_delta(cur, prev, clu_stride, m, K, L->k_tok, L->capacity, L->n_sink, invn, L->csum, L->csize,
-                            L->cdir, units, s);
+    if (middle) {
+      e = ckv::launch_delta(cur16, prev16, stride16, clu_stride, m, K, L->k_tok, L->capacity, L->n_sink, invn,
+                            L->csum, L->csize, L->cdir, units, s);
       if (e != hipSuccess) return hip_status(e, "delta update");
       continue;
     }
     // index, then the sums and directions from scratch (the first of rounds by
     // changes keeps them as fixed-point sums); the last round also writes the
     // means and the cluster-ordered rows
-    e = ckv::launch_index(cur, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
+    e = ckv::launch_index(L->assign, clu_stride, m, K, L->n_sink, L->perm, L->offsets, units, s);
     if (e != hipSuccess) return hip_status(e, "index");
     const int mode = last ? ckv::kUpdFinal : (by_changes ? ckv::kUpdFixed : ckv::kUpdIter);
     e = ckv::launch_update(mode, L->k_tok, L->v_tok, L->capacity, L->n_sink, L->perm, clu_stride, L->offsets, K, invn,

@@ -304,11 +304,14 @@ constexpr int kAsResMaxK = 512;
 // invn[u, first + i], from the key registers it already holds (the chunk sums
 // and butterfly of inv_norm_kernel, so the values are the same bits); the
 // prefill's first round uses it instead of a separate pass over the keys.
+// Labels go to assign (int32, row stride clu_stride) and / or assign16
+// (uint16, row stride stride16), either of which may be null.
 template <bool NORMS>
 __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
     const uint16_t* __restrict__ k_tok, int capacity, int row0, int count,
     const uint16_t* __restrict__ cdir, int K, int32_t* __restrict__ assign, int clu_stride, int first,
-    int wg_per_unit, int tiles_per_wg, double* __restrict__ invn) {
+    int wg_per_unit, int tiles_per_wg, double* __restrict__ invn, uint16_t* __restrict__ assign16,
+    int stride16) {
   extern __shared__ __attribute__((aligned(16))) uint16_t csr[];
   const int u = blockIdx.x / wg_per_unit;
   const int part = blockIdx.x % wg_per_unit;
@@ -333,7 +336,8 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
   __syncthreads();
 
   const uint16_t* kbase = k_tok + ((size_t)u * capacity + row0) * kHeadDim;
-  int32_t* out = assign + (size_t)u * clu_stride + first;
+  int32_t* out = assign != nullptr ? assign + (size_t)u * clu_stride + first : nullptr;
+  uint16_t* out16 = assign16 != nullptr ? assign16 + (size_t)u * stride16 + first : nullptr;
   auto load_tile = [&](bf16x8 (&a)[kAsResMt][4], int t) {
 #pragma unroll
     for (int mt = 0; mt < kAsResMt; ++mt) {
@@ -454,7 +458,10 @@ __global__ __launch_bounds__(kAsResWaves * 64) void assign_resident_kernel(
         bi = take ? oi : bi;
       }
       const int r = t * kAsResTile + mt * 16 + r16;
-      if (kg == 0 && r < count) out[r] = bi;
+      if (kg == 0 && r < count) {
+        if (out != nullptr) out[r] = bi;
+        if (out16 != nullptr) out16[r] = (uint16_t)bi;
+      }
     }
     if constexpr (NORMS) {
       // lane (r16, kg) holds chunks c = 4 s + kg of key r16: the butterfly's
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __res
 // ---------------------------------------------------------------------------
 constexpr int kDelThreads = 1024;
 constexpr int kDelWaves = kDelThreads / kWave;
-constexpr int kDelPer = 12;                   // labels per lane loaded together
+constexpr int kDelPer = 16;                   // label dwords (two tokens each) per lane loaded together
 constexpr int kDelBuf = 8 * kWave;            // listed keys per wave
 constexpr int kDelMaxRanges = 32;            // cluster ranges per unit
 
@@ -751,7 +758,8 @@ size_t delta_lds_bytes(int K, int ranges) {
 // whether the delta rounds take this shape: the LDS rows fit and a wave's
 // segment offsets fit their field of a listed key
 bool delta_supported(int K, int count, int units) {
-  if (K < 1 || K > kMaxClusters || count < 1) return false;
+  // the rounds' 16-bit labels come from the resident assignment kernel
+  if (K < 1 || K > kAsResMaxK || count < 1) return false;
   const int D = delta_dims(K);
   if (delta_lds_bytes(K, delta_ranges(units, K)) > (size_t)kIdxLdsMax) return false;
   return delta_seg(count) <= (1 << (32 - 2 * delta_label_bits(D)));
@@ -766,7 +774,8 @@ int delta_fbits(int m) {
 
 template <int D>
 __global__ __launch_bounds__(kDelThreads) void delta_kernel(
-    const int32_t* __restrict__ cur_lab, const int32_t* __restrict__ prev_lab, int clu_stride, int count, int K,
+    const uint16_t* __restrict__ cur_lab, const uint16_t* __restrict__ prev_lab, int stride16, int clu_stride,
+    int count, int K,
     int ranges, int xcd_map, const uint16_t* __restrict__ k_tok, int capacity, int n_sink,
     const double* __restrict__ invn, int fbits, long long* __restrict__ sfix, int32_t* __restrict__ csize) {
   constexpr int kSlices = kHeadDim / D;
@@ -800,8 +809,9 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
   __syncthreads();
 
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int32_t* cu = cur_lab + (size_t)u * clu_stride;
-  const int32_t* pu = prev_lab + (size_t)u * clu_stride;
+  // a unit's labels as dwords of two (stride16 and the segments' starts are even)
+  const uint32_t* cu = reinterpret_cast<const uint32_t*>(cur_lab + (size_t)u * stride16);
+  const uint32_t* pu = reinterpret_cast<const uint32_t*>(prev_lab + (size_t)u * stride16);
   const int seg = delta_seg(count);
   const int s_lo = min(count, wave * seg), s_hi = min(count, s_lo + seg);
   uint32_t* wb = buf + wave * kDelBuf;
@@ -866,34 +876,27 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
     __builtin_amdgcn_wave_barrier();  // the list is read before it is refilled
   };
 
-  // Each wave walks its token segment in chunks of kDelPer batches, with all
-  // of a chunk's labels (this round's and the previous one's, packed as
-  // new | old << 16) loaded together.  It lists the keys that changed
-  // cluster whose new or old cluster is in the range, and adds them when the
-  // list could not take 4 more batches, so a round with few changes pays few
-  // row loads.
+  // Each wave walks its token segment in chunks of 2 kDelPer batches, with
+  // both rounds' labels of a chunk loaded together as dwords of two tokens
+  // (one load round trip per chunk: a whole segment at the benchmark's
+  // shapes).  It lists the keys that changed cluster whose new or old cluster
+  // is in the range, and adds them when the list could not take 4 more
+  // batches, so a round with few changes pays few row loads.
   int nb = 0;  // listed keys (uniform over the wave)
-  for (int b0 = s_lo; b0 < s_hi; b0 += kDelPer * kWave) {
-    uint32_t lv[kDelPer];
-    {
-      int cv[kDelPer], ov[kDelPer];
+  for (int b0 = s_lo; b0 < s_hi; b0 += 2 * kDelPer * kWave) {
+    uint32_t cd[kDelPer], od[kDelPer];
 #pragma unroll
-      for (int j = 0; j < kDelPer; ++j) {
-        const int i = b0 + j * kWave + lane;
-        cv[j] = i < s_hi ? cu[i] : 0;
-        ov[j] = i < s_hi ? pu[i] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kDelPer; ++j) {
-        const int c = cv[j] < 0 ? 0 : (cv[j] >= K ? K - 1 : cv[j]);
-        const int o = ov[j] < 0 ? 0 : (ov[j] >= K ? K - 1 : ov[j]);
-        lv[j] = (uint32_t)c | ((uint32_t)o << 16);
-      }
+    for (int j = 0; j < kDelPer; ++j) {
+      const int i = b0 + 2 * (j * kWave + lane);  // even: tokens i and i + 1
+      cd[j] = i < s_hi ? cu[i >> 1] : 0u;
+      od[j] = i < s_hi ? pu[i >> 1] : 0u;
     }
-    // batch j of the chunk into the list
-    auto list_batch = [&](int j, uint32_t l) __attribute__((always_inline)) {
-      const int i = b0 + j * kWave + lane;
-      const int c = (int)(l & 0xffffu), o = (int)(l >> 16);
+    // one token per lane of dword j (h = 0: its low label, 1: its high one)
+    auto list_batch = [&](int j, int h, uint32_t cdw, uint32_t odw) __attribute__((always_inline)) {
+      const int i = b0 + 2 * (j * kWave + lane) + h;
+      const int c_raw = (int)(h ? cdw >> 16 : cdw & 0xffffu), o_raw = (int)(h ? odw >> 16 : odw & 0xffffu);
+      const int c = c_raw >= K ? K - 1 : c_raw;
+      const int o = o_raw >= K ? K - 1 : o_raw;
       const bool moved = c != o;
       const bool cin = i < s_hi && moved && c >= c_lo && c < c_hi;
       const bool pin = i < s_hi && moved && o >= c_lo && o < c_hi;
@@ -912,35 +915,19 @@ __global__ __launch_bounds__(kDelThreads) void delta_kernel(
                                     ((pin ? (uint32_t)(o - c_lo) : kNone) << (OB + LB));
       nb += __popcll(m);
     };
-    // four batches at a time, the list drained first when it could not take
-    // them (one drain site in a loop that is not unrolled)
-#pragma unroll 1
-    for (int j0 = 0; j0 < kDelPer; j0 += 4) {
-      if (b0 + j0 * kWave >= s_hi) break;  // uniform over the wave
+    // two dwords (four batches) at a time, the list drained first when it
+    // could not take them
+#pragma unroll
+    for (int j0 = 0; j0 < kDelPer; j0 += 2) {
+      if (b0 + 2 * j0 * kWave >= s_hi) break;  // uniform over the wave
       if (nb > kDelBuf - 4 * kWave) {
         drain(nb);
         nb = 0;
       }
-      static_assert(kDelPer % 4 == 0 && kDelPer <= 32, "one case per 4 batches of the chunk");
-      switch (j0) {  // static register indices for the labels
-#define CKV_LIST4(J)                                      \
-  case J:                                                 \
-    if (J < kDelPer) {                                    \
-      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) {  \
-        if (b0 + (J + jj) * kWave >= s_hi) break;         \
-        list_batch(J + jj, lv[(J + jj) % kDelPer]);       \
-      }                                                   \
-    }                                                     \
-    break;
-        CKV_LIST4(0)
-        CKV_LIST4(4)
-        CKV_LIST4(8)
-        CKV_LIST4(12)
-        CKV_LIST4(16)
-        CKV_LIST4(20)
-        CKV_LIST4(24)
-        CKV_LIST4(28)
-#undef CKV_LIST4
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        list_batch(j0 + jj, 0, cd[j0 + jj], od[j0 + jj]);
+        list_batch(j0 + jj, 1, cd[j0 + jj], od[j0 + jj]);
       }
     }
   }
@@ -1463,8 +1450,10 @@ hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int
 
 hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
-                         int first, int units, hipStream_t s, double* invn) {
+                         int first, int units, hipStream_t s, double* invn, uint16_t* assign16,
+                         int stride16) {
   if (count <= 0) return hipSuccess;
+  if (assign16 != nullptr && K > kAsResMaxK) return hipErrorInvalidValue;  // the resident kernel only
   if (K <= kAsResMaxK) {
     // about one 8-wave workgroup per CU, each on one unit's range of key tiles
     const int ntiles = (count + kAsResTile - 1) / kAsResTile;
@@ -1489,10 +1478,12 @@ hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int coun
     if (lds_status != hipSuccess) return lds_status;
     if (invn != nullptr)
       hipLaunchKernelGGL(assign_resident_kernel<true>, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds,
-                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn);
+                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn,
+                         assign16, stride16);
     else
       hipLaunchKernelGGL(assign_resident_kernel<false>, dim3((unsigned)(units * wpu)), dim3(kAsResWaves * 64), lds,
-                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn);
+                         s, k_tok, capacity, row0, count, cdir, K, assign, clu_stride, first, wpu, tpw, invn,
+                         assign16, stride16);
     return hipGetLastError();
   }
   if (invn != nullptr) {  // the chunked kernel does not hold whole rows: a separate pass
@@ -1524,9 +1515,10 @@ hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K,
   return hipGetLastError();
 }
 
-hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu_stride, int count, int K,
-                        const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
+hipError_t launch_delta(const uint16_t* cur_lab, const uint16_t* prev_lab, int stride16, int clu_stride, int count,
+                        int K, const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
                         int32_t* csize, uint16_t* cdir, int units, hipStream_t s) {
+  if ((stride16 & 1) != 0 || stride16 < count) return hipErrorInvalidValue;
   if (!delta_supported(K, count, units) || prev_lab == nullptr) return hipErrorInvalidValue;
   const int D = delta_dims(K);
   const int ranges = delta_ranges(units, K);
@@ -1546,10 +1538,12 @@ hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu
   const dim3 grid((unsigned)(units * (kHeadDim / D) * ranges));
   if (D == 32)
     hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<32>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab,
-                       clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize);
+                       stride16, clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix,
+                       csize);
   else
     hipLaunchKernelGGL(HIP_KERNEL_NAME(delta_kernel<16>), grid, dim3(kDelThreads), lds, s, cur_lab, prev_lab,
-                       clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix, csize);
+                       stride16, clu_stride, count, K, ranges, xcd_map, k_tok, capacity, n_sink, invn, fbits, sfix,
+                       csize);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)units * K;

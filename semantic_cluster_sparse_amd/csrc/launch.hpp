@@ -27,9 +27,12 @@ hipError_t launch_init_dirs(const uint16_t* k_tok, int capacity, int n_sink, int
 // assign[u, first + i] = argmax_j k_tok[u, row0 + i] . cdir[u, j] for i < count.
 // With invn non-null also invn[u, first + i] = 1/|k_tok[u, row0 + i]| (f64),
 // the same values launch_inv_norm writes.
+// assign16 (uint16, row stride stride16; K <= 512 only) takes a copy of the
+// labels, and assign may be null when only that copy is wanted.
 hipError_t launch_assign(const uint16_t* k_tok, int capacity, int row0, int count,
                          const uint16_t* cdir, int K, int32_t* assign, int clu_stride,
-                         int first, int units, hipStream_t s, double* invn = nullptr);
+                         int first, int units, hipStream_t s, double* invn = nullptr,
+                         uint16_t* assign16 = nullptr, int stride16 = 0);
 
 // 1/|x| (f64) of clustered tokens [first, first + count) into invn[u, first + i].
 hipError_t launch_inv_norm(const uint16_t* k_tok, int capacity, int n_sink, int first, int count,
@@ -41,15 +44,16 @@ hipError_t launch_index(const int32_t* assign, int clu_stride, int count, int K,
                         int32_t* offsets, int units, hipStream_t s);
 
 // A Lloyd round between the first and the last from the keys that changed
-// cluster between prev_lab and cur_lab [u, 0:count).  While the rounds run,
-// csum holds the unit-key sums as int64 fixed point (the first round's
-// kUpdFixed update writes them, the last round's update writes them in f64
-// again); csize and cdir are kept current.  invn[u, i] = 1/|x_i| of every
-// clustered token.  delta_supported says whether a shape takes this form
-// (else every round rebuilds from the index).
+// cluster between prev_lab and cur_lab (uint16 labels, row stride stride16,
+// even and >= count; columns 0:count).  While the rounds run, csum holds the
+// unit-key sums as int64 fixed point (the first round's kUpdFixed update
+// writes them, the last round's update writes them in f64 again); csize and
+// cdir are kept current.  invn[u, i] (row stride clu_stride) = 1/|x_i| of
+// every clustered token.  delta_supported says whether a shape takes this
+// form (else every round rebuilds from the index).
 bool delta_supported(int K, int count, int units);
-hipError_t launch_delta(const int32_t* cur_lab, const int32_t* prev_lab, int clu_stride, int count, int K,
-                        const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
+hipError_t launch_delta(const uint16_t* cur_lab, const uint16_t* prev_lab, int stride16, int clu_stride, int count,
+                        int K, const uint16_t* k_tok, int capacity, int n_sink, const double* invn, double* csum,
                         int32_t* csize, uint16_t* cdir, int units, hipStream_t s);
 
 // Per-cluster segmented reduction over the members listed by perm/offsets.
