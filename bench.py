@@ -124,11 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "5af90ca1745a9b59aa68c25e7d7bf0fd593daea21386301b7937b22c4c8f2a98",
-                      "fetch_kib": 47176.1, "write_kib": 1274.3},
+                      "sha256": "57889b6ee009ba5453cd58246d647d9c4b82f2d4e14354df4d98a2a94b8f0645",
+                      "fetch_kib": 47176.3, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "3a47c2f286c48994e806d56d51569a6015a015093a480f532bda51fd9964f8ea",
-                      "fetch_kib": 34287.0, "write_kib": 762.0},
+                      "sha256": "8feced37d9113643b6d125b3ef6798e13c146b997b2591ef2bb70ee7f5084a6a",
+                      "fetch_kib": 34287.2, "write_kib": 762.0},
 }
 
 

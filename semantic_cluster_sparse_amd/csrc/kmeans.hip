@@ -23,8 +23,7 @@ namespace ckv {
 // j = m - K .. m - 1 a draw r gives t = r mod (j + 1); t is inserted unless it
 // is already in the sample, in which case j is.  One workgroup per unit.  The
 // generator's state after i + 1 steps is its initial state plus (i + 1) times
-// its increment, so the lanes compute every draw's t at once; only the
-// membership tests and inserts run in order.
+// its increment, so the lanes compute every draw's t at once.
 // ---------------------------------------------------------------------------
 constexpr uint64_t kSplitMixGamma = 0x9E3779B97F4A7C15ull;
 
@@ -44,27 +43,55 @@ __device__ __forceinline__ void floyd_targets(uint64_t seed, int u, int m, int K
 }
 
 // Membership of the indices drawn so far: a bitmap over [0, m) in LDS when it
-// fits (one lane then makes the inserts, with no barrier between them), else
-// the list of draws scanned by all 64 lanes.
+// fits, else the list of draws scanned by all 64 lanes.
 constexpr int kDrawBitmapWords = 16384;  // 64 KiB of LDS: m up to 524288
 
+// The bitmap form takes the draws 64 at a time, one per lane.  With low = m - K,
+// draw i's target t lies in [0, low + i], and t is already in the sample when
+// (a) an earlier batch inserted it (the bitmap), (b) an earlier draw of this
+// batch has the same target (that draw inserted t, or t was in already), or
+// (c) t = low + j for an earlier draw j of this batch that found its own target
+// taken and so inserted low + j.  (c) links a draw to one earlier draw; the
+// links are resolved by repeating it until no flag changes (each repetition
+// settles at least one more link of every chain, so at most 64 repetitions).
+// The result equals inserting the draws one after another.
 __global__ __launch_bounds__(64) void init_draw_bitmap_kernel(uint64_t seed, int m, int K,
                                                               int32_t* __restrict__ init_idx) {
   extern __shared__ uint32_t bitmap[];
-  __shared__ int tdraw[kMaxClusters];
   const int u = blockIdx.x;
+  const int lane = lane_id();
   const int words = (m + 31) >> 5;
-  for (int i = threadIdx.x; i < words; i += kWave) bitmap[i] = 0u;
-  floyd_targets(seed, u, m, K, tdraw);
+  for (int i = lane; i < words; i += kWave) bitmap[i] = 0u;
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  const uint64_t s0 = seed + (uint64_t)u;
+  const int low = m - K;
   int32_t* out = init_idx + (size_t)u * K;
-  for (int i = 0; i < K; ++i) {
-    const int t = tdraw[i];
-    const bool taken = (bitmap[t >> 5] >> (t & 31)) & 1u;
-    const int pick = taken ? m - K + i : t;  // m - K + i itself is never taken yet: every earlier pick is below it
-    bitmap[pick >> 5] |= 1u << (pick & 31);
-    out[i] = pick;
+  for (int base = 0; base < K; base += kWave) {
+    const int i = base + lane;
+    const bool live = i < K;
+    int t = 0;
+    if (live) {
+      const uint64_t r = splitmix64_mix(s0 + (uint64_t)(i + 1) * kSplitMixGamma);
+      t = (int)(r % (uint64_t)(low + i + 1));
+    }
+    bool taken = (bitmap[t >> 5] >> (t & 31)) & 1u;
+#pragma unroll 8
+    for (int j = 0; j < kWave - 1; ++j) taken |= (j < lane) & (__builtin_amdgcn_readlane(t, j) == t);
+    taken = taken && live;
+    const int src = t - low - base;  // lane of the draw whose own index is t
+    const bool linked = live && src >= 0 && src < lane;
+    unsigned long long cur = __ballot(taken), prev = 0;
+    while (cur != prev) {
+      prev = cur;
+      taken = taken || (linked && ((cur >> (src & 63)) & 1ull));
+      cur = __ballot(taken);
+    }
+    const int pick = taken ? low + i : t;  // low + i itself is never taken: every earlier pick is below it
+    if (live) {
+      atomicOr(&bitmap[pick >> 5], 1u << (pick & 31));
+      out[i] = pick;
+    }
+    __syncthreads();  // the inserts are seen by the next batch's membership tests
   }
 }
 

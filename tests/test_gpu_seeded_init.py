@@ -30,6 +30,8 @@ D = 128
     (64, 16, 32752, 400, 2 ** 64 - 3),   # seed + unit wraps around 2^64
     (3, 0, 5000, 1024, 77),              # the largest K
     (5, 16, 40, 40, 9),                  # K = m: every index, in Floyd's order
+    (4, 16, 1100, 1024, 3),              # K near m: most draws' targets already taken, long chains
+    (2, 0, 130, 128, 11),
     (2, 5, 1, 1, 123456789),
     (1, 16, 600000, 50, 5),              # beyond the LDS bitmap: the draws' list is scanned instead
 ])
