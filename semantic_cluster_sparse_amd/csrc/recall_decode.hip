@@ -265,8 +265,10 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   if (W > 1) {
     const int even = (R + W - 1) / W;
     const int tail = need > 0 ? max(need, even - kCutPenaltyRows) : even;
-    int chunk = (R - tail + W - 2) / (W - 1);
-    chunk = (chunk + 15) & ~15;
+    // rounded down: the first W - 1 chunks end at or before R - tail, so
+    // every cut row falls in the last chunk and no other workgroup scores
+    // the cut cluster
+    const int chunk = (R - tail) / (W - 1);
     c0 = min(w * chunk, R);
     c1 = w == W - 1 ? R : min(c0 + chunk, R);
   }
