@@ -124,8 +124,8 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "57889b6ee009ba5453cd58246d647d9c4b82f2d4e14354df4d98a2a94b8f0645",
-                      "fetch_kib": 47176.3, "write_kib": 1274.4},
+                      "sha256": "5b1d0a9756025c733b95a5d7c087e09cfdb4d48e80c8ef44e67abe5564875c4f",
+                      "fetch_kib": 47210.8, "write_kib": 1274.3},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
                       "sha256": "8feced37d9113643b6d125b3ef6798e13c146b997b2591ef2bb70ee7f5084a6a",
                       "fetch_kib": 34287.2, "write_kib": 762.0},
