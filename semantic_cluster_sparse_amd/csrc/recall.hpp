@@ -158,6 +158,30 @@ __device__ __forceinline__ void qbar8(const uint16_t* q, int u, int G, int li, f
   }
 }
 
+// The same sum in two parts: qrows_load issues the GT (>= G) row loads with
+// no condition on G (rows past G - 1 repeat the last), so that a caller can
+// issue more loads behind them and the sum waits for these alone; qbar_sum
+// adds heads 0 .. G - 1 in order, the operations of qbar8.
+template <int GT>
+__device__ __forceinline__ void qrows_load(const uint16_t* q, int u, int G, int li, uint4 (&w)[GT]) {
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+    w[h] = *reinterpret_cast<const uint4*>(q + ((size_t)u * G + min(h, G - 1)) * kHeadDim + li * 8);
+}
+template <int GT>
+__device__ __forceinline__ void qbar_sum(const uint4 (&w)[GT], int G, float* qb) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qb[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const bool on = h < G;
+    qb[0] = on ? qb[0] + bf16_lo(w[h].x) : qb[0]; qb[1] = on ? qb[1] + bf16_hi(w[h].x) : qb[1];
+    qb[2] = on ? qb[2] + bf16_lo(w[h].y) : qb[2]; qb[3] = on ? qb[3] + bf16_hi(w[h].y) : qb[3];
+    qb[4] = on ? qb[4] + bf16_lo(w[h].z) : qb[4]; qb[5] = on ? qb[5] + bf16_hi(w[h].z) : qb[5];
+    qb[6] = on ? qb[6] + bf16_lo(w[h].w) : qb[6]; qb[7] = on ? qb[7] + bf16_hi(w[h].w) : qb[7];
+  }
+}
+
 // Partial fill of the cut cluster by one wave: the `need` highest token keys
 // (ties: smaller position first), written in position order at `o`.
 __device__ __forceinline__ void fill_cut(const uint32_t* tk, int n, int need, int lo, int o, int* hist,

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   __shared__ int wl_end[kMaxClusters];  // running row count through the t-th whole cluster
   __shared__ int wl_off[kMaxClusters];  // its first position, | kAfterCut above the cut
   __shared__ int sh[8];
+  __shared__ __attribute__((aligned(16))) float qbar_lds[kHeadDim];  // the group's query sum
   RecallScratch& rs = *reinterpret_cast<RecallScratch*>(smem);
   SelScratch<kRdThreads>& ws = rs.ws;
   int* rowsrc = reinterpret_cast<int*>(smem + kRingBytes);
@@ -108,23 +109,39 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   const int m = off[K];
   const int beff = budget < m ? budget : m;
   const float* mu_u = cmean + (size_t)u * K * kHeadDim + li * 8;
-  // The query sum first: its loads leave before the centroid rows', which
-  // complete in order after them (1.4 us less per launch than summing after
-  // the rows' loads are issued).
-  float qb[8];
-  qbar8(q, v, G, li, qb);
-  for (int j0 = 0; j0 < K; j0 += kRdGroups * kRdRowsInFlight) {
-    float4 a[kRdRowsInFlight][2];
+  // The query sum is made once per workgroup, by lanes 0-15 of wave 0 (one
+  // 16-byte slice of every head each), and handed to the other threads in
+  // LDS.  (Every thread loading every head's slice moved G x 16 KB per
+  // workgroup through its load pipe for a 4 KB query and, at G = 16, held the
+  // centroid rows back by ~1.2 us.)  The makers issue their query loads before
+  // their centroid rows' and sum behind them: a wave's loads complete in order.
+  const bool qmaker = tid < 16;
+  uint4 qw[GT];
+  if (qmaker) qrows_load<GT>(q, v, G, li, qw);
+  constexpr int kRound = kRdGroups * kRdRowsInFlight;
+  float4 a[kRdRowsInFlight][2];
 #pragma unroll
-    for (int t = 0; t < kRdRowsInFlight; ++t) {
-      const int j = j0 + grp + t * kRdGroups;
-      if (j < K) {
-        a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
-        a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
-      } else {
-        a[t][0] = a[t][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
+  for (int t = 0; t < kRdRowsInFlight; ++t) {  // rows past K - 1 repeat the last; their scores are dropped
+    const int j = min(grp + t * kRdGroups, K - 1);
+    a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
+    a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the sum (and its wait) stays behind the row loads
+  if (qmaker) {
+    float qs[8];
+    qbar_sum<GT>(qw, G, qs);
+    *reinterpret_cast<float4*>(&qbar_lds[li * 8]) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+    *reinterpret_cast<float4*>(&qbar_lds[li * 8 + 4]) = make_float4(qs[4], qs[5], qs[6], qs[7]);
+  }
+  lds_barrier();
+  float qb[8];
+  {
+    const float4 q0 = *reinterpret_cast<const float4*>(&qbar_lds[li * 8]);
+    const float4 q1 = *reinterpret_cast<const float4*>(&qbar_lds[li * 8 + 4]);
+    qb[0] = q0.x; qb[1] = q0.y; qb[2] = q0.z; qb[3] = q0.w;
+    qb[4] = q1.x; qb[5] = q1.y; qb[6] = q1.z; qb[7] = q1.w;
+  }
+  for (int j0 = 0;;) {
 #pragma unroll
     for (int t = 0; t < kRdRowsInFlight; ++t) {
       const int j = j0 + grp + t * kRdGroups;
@@ -134,6 +151,14 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
       d = fmaf(qb[7], a[t][1].w, d);
       d = sum16(d);
       if (li == 0 && j < K) rs.csc[j] = d;
+    }
+    j0 += kRound;
+    if (j0 >= K) break;
+#pragma unroll
+    for (int t = 0; t < kRdRowsInFlight; ++t) {
+      const int j = min(j0 + grp + t * kRdGroups, K - 1);
+      a[t][0] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim);
+      a[t][1] = *reinterpret_cast<const float4*>(mu_u + (size_t)j * kHeadDim + 4);
     }
   }
 #pragma unroll
