@@ -124,11 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "5b1d0a9756025c733b95a5d7c087e09cfdb4d48e80c8ef44e67abe5564875c4f",
-                      "fetch_kib": 47210.8, "write_kib": 1274.3},
+                      "sha256": "19725d9ea8533a5cb79f21d3236d9f1ebc47cbc7f1e1885a1e21de645552ad73",
+                      "fetch_kib": 47205.0, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
                       "sha256": "8feced37d9113643b6d125b3ef6798e13c146b997b2591ef2bb70ee7f5084a6a",
-                      "fetch_kib": 34287.2, "write_kib": 762.0},
+                      "fetch_kib": 34286.9, "write_kib": 762.0},
 }
 
 
