@@ -48,6 +48,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ __attribute__((aligned(16))) float tsc[kCutLds];
   __shared__ __attribute__((aligned(16))) SelScratch<kSelThreads> ws;
   __shared__ int sh_last;
+  __shared__ __attribute__((aligned(16))) float qbar_lds[kHeadDim];  // the group's query sum
 
   // selection v of physical unit u: hs = 1 (one recall per KV head, q_bar over
   // its G query heads) or hs = G (one recall per query head, G passed as 1)
@@ -93,8 +94,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         a[t][0] = a[t][1] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    // the query sum while the centroid rows are in flight
-    qbar8(q, v, G, li, qb);
+    // the query sum while the centroid rows are in flight, made once per
+    // workgroup by lanes 0-15 of wave 0 and handed over in LDS (every thread
+    // loading every head's slice moved G x 16 KB through the load pipe)
+    if (tid < 16) {
+      float qs[8];
+      qbar8(q, v, G, li, qs);
+      *reinterpret_cast<float4*>(&qbar_lds[li * 8]) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+      *reinterpret_cast<float4*>(&qbar_lds[li * 8 + 4]) = make_float4(qs[4], qs[5], qs[6], qs[7]);
+    }
+    lds_barrier();
+    {
+      const float4 q0 = *reinterpret_cast<const float4*>(&qbar_lds[li * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&qbar_lds[li * 8 + 4]);
+      qb[0] = q0.x; qb[1] = q0.y; qb[2] = q0.z; qb[3] = q0.w;
+      qb[4] = q1.x; qb[5] = q1.y; qb[6] = q1.z; qb[7] = q1.w;
+    }
 #pragma unroll
     for (int t = 0; t < kRowsInFlight; ++t) {
       const int j = j_lo + grp + t * kSelGroups;
