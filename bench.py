@@ -124,11 +124,11 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "19725d9ea8533a5cb79f21d3236d9f1ebc47cbc7f1e1885a1e21de645552ad73",
+                      "sha256": "8c988f0d63e56ea3320a914ad73821db3535f109c8dc81eff6efbfdf8d8cdf11",
                       "fetch_kib": 47205.0, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
                       "sha256": "8feced37d9113643b6d125b3ef6798e13c146b997b2591ef2bb70ee7f5084a6a",
-                      "fetch_kib": 34286.9, "write_kib": 762.0},
+                      "fetch_kib": 34286.7, "write_kib": 762.0},
 }
 
 
