@@ -124,7 +124,7 @@ def fused_bytes(units: int, n_sink: int, c: int, r: int, group: int, K: int) -> 
 # when the hash of those sources differs, traffic is reported as null.
 TRAFFIC = {
     "recall_decode": {"sources": ("recall_decode.hip", "recall.hpp", "stream.hpp", "common.hpp", "launch.hpp"),
-                      "sha256": "8c988f0d63e56ea3320a914ad73821db3535f109c8dc81eff6efbfdf8d8cdf11",
+                      "sha256": "ff5964b03e987cd2c290cbe854c0cb60f4f4132e8d48595fb6e60067d30df1c4",
                       "fetch_kib": 47205.0, "write_kib": 1274.4},
     "sparse_decode": {"sources": ("decode.hip", "stream.hpp", "common.hpp", "launch.hpp"),
                       "sha256": "8feced37d9113643b6d125b3ef6798e13c146b997b2591ef2bb70ee7f5084a6a",

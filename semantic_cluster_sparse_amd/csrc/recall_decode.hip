@@ -396,7 +396,9 @@ __global__ __launch_bounds__(kRdThreads) void recall_decode_kernel(
   for (int seg = c0; seg < c1; seg += kRowSegment) {
     const int seg_end = min(c1, seg + kRowSegment);
     const int nrows = seg_end - seg;
-    if (seg != c0) __syncthreads();  // the previous segment's rows are all streamed
+    // the previous segment's rows are all streamed (the first segment follows
+    // the barrier that ends the recall)
+    if (seg != c0) __syncthreads();
     // sinks, recent rows and (fallback) the cut's rows: one thread per row
 #pragma unroll
     for (int k = 0; k < kSegPerThread; ++k) {
